@@ -1,0 +1,395 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test ties one oracle function to a library routine, a closed form, exact
+rational arithmetic, exhaustive enumeration or hand-computed values, chosen so
+that a plausible slip (dropped term, wrong sign or index, transposed operand,
+off-by-one count) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import brute
+
+RNG = np.random.default_rng(12345)
+
+
+def bf16_bits(x):
+    """torch's own fp32 -> bf16 rounding (RNE), as uint16 bit patterns."""
+    t = torch.as_tensor(np.asarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_values(bits):
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------- Philox
+@pytest.mark.parametrize("ctr,key", [
+    ([1, 0, 0, 0], [0, 0]),
+    ([5, 0, 0, 0], [7, 0]),
+    ([1, 2, 3, 4], [5, 6]),
+    ([2**63 + 11, 2**40 + 3, 99, 2**64 - 5], [2**64 - 1, 2**33]),
+    ([123456789, 0, (7 << 32) | 5, 42], [0xDEADBEEF, 0]),
+])
+def test_philox_matches_numpy(ctr, key):
+    # numpy's Philox (Philox-4x64-10) increments its counter before each block,
+    # so numpy seeded with c - 1 produces the block of counter c (no carry here).
+    mine = oracle.philox4x64_10(ctr, key)
+    c = list(ctr)
+    c[0] -= 1
+    ref = np.random.Philox(counter=np.array(c, np.uint64),
+                              key=np.array(key, np.uint64)).random_raw(4).astype(np.uint64)
+    assert np.array_equal(mine, ref)
+
+
+def test_philox_grid_matches_numpy():
+    for i in range(64):
+        ctr = [int(v) for v in RNG.integers(1, 2**63, 4, dtype=np.uint64)]
+        key = [int(v) for v in RNG.integers(0, 2**63, 2, dtype=np.uint64)]
+        c = list(ctr)
+        c[0] -= 1
+        ref = np.random.Philox(counter=np.array(c, np.uint64),
+                              key=np.array(key, np.uint64)).random_raw(4).astype(np.uint64)
+        assert np.array_equal(oracle.philox4x64_10(ctr, key), ref), i
+
+
+def test_random_score_counter_layout_matches_numpy():
+    seed, req, pss, layer, head, N, P = 0x1234_5678_9ABC, 77, 5, 3, 6, 203, 37
+    u = oracle.random_score(seed, req, pss, layer, head, N, P)
+    assert u.shape == (N - P,) and u.dtype == np.uint32
+    for n in [P, P + 1, P + 2, 40, 41, 42, 43, 100, N - 1]:
+        ctr = [n // 4 - 1, pss, (layer << 32) | head, req]
+        if ctr[0] < 0:
+            continue
+        words = np.random.Philox(counter=np.array(ctr, np.uint64),
+                                key=np.array([seed, 0], np.uint64)).random_raw(4)
+        assert int(u[n - P]) == int(words[n % 4]) >> 32, n
+
+
+def test_random_score_uniform_and_fresh_per_pass_and_head():
+    N, P = 40000, 0
+    u = oracle.random_score(9, 1, 0, 0, 0, N, P).astype(np.float64) / 2**32
+    hist, _ = np.histogram(u, bins=50, range=(0, 1))
+    expected = N / 50
+    chi2 = ((hist - expected) ** 2 / expected).sum()
+    assert chi2 < 100, chi2          # 49 dof; p ~ 5e-5 at 100
+    a = oracle.random_score(9, 1, 0, 0, 0, 4096, 0)
+    assert not np.array_equal(a, oracle.random_score(9, 1, 1, 0, 0, 4096, 0))   # new pass
+    assert not np.array_equal(a, oracle.random_score(9, 1, 0, 0, 1, 4096, 0))   # other head
+    assert not np.array_equal(a, oracle.random_score(9, 1, 0, 1, 0, 4096, 0))   # other layer
+    assert not np.array_equal(a, oracle.random_score(9, 2, 0, 0, 0, 4096, 0))   # other request
+    # slot-addressed: prompt length only changes which slots are scored
+    b = oracle.random_score(9, 1, 0, 0, 0, 4096, 100)
+    assert np.array_equal(a[100:], b)
+
+
+# --------------------------------------------------------------- maintenance
+def test_bf16_round_matches_torch():
+    x = np.concatenate([RNG.standard_normal(5000).astype(np.float32) * 10,
+                        np.array([1.0, -1.0, 0.0, 1 + 2**-8, 1 + 3 * 2**-9, 1 + 2**-9,
+                                  -(1 + 2**-9), 3.0 + 2**-7], np.float32)])
+    mine = np.array([oracle.bf16_round(v) for v in x], np.uint16)
+    assert np.array_equal(mine, bf16_bits(x))
+
+
+def test_macqueen_fill_is_exact():
+    T, G, d, K = 5, 2, 16, 12
+    q = bf16_bits(RNG.standard_normal((T, G, d)))
+    b, c, a = oracle.beacon_update(q, np.full((K, d), 7.0, np.float32), np.zeros(K, np.int32))
+    assert list(a) == list(range(10))
+    assert np.array_equal(c, np.array([1] * 10 + [0] * 2, np.int32))
+    assert np.array_equal(b[:10], bf16_values(q.reshape(10, d)))
+    assert np.all(b[10:] == 7.0)
+
+
+def test_fills_first_empty_slot_even_when_not_leading():
+    d, K = 8, 4
+    b0 = RNG.standard_normal((K, d)).astype(np.float32)
+    c0 = np.array([3, 0, 5, 0], np.int32)
+    q = bf16_bits(RNG.standard_normal((2, 1, d)))
+    b, c, a = oracle.beacon_update(q, b0, c0)
+    assert list(a) == [1, 3]
+    assert list(c) == [3, 1, 5, 1]
+    assert np.array_equal(b[[0, 2]], b0[[0, 2]])
+
+
+def test_update_hand_computed_values():
+    # b = 0, count 1; query 3.0 -> count 2, b = 0 + (3 - 0)/2 = 1.5;
+    # query 1.5 -> count 3, b = 1.5 + 0/3 = 1.5; query -4.5 -> count 4,
+    # b = 1.5 + (-6)/4 = 0.
+    d = 2
+    q = bf16_bits(np.array([[[3.0, 1.0]], [[1.5, 1.0]], [[-4.5, 1.0]]]))
+    b, c, _ = oracle.beacon_update(q, np.array([[0.0, 1.0]], np.float32),
+                                   np.array([1], np.int32))
+    assert c[0] == 4
+    assert b[0, 0] == 0.0 and b[0, 1] == 1.0
+    # a non-representable step rounds once per IEEE fp32 operation:
+    # b = 1, count 2 -> x = 2: b = 1 + (2 - 1)/3 = 1 + fl32(1/3)
+    q = bf16_bits(np.array([[[2.0, 0.0]]]))
+    b, c, _ = oracle.beacon_update(q, np.array([[1.0, 0.0]], np.float32), np.array([2], np.int32))
+    assert b[0, 0] == np.float32(np.float32(1.0) + np.float32(np.float32(1.0) / np.float32(3.0)))
+
+
+def test_running_mean_tracks_exact_mean():
+    T, G, d, K = 40, 4, 32, 6
+    q = bf16_bits(RNG.standard_normal((T, G, d)) + 0.5)
+    b0 = RNG.standard_normal((K, d)).astype(np.float32)
+    c0 = RNG.integers(1, 9, K).astype(np.int32)
+    b, c, a = oracle.beacon_update(q, b0, c0)
+    assert c.sum() == c0.sum() + T * G
+    xs = bf16_values(q.reshape(T * G, d)).astype(np.float64)
+    for j in range(K):
+        m = np.flatnonzero(a == j)
+        assert c[j] == c0[j] + len(m)
+        mean = (c0[j] * b0[j].astype(np.float64) + xs[m].sum(0)) / (c0[j] + len(m))
+        # each fp32 update adds at most a few ulps of max(|x|, |b|)
+        scale = max(np.abs(xs).max(), np.abs(b0[j]).max())
+        tol = 4 * (len(m) + 1) * 2**-24 * scale
+        assert np.max(np.abs(b[j] - mean)) <= tol, (j, np.max(np.abs(b[j] - mean)), tol)
+
+
+def test_assignment_is_exact_argmax_on_tiny_inputs():
+    for trial in range(6):
+        T, G, d, K = 6, 2, 6, 5
+        q = bf16_bits(RNG.standard_normal((T, G, d)))
+        b0 = RNG.standard_normal((K, d)).astype(np.float32)
+        if trial == 0:
+            b0[2] = 0.0                       # a zero-norm beacon counts as cosine 0
+        c0 = RNG.integers(1, 5, K).astype(np.int32)
+        _, _, a = oracle.beacon_update(q, b0, c0)
+        flat = q.reshape(T * G, d)
+        for s in range(T * G):
+            if s == 0:
+                bs = b0
+            else:
+                bs, _, _ = oracle.beacon_update(flat[:s].reshape(s, 1, d), b0, c0)
+            assert a[s] == brute.exact_nearest(flat[s], bs), (trial, s)
+
+
+def test_zero_query_goes_to_row_zero():
+    d, K = 8, 3
+    b0 = RNG.standard_normal((K, d)).astype(np.float32)
+    q = np.zeros((1, 1, d), np.uint16)
+    _, _, a = oracle.beacon_update(q, b0, np.ones(K, np.int32))
+    assert a[0] == 0
+
+
+def test_forced_replay_gap_and_rules():
+    T, G, d, K = 20, 2, 16, 4
+    q = bf16_bits(RNG.standard_normal((T, G, d)))
+    b0 = np.zeros((K, d), np.float32)
+    c0 = np.zeros(K, np.int32)
+    b1, c1, a = oracle.beacon_update(q, b0, c0)
+    b2, c2, gap = oracle.beacon_update_forced(q, b0, c0, a)
+    assert np.array_equal(b1, b2) and np.array_equal(c1, c2)
+    assert np.all(gap == 0.0)
+    bad = a.copy()
+    bad[0] = 1                                    # breaks the empty-slot rule
+    _, _, gap = oracle.beacon_update_forced(q, b0, c0, bad)
+    assert np.isinf(gap[0])
+    bad = a.copy()
+    s = K + 3
+    bad[s] = (a[s] + 1) % K                       # a worse row after the fill
+    _, _, gap = oracle.beacon_update_forced(q, b0, c0, bad)
+    assert gap[s] > 0
+
+
+# --------------------------------------------------------------- scoring
+def _keys(N, d, scale=1.0):
+    return bf16_bits(RNG.standard_normal((N, d)) * scale)
+
+
+def test_single_beacon_score_is_torch_softmax():
+    N, P, d, W = 300, 40, 128, 64
+    k = _keys(N, d)
+    b = RNG.standard_normal((1, d)).astype(np.float32)
+    s, lse = oracle.beacon_score(k, b, np.array([3], np.int32), P, W=W, bonus=0.0)
+    kv = torch.tensor(bf16_values(k), dtype=torch.float64)
+    bv = torch.tensor(bf16_values(bf16_bits(b)), dtype=torch.float64)    # torch's bf16 RNE
+    logits = (kv @ bv[0]) / math.sqrt(d)
+    ref = torch.softmax(logits, 0).numpy()
+    assert np.allclose(s, ref[P:], rtol=1e-12, atol=0)
+    assert abs(lse[0] - torch.logsumexp(logits, 0).item()) < 1e-12
+
+
+def test_window_bonus_and_max_over_beacons():
+    N, P, d, K, W = 260, 20, 128, 3, 64
+    k = _keys(N, d)
+    b = RNG.standard_normal((K, d)).astype(np.float32)
+    c = np.array([1, 2, 3], np.int32)
+    s0, _ = oracle.beacon_score(k, b, c, P, W=W, bonus=0.0)
+    s1, _ = oracle.beacon_score(k, b, c, P, W=W, bonus=1.0)
+    diff = s1 - s0
+    n = np.arange(P, N)
+    assert np.allclose(diff[n >= N - W], 1.0, atol=1e-15)
+    assert np.all(diff[n < N - W] == 0.0)
+    singles = [oracle.beacon_score(k, b[j:j + 1], c[j:j + 1], P, W=W, bonus=0.0)[0]
+               for j in range(K)]
+    assert np.array_equal(s0, np.maximum.reduce(singles))
+
+
+def test_lse_normalises_every_live_beacon():
+    N, P, d, K = 500, 0, 128, 5
+    k = _keys(N, d, 2.0)
+    b = (RNG.standard_normal((K, d)) * 1.5).astype(np.float32)
+    c = np.array([2, 0, 5, 1, 9], np.int32)
+    s, lse = oracle.beacon_score(k, b, c, P, W=0, bonus=0.0)
+    assert np.isnan(lse[1]) and not np.isnan(lse[[0, 2, 3, 4]]).any()
+    kv = bf16_values(k).astype(np.float64)
+    bv = bf16_values(bf16_bits(b)).astype(np.float64)
+    logits = bv @ kv.T / math.sqrt(d)                      # [K, N]
+    for j in (0, 2, 3, 4):
+        assert abs(np.exp(logits[j] - lse[j]).sum() - 1.0) < 1e-12
+    assert np.all(s > 0) and np.all(s <= 1.0)
+
+
+def test_identical_keys_give_uniform_sigma():
+    N, P, d, K = 128, 16, 128, 4
+    row = _keys(1, d)
+    k = np.repeat(row, N, axis=0)
+    b = RNG.standard_normal((K, d)).astype(np.float32)
+    s, _ = oracle.beacon_score(k, b, np.ones(K, np.int32), P, W=0, bonus=0.0)
+    assert np.allclose(s, 1.0 / N, rtol=1e-13)
+
+
+def test_dead_beacons_are_ignored_and_empty_set_scores_zero():
+    N, P, d, W = 200, 50, 128, 64
+    k = _keys(N, d)
+    b = RNG.standard_normal((3, d)).astype(np.float32)
+    s_all, _ = oracle.beacon_score(k, b, np.array([4, 0, 1], np.int32), P, W=W)
+    s_sub, _ = oracle.beacon_score(k, b[[0, 2]], np.array([4, 1], np.int32), P, W=W)
+    assert np.array_equal(s_all, s_sub)
+    s_none, lse = oracle.beacon_score(k, b, np.zeros(3, np.int32), P, W=W, bonus=1.0)
+    n = np.arange(P, N)
+    assert np.array_equal(s_none, np.where(n >= N - W, 1.0, 0.0))
+    assert np.isnan(lse).all()
+
+
+def test_more_beacons_never_lower_sigma():
+    N, P, d = 300, 0, 128
+    k = _keys(N, d)
+    b = RNG.standard_normal((6, d)).astype(np.float32)
+    prev = np.zeros(N)
+    for K in range(1, 7):
+        s, _ = oracle.beacon_score(k, b[:K], np.ones(K, np.int32), P, W=0, bonus=0.0)
+        assert np.all(s >= prev)
+        prev = s
+
+
+def test_beacons_are_rounded_to_bf16_once():
+    N, P, d = 100, 0, 128
+    k = _keys(N, d)
+    b = RNG.standard_normal((2, d)).astype(np.float32)
+    b_rounded = bf16_values(bf16_bits(b))
+    s1, l1 = oracle.beacon_score(k, b, np.ones(2, np.int32), P, W=0, bonus=0.0)
+    s2, l2 = oracle.beacon_score(k, b_rounded, np.ones(2, np.int32), P, W=0, bonus=0.0)
+    assert np.array_equal(s1, s2) and np.array_equal(l1, l2)
+
+
+# --------------------------------------------------------------- selection
+def test_topk_matches_exhaustive_dominance_search():
+    for trial in range(30):
+        P = int(RNG.integers(0, 4))
+        m = int(RNG.integers(1, 10))
+        B = P + int(RNG.integers(0, m))          # N > B so a real choice is made
+        N = P + m
+        if trial % 3 == 0:
+            scores = RNG.integers(0, 3, m).astype(np.float64)     # many ties
+        else:
+            scores = RNG.random(m)
+        keep = oracle.topk_select(scores, N, P, B)
+        found = brute.topk_by_dominance(list(scores), P, B)
+        assert len(found) == 1
+        assert list(keep) == list(range(P)) + found[0], (trial, keep, found)
+
+
+def test_topk_invariants_on_larger_inputs():
+    for N, P, B in [(2112, 1024, 2048), (4096, 512, 1024), (3136, 1500, 3072), (700, 0, 64)]:
+        s = RNG.random(N - P)
+        s[::7] = 0.5                                   # plant ties
+        keep = oracle.topk_select(s, N, P, B)
+        assert keep.shape == (B,)
+        assert np.array_equal(keep[:P], np.arange(P))
+        assert np.all(np.diff(keep) > 0)
+        mask = np.zeros(N, bool)
+        mask[keep] = True
+        kept, evicted = np.flatnonzero(mask[P:]), np.flatnonzero(~mask[P:])
+        lo = s[kept].min()
+        hi = s[evicted].max()
+        assert lo >= hi
+        if lo == hi:   # ties at the boundary go to the lower slots
+            assert kept[s[kept] == lo].max() < evicted[s[evicted] == hi].min()
+
+
+def test_topk_edge_cases():
+    assert list(oracle.topk_select(np.ones(5), 8, 3, 10)) == list(range(8))    # N <= B
+    assert list(oracle.topk_select(np.ones(5), 8, 3, 8)) == list(range(8))     # N == B
+    assert list(oracle.topk_select(np.ones(5), 8, 3, 3)) == [0, 1, 2]         # P == B
+    assert list(oracle.topk_select(np.ones(5), 8, 3, 5)) == [0, 1, 2, 3, 4]   # all tied
+    assert list(oracle.topk_select(np.zeros(0), 0, 0, 4)) == []               # empty
+    with pytest.raises(ValueError):
+        oracle.topk_select(np.ones(5), 8, 3, 2)                                # P > B
+
+
+def test_topk_on_uint32_draws_is_exact():
+    u = np.array([5, 2**32 - 1, 2**32 - 2, 7, 2**32 - 1, 0], np.uint32)
+    keep = oracle.topk_select(u, 8, 2, 5)
+    # best three: slot 3 (2^32-1), slot 6 (2^32-1, later), slot 4 (2^32-2)
+    assert list(keep) == [0, 1, 3, 4, 6]
+
+
+# --------------------------------------------------------------- compaction
+def test_compaction_is_numpy_gather():
+    rows = RNG.integers(0, 2**16, (300, 128), dtype=np.uint16)
+    keep = np.sort(RNG.choice(300, 120, replace=False)).astype(np.int32)
+    out = oracle.kv_compact(rows, keep)
+    assert np.array_equal(out, rows[keep])
+    assert oracle.kv_compact(rows, np.zeros(0, np.int32)).shape == (0, 128)
+
+
+def test_gather_paged_reads_block_table():
+    pool = RNG.integers(0, 2**16, (10, 2, 16, 4), dtype=np.uint16)
+    table = np.array([7, 2, 9], np.int32)
+    dense = oracle.gather_paged(pool, table, 1, 40)
+    assert np.array_equal(dense[:16], pool[7, 1])
+    assert np.array_equal(dense[16:32], pool[2, 1])
+    assert np.array_equal(dense[32:40], pool[9, 1, :8])
+
+
+# --------------------------------------------------------------- random retention
+def test_random_retention_survival_decays_geometrically():
+    """A generated token must survive every eviction, so under the random
+    selector its survival falls geometrically.  In steady state with budget B,
+    prompt P and T new slots per pass, each candidate is kept with probability
+    (B-P)/(B-P+T) per pass, independently across passes (fresh draws)."""
+    P, B, T = 8, 72, 16                  # keep 64 of 80 -> p = 0.8
+    p = (B - P) / (B - P + T)
+    heads, passes, cohorts, ages = 24, 40, 28, 12
+    alive_at_age = np.zeros(ages)
+    for h in range(heads):
+        pos = list(range(B))             # token ids in slot order
+        birth = {}
+        nxt = B
+        for ps in range(passes):
+            new = list(range(nxt, nxt + T))
+            nxt += T
+            for t in new:
+                birth[t] = ps
+            pos = pos + new
+            u = oracle.random_score(2024, h, ps, 0, h, len(pos), P)
+            keep = oracle.topk_select(u, len(pos), P, B)
+            pos = [pos[i] for i in keep]
+            for t in pos:
+                b = birth.get(t)
+                if b is not None and b < cohorts and ps - b < ages:
+                    alive_at_age[ps - b] += 1
+    n = heads * cohorts * T
+    for m in range(ages):
+        rate = alive_at_age[m] / n
+        expect = p ** (m + 1)
+        sd = math.sqrt(expect * (1 - expect) / n)
+        assert abs(rate - expect) < 5 * sd, (m, rate, expect)
