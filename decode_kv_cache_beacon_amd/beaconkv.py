@@ -1,0 +1,405 @@
+"""ctypes binding of libbeaconkv.so (the C ABI in include/beaconkv.h).
+
+Argument marshalling only: every step of the eviction pass runs in the HIP
+kernels of the library.  Functions carry the C names; tensors are torch
+tensors on the GPU (torch provides device memory and the current stream).
+Importing this module fails loudly when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbeaconkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m decode_kv_cache_beacon_amd.build` "
+        "(the eviction pass has no CPU fallback)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ---------------------------------------------------------------- constants
+BKV_ABI_VERSION = 1
+BKV_OK, BKV_ERR_NULL, BKV_ERR_INVALID, BKV_ERR_BUDGET, BKV_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
+BKV_ERR_WORKSPACE, BKV_ERR_HIP, BKV_ERR_LENGTH, BKV_ERR_BLOCK_TABLE = 5, 6, 7, 8
+BKV_SCORE_F32, BKV_SCORE_U32 = 0, 1
+BKV_SELECT_BEACON, BKV_SELECT_RANDOM = 0, 1
+BKV_MAX_BEACONS = 256
+BKV_MAX_CANDIDATES = 32768
+HEAD_DIM = 128
+BLOCK_SIZE = 16
+
+_P = ctypes.c_void_p
+_i32, _i64, _u64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
+
+
+class bkv_cache(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", _i32), ("n_requests", _i32), ("n_kv_heads", _i32), ("head_dim", _i32),
+        ("block_size", _i32), ("max_blocks", _i32), ("num_blocks", _i64),
+        ("k_pools", _P), ("v_pools", _P), ("block_table", _P), ("seq_len", _P),
+        ("prompt_len", _P),
+    ]
+
+
+class bkv_pass_args(ctypes.Structure):
+    _fields_ = [
+        ("selector", _i32), ("budget", _i32), ("score_stride", _i32),
+        ("n_beacons", _i32), ("T", _i32), ("G", _i32), ("window", _i32), ("bonus", _f32),
+        ("queries", _P), ("beacons", _P), ("counts", _P), ("assign", _P), ("lse", _P),
+        ("seed", _u64), ("request_ids", _P), ("pass_idx", _P),
+        ("pos_ids", _P), ("pos_stride", _i32), ("scores_out", _P), ("keep_out", _P),
+    ]
+
+
+_lib.bkv_abi_version.argtypes = []
+_lib.bkv_abi_version.restype = _i32
+_lib.bkv_status_string.argtypes = [_i32]
+_lib.bkv_status_string.restype = ctypes.c_char_p
+_lib.bkv_beacon_update.argtypes = [_i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P]
+_lib.bkv_beacon_update.restype = _i32
+_lib.bkv_beacon_score.argtypes = [ctypes.POINTER(bkv_cache), _P, _P, _i32, _i32, _f32, _P, _i32,
+                                  _P, _P, _P]
+_lib.bkv_beacon_score.restype = _i32
+_lib.bkv_random_score.argtypes = [ctypes.POINTER(bkv_cache), _u64, _P, _P, _P, _i32, _P, _P]
+_lib.bkv_random_score.restype = _i32
+_lib.bkv_topk_select.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i32, _i32, _P, _P, _P]
+_lib.bkv_topk_select.restype = _i32
+_lib.bkv_kv_compact.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _P, _i32, _P, _P]
+_lib.bkv_kv_compact.restype = _i32
+_lib.bkv_workspace_size.argtypes = [ctypes.POINTER(bkv_cache), ctypes.POINTER(bkv_pass_args),
+                                    ctypes.POINTER(_sz)]
+_lib.bkv_workspace_size.restype = _i32
+_lib.bkv_evict_pass.argtypes = [ctypes.POINTER(bkv_cache), ctypes.POINTER(bkv_pass_args), _P, _sz,
+                                _P, _P]
+_lib.bkv_evict_pass.restype = _i32
+
+EXPORTS = ("bkv_abi_version", "bkv_status_string", "bkv_beacon_update", "bkv_beacon_score",
+           "bkv_random_score", "bkv_topk_select", "bkv_kv_compact", "bkv_workspace_size",
+           "bkv_evict_pass")
+
+
+class BkvError(RuntimeError):
+    def __init__(self, code: int, where: str, device: bool = False):
+        self.code = code
+        self.device = device
+        if device:
+            names = [bkv_status_string(b) for b in range(1, 31) if code & (1 << b)]
+            msg = f"{where}: device-detected error bits {code:#x}: " + "; ".join(names)
+        else:
+            msg = f"{where}: {bkv_status_string(code)} (code {code})"
+        super().__init__(msg)
+
+
+def bkv_abi_version() -> int:
+    return int(_lib.bkv_abi_version())
+
+
+def bkv_status_string(code: int) -> str:
+    return _lib.bkv_status_string(int(code)).decode()
+
+
+# ---------------------------------------------------------------- helpers
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape: Optional[Sequence[int]] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _check(code: int, where: str):
+    if code != BKV_OK:
+        raise BkvError(code, where)
+
+
+def _status(status: Optional[torch.Tensor], device):
+    if status is None:
+        return torch.zeros(1, dtype=torch.int32, device=device), True
+    _need(status, "status", torch.int32)
+    return status, False
+
+
+def check_status(status: torch.Tensor, where: str = "eviction pass", stream=None):
+    """Synchronise the stream and raise if the kernels flagged an error."""
+    (stream or torch.cuda.current_stream()).synchronize()
+    v = int(status.view(-1)[0].item())
+    if v:
+        raise BkvError(v, where, device=True)
+
+
+@dataclasses.dataclass
+class PagedCache:
+    """A paged bf16 KV cache: per-layer pools [num_blocks, H, 16, 128]."""
+    k_pools: list
+    v_pools: list
+    block_table: torch.Tensor   # int32 [R, max_blocks]
+    seq_len: torch.Tensor       # int32 [R]
+    prompt_len: torch.Tensor    # int32 [R]
+    _k_addr: torch.Tensor = None
+    _v_addr: torch.Tensor = None
+
+    def __post_init__(self):
+        if len(self.k_pools) != len(self.v_pools) or not self.k_pools:
+            raise ValueError("need one K and one V pool per layer")
+        shape = tuple(self.k_pools[0].shape)
+        if len(shape) != 4 or shape[2] != BLOCK_SIZE or shape[3] != HEAD_DIM:
+            raise ValueError(f"pools must be [num_blocks, H, {BLOCK_SIZE}, {HEAD_DIM}] (got {shape})")
+        for i, (k, v) in enumerate(zip(self.k_pools, self.v_pools)):
+            _need(k, f"k_pools[{i}]", torch.bfloat16, shape)
+            _need(v, f"v_pools[{i}]", torch.bfloat16, shape)
+        R = self.block_table.shape[0]
+        _need(self.block_table, "block_table", torch.int32)
+        if self.block_table.dim() != 2:
+            raise ValueError("block_table must be [R, max_blocks]")
+        _need(self.seq_len, "seq_len", torch.int32, (R,))
+        _need(self.prompt_len, "prompt_len", torch.int32, (R,))
+        dev = self.k_pools[0].device
+        self._k_addr = torch.tensor([t.data_ptr() for t in self.k_pools], dtype=torch.int64,
+                                    device=dev)
+        self._v_addr = torch.tensor([t.data_ptr() for t in self.v_pools], dtype=torch.int64,
+                                    device=dev)
+
+    @property
+    def n_layers(self):
+        return len(self.k_pools)
+
+    @property
+    def n_requests(self):
+        return self.block_table.shape[0]
+
+    @property
+    def n_kv_heads(self):
+        return self.k_pools[0].shape[1]
+
+    @property
+    def max_blocks(self):
+        return self.block_table.shape[1]
+
+    @property
+    def num_blocks(self):
+        return self.k_pools[0].shape[0]
+
+    @property
+    def n_head_caches(self):
+        return self.n_layers * self.n_requests * self.n_kv_heads
+
+    @property
+    def max_slots(self):
+        return self.max_blocks * BLOCK_SIZE
+
+    @property
+    def device(self):
+        return self.k_pools[0].device
+
+    def struct(self) -> bkv_cache:
+        return bkv_cache(self.n_layers, self.n_requests, self.n_kv_heads, HEAD_DIM, BLOCK_SIZE,
+                         self.max_blocks, self.num_blocks, self._k_addr.data_ptr(),
+                         self._v_addr.data_ptr(), self.block_table.data_ptr(),
+                         self.seq_len.data_ptr(), self.prompt_len.data_ptr())
+
+
+# ---------------------------------------------------------------- entry points
+def bkv_beacon_update(queries, beacons, counts, assign=None, stream=None):
+    """queries bf16 [HC,T,G,128]; beacons fp32 [HC,K,128]; counts int32 [HC,K] (in place)."""
+    _need(queries, "queries", torch.bfloat16)
+    if queries.dim() != 4 or queries.shape[3] != HEAD_DIM:
+        raise ValueError("queries must be [HC, T, G, 128]")
+    HC, T, G, _ = queries.shape
+    if beacons.dim() != 3:
+        raise ValueError("beacons must be [HC, K, 128]")
+    K = beacons.shape[1]
+    _need(beacons, "beacons", torch.float32, (HC, K, HEAD_DIM))
+    _need(counts, "counts", torch.int32, (HC, K))
+    if assign is not None:
+        _need(assign, "assign", torch.int32, (HC, T * G))
+    code = _lib.bkv_beacon_update(HC, T, G, HEAD_DIM, K, _ptr(queries), _ptr(beacons),
+                                  _ptr(counts), _ptr(assign), _stream(stream))
+    _check(code, "bkv_beacon_update")
+
+
+def bkv_beacon_score(cache: PagedCache, beacons, counts, scores, window=64, bonus=1.0, lse=None,
+                     status=None, check=True, stream=None):
+    """scores fp32 [HC, stride] receives score(n) at column n - P."""
+    HC = cache.n_head_caches
+    if beacons.dim() != 3:
+        raise ValueError("beacons must be [HC, K, 128]")
+    K = beacons.shape[1]
+    _need(beacons, "beacons", torch.float32, (HC, K, HEAD_DIM))
+    _need(counts, "counts", torch.int32, (HC, K))
+    _need(scores, "scores", torch.float32)
+    if scores.dim() != 2 or scores.shape[0] != HC:
+        raise ValueError("scores must be [HC, stride]")
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (HC, K))
+    st, own = _status(status, cache.device)
+    c = cache.struct()
+    code = _lib.bkv_beacon_score(ctypes.byref(c), _ptr(beacons), _ptr(counts), K, int(window),
+                                 float(bonus), _ptr(scores), scores.shape[1], _ptr(lse), _ptr(st),
+                                 _stream(stream))
+    _check(code, "bkv_beacon_score")
+    if own and check:
+        check_status(st, "bkv_beacon_score", stream)
+    return st
+
+
+def bkv_random_score(cache: PagedCache, seed, request_ids, pass_idx, scores, status=None,
+                     check=True, stream=None):
+    """scores uint32 draws (stored in an int32 tensor) [HC, stride]."""
+    HC, R = cache.n_head_caches, cache.n_requests
+    _need(request_ids, "request_ids", torch.int64, (R,))
+    _need(pass_idx, "pass_idx", torch.int32, (R,))
+    _need(scores, "scores", torch.int32)
+    if scores.dim() != 2 or scores.shape[0] != HC:
+        raise ValueError("scores must be [HC, stride]")
+    st, own = _status(status, cache.device)
+    c = cache.struct()
+    code = _lib.bkv_random_score(ctypes.byref(c), int(seed) & (2**64 - 1), _ptr(request_ids),
+                                 _ptr(pass_idx), _ptr(scores), scores.shape[1], _ptr(st),
+                                 _stream(stream))
+    _check(code, "bkv_random_score")
+    if own and check:
+        check_status(st, "bkv_random_score", stream)
+    return st
+
+
+def bkv_topk_select(cache: PagedCache, scores, budget, keep, status=None, check=True,
+                    stream=None):
+    """scores fp32 (beacon) or int32-stored uint32 (random) [HC, stride]; keep int32 [HC, budget]."""
+    HC = cache.n_head_caches
+    if scores.dtype == torch.float32:
+        kind = BKV_SCORE_F32
+    elif scores.dtype == torch.int32:
+        kind = BKV_SCORE_U32
+    else:
+        raise ValueError("scores must be float32 or int32 (uint32 bit patterns)")
+    _need(scores, "scores", scores.dtype)
+    if scores.dim() != 2 or scores.shape[0] != HC:
+        raise ValueError("scores must be [HC, stride]")
+    _need(keep, "keep", torch.int32, (HC, budget))
+    st, own = _status(status, cache.device)
+    c = cache.struct()
+    code = _lib.bkv_topk_select(ctypes.byref(c), _ptr(scores), kind, scores.shape[1], int(budget),
+                                _ptr(keep), _ptr(st), _stream(stream))
+    _check(code, "bkv_topk_select")
+    if own and check:
+        check_status(st, "bkv_topk_select", stream)
+    return st
+
+
+def bkv_kv_compact(cache: PagedCache, keep, budget, pos_ids=None, status=None, check=True,
+                   stream=None):
+    """In-place compaction of every layer pool; pos_ids int32 [HC, >= max_slots] optional."""
+    HC = cache.n_head_caches
+    _need(keep, "keep", torch.int32, (HC, budget))
+    pos_stride = 0
+    if pos_ids is not None:
+        _need(pos_ids, "pos_ids", torch.int32)
+        if pos_ids.dim() != 2 or pos_ids.shape[0] != HC:
+            raise ValueError("pos_ids must be [HC, stride]")
+        pos_stride = pos_ids.shape[1]
+    st, own = _status(status, cache.device)
+    c = cache.struct()
+    code = _lib.bkv_kv_compact(ctypes.byref(c), _ptr(keep), int(budget), _ptr(pos_ids),
+                               pos_stride, _ptr(st), _stream(stream))
+    _check(code, "bkv_kv_compact")
+    if own and check:
+        check_status(st, "bkv_kv_compact", stream)
+    return st
+
+
+def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, window, bonus,
+               assign, lse, seed, request_ids, pass_idx, pos_ids, scores_out, keep_out,
+               score_stride):
+    HC, R = cache.n_head_caches, cache.n_requests
+    a = bkv_pass_args()
+    a.selector = selector
+    a.budget = int(budget)
+    a.score_stride = int(score_stride)
+    if selector == BKV_SELECT_BEACON:
+        _need(queries, "queries", torch.bfloat16)
+        if queries.dim() != 4 or queries.shape[0] != HC or queries.shape[3] != HEAD_DIM:
+            raise ValueError("queries must be [HC, T, G, 128]")
+        K = beacons.shape[1]
+        _need(beacons, "beacons", torch.float32, (HC, K, HEAD_DIM))
+        _need(counts, "counts", torch.int32, (HC, K))
+        a.n_beacons, a.T, a.G = K, queries.shape[1], queries.shape[2]
+        a.window, a.bonus = int(window), float(bonus)
+        a.queries, a.beacons, a.counts = queries.data_ptr(), beacons.data_ptr(), counts.data_ptr()
+        if assign is not None:
+            _need(assign, "assign", torch.int32, (HC, a.T * a.G))
+            a.assign = assign.data_ptr()
+        if lse is not None:
+            _need(lse, "lse", torch.float32, (HC, K))
+            a.lse = lse.data_ptr()
+    elif selector == BKV_SELECT_RANDOM:
+        _need(request_ids, "request_ids", torch.int64, (R,))
+        _need(pass_idx, "pass_idx", torch.int32, (R,))
+        a.seed = int(seed) & (2**64 - 1)
+        a.request_ids, a.pass_idx = request_ids.data_ptr(), pass_idx.data_ptr()
+    else:
+        raise ValueError("selector must be BKV_SELECT_BEACON or BKV_SELECT_RANDOM")
+    if pos_ids is not None:
+        _need(pos_ids, "pos_ids", torch.int32)
+        a.pos_ids, a.pos_stride = pos_ids.data_ptr(), pos_ids.shape[1]
+    stride = score_stride if score_stride > 0 else cache.max_slots
+    if scores_out is not None:
+        want = torch.float32 if selector == BKV_SELECT_BEACON else torch.int32
+        _need(scores_out, "scores_out", want, (HC, stride))
+        a.scores_out = scores_out.data_ptr()
+    if keep_out is not None:
+        _need(keep_out, "keep_out", torch.int32, (HC, budget))
+        a.keep_out = keep_out.data_ptr()
+    return a
+
+
+def bkv_workspace_size(cache: PagedCache, args: bkv_pass_args) -> int:
+    n = _sz(0)
+    c = cache.struct()
+    _check(_lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(args), ctypes.byref(n)),
+           "bkv_workspace_size")
+    return int(n.value)
+
+
+def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons=None,
+                   counts=None, window=64, bonus=1.0, assign=None, lse=None, seed=0,
+                   request_ids=None, pass_idx=None, pos_ids=None, scores_out=None,
+                   keep_out=None, score_stride=0, workspace=None, status=None, check=True,
+                   stream=None):
+    """One whole eviction pass (beacon: update -> score -> select -> compact;
+    random: score -> select -> compact), every layer/request/head at once."""
+    a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
+                   seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride)
+    need = bkv_workspace_size(cache, a)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=cache.device)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8)
+    st, own = _status(status, cache.device)
+    c = cache.struct()
+    code = _lib.bkv_evict_pass(ctypes.byref(c), ctypes.byref(a), _ptr(workspace),
+                               0 if workspace is None else workspace.numel(), _ptr(st),
+                               _stream(stream))
+    _check(code, "bkv_evict_pass")
+    if own and check:
+        check_status(st, "bkv_evict_pass", stream)
+    return st

@@ -1,0 +1,250 @@
+// abi.hip -- extern "C" entry points of libbeaconkv.so: synchronous argument
+// validation (nothing is enqueued on failure), then kernel launches on the
+// caller's stream.  No allocation, no global state.
+
+#include <limits.h>
+
+#include "bkv_internal.h"
+
+using namespace bkv;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t check_cache(const bkv_cache* cache, CacheView* v) {
+    if (!cache) return BKV_ERR_NULL;
+    if (!cache->k_pools || !cache->v_pools || !cache->block_table || !cache->seq_len ||
+        !cache->prompt_len)
+        return BKV_ERR_NULL;
+    if (cache->head_dim != kHeadDim || cache->block_size != kBlock) return BKV_ERR_UNSUPPORTED;
+    if (cache->n_layers < 1 || cache->n_requests < 1 || cache->n_kv_heads < 1 ||
+        cache->max_blocks < 1 || cache->num_blocks < 1)
+        return BKV_ERR_INVALID;
+    const int64_t hc = (int64_t)cache->n_layers * cache->n_requests * cache->n_kv_heads;
+    if (hc > INT_MAX || (int64_t)cache->max_blocks * kBlock > kMaxSlots ||
+        cache->num_blocks > INT_MAX)
+        return BKV_ERR_INVALID;
+    if (!aligned(cache->k_pools, 8) || !aligned(cache->v_pools, 8) ||
+        !aligned(cache->block_table, 4) || !aligned(cache->seq_len, 4) ||
+        !aligned(cache->prompt_len, 4))
+        return BKV_ERR_INVALID;
+    v->L = cache->n_layers;
+    v->R = cache->n_requests;
+    v->H = cache->n_kv_heads;
+    v->max_blocks = cache->max_blocks;
+    v->num_blocks = cache->num_blocks;
+    v->k_pools = cache->k_pools;
+    v->v_pools = cache->v_pools;
+    v->block_table = cache->block_table;
+    v->seq_len = cache->seq_len;
+    v->prompt_len = cache->prompt_len;
+    return BKV_OK;
+}
+
+int64_t head_caches(const CacheView& v) { return (int64_t)v.L * v.R * v.H; }
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? BKV_OK : BKV_ERR_HIP; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct PassLayout {
+    int stride;
+    size_t scores_off, keep_off, total;
+};
+
+int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
+    const int max_slots = v.max_blocks * kBlock;
+    const int stride = a->score_stride > 0 ? a->score_stride : max_slots;
+    if (stride > BKV_MAX_CANDIDATES) return BKV_ERR_INVALID;
+    if (a->budget < 1) return BKV_ERR_INVALID;
+    const size_t HC = (size_t)head_caches(v);
+    size_t off = 0;
+    L->stride = stride;
+    L->scores_off = L->keep_off = 0;
+    if (!a->scores_out) {
+        L->scores_off = off;
+        off = round_up(off + HC * (size_t)stride * 4, 256);
+    }
+    if (!a->keep_out) {
+        L->keep_off = off;
+        off = round_up(off + HC * (size_t)a->budget * 4, 256);
+    }
+    L->total = off;
+    return BKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t bkv_abi_version(void) { return BKV_ABI_VERSION; }
+
+const char* bkv_status_string(int32_t code) {
+    switch (code) {
+        case BKV_OK: return "ok";
+        case BKV_ERR_NULL: return "a required pointer is NULL";
+        case BKV_ERR_INVALID: return "invalid size, count, stride, alignment or keep list";
+        case BKV_ERR_BUDGET: return "a request's prompt length exceeds the budget";
+        case BKV_ERR_UNSUPPORTED: return "unsupported head_dim or block_size (need 128 and 16)";
+        case BKV_ERR_WORKSPACE: return "workspace missing or too small";
+        case BKV_ERR_HIP: return "HIP launch error";
+        case BKV_ERR_LENGTH: return "seq_len / prompt_len out of range";
+        case BKV_ERR_BLOCK_TABLE: return "block id outside the pool";
+        default: return "unknown status code";
+    }
+}
+
+int32_t bkv_beacon_update(int32_t n_head_caches, int32_t T, int32_t G, int32_t head_dim, int32_t K,
+                          const uint16_t* queries, float* beacons, int32_t* counts,
+                          int32_t* assign, bkv_stream_t stream) {
+    if (head_dim != kHeadDim) return BKV_ERR_UNSUPPORTED;
+    if (n_head_caches < 0 || T < 1 || G < 1 || K < 1 || K > BKV_MAX_BEACONS) return BKV_ERR_INVALID;
+    if ((int64_t)T * G > INT_MAX / kHeadDim) return BKV_ERR_INVALID;
+    if (n_head_caches == 0) return BKV_OK;
+    if (!queries || !beacons || !counts) return BKV_ERR_NULL;
+    if (!aligned(queries, 16) || !aligned(beacons, 16) || !aligned(counts, 4) ||
+        (assign && !aligned(assign, 4)))
+        return BKV_ERR_INVALID;
+    return hip_status(launch_beacon_update(n_head_caches, T, G, K, queries, beacons, counts, assign,
+                                           nullptr, Check{-1, -1, 0}, nullptr,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int32_t bkv_beacon_score(const bkv_cache* cache, const float* beacons, const int32_t* counts,
+                         int32_t K, int32_t window, float bonus, float* scores,
+                         int32_t score_stride, float* lse, int32_t* status, bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!beacons || !counts || !scores) return BKV_ERR_NULL;
+    if (K < 1 || K > BKV_MAX_BEACONS || score_stride < 1 || window < 0) return BKV_ERR_INVALID;
+    if (!aligned(beacons, 16) || !aligned(counts, 4) || !aligned(scores, 4) ||
+        (lse && !aligned(lse, 4)) || (status && !aligned(status, 4)))
+        return BKV_ERR_INVALID;
+    return hip_status(launch_beacon_score(v, beacons, counts, K, window, bonus, scores,
+                                          score_stride, lse, Check{-1, score_stride, 1}, status,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int32_t bkv_random_score(const bkv_cache* cache, uint64_t seed, const uint64_t* request_ids,
+                         const int32_t* pass_idx, uint32_t* scores, int32_t score_stride,
+                         int32_t* status, bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!request_ids || !pass_idx || !scores) return BKV_ERR_NULL;
+    if (score_stride < 1) return BKV_ERR_INVALID;
+    if (!aligned(request_ids, 8) || !aligned(pass_idx, 4) || !aligned(scores, 4) ||
+        (status && !aligned(status, 4)))
+        return BKV_ERR_INVALID;
+    return hip_status(launch_random_score(v, seed, request_ids, pass_idx, scores, score_stride,
+                                          Check{-1, score_stride, 0}, status,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int32_t bkv_topk_select(const bkv_cache* cache, const void* scores, int32_t score_kind,
+                        int32_t score_stride, int32_t budget, int32_t* keep_idx, int32_t* status,
+                        bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!scores || !keep_idx) return BKV_ERR_NULL;
+    if (score_kind != BKV_SCORE_F32 && score_kind != BKV_SCORE_U32) return BKV_ERR_INVALID;
+    if (score_stride < 1 || score_stride > BKV_MAX_CANDIDATES || budget < 1) return BKV_ERR_INVALID;
+    if (!aligned(scores, 4) || !aligned(keep_idx, 4) || (status && !aligned(status, 4)))
+        return BKV_ERR_INVALID;
+    return hip_status(launch_topk_select(v, scores, score_kind, score_stride, budget, keep_idx,
+                                         Check{budget, score_stride, 0}, status,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int32_t bkv_kv_compact(const bkv_cache* cache, const int32_t* keep_idx, int32_t budget,
+                       int32_t* pos_ids, int32_t pos_stride, int32_t* status,
+                       bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!keep_idx) return BKV_ERR_NULL;
+    if (budget < 1) return BKV_ERR_INVALID;
+    if (pos_ids && pos_stride < v.max_blocks * kBlock) return BKV_ERR_INVALID;
+    if (!aligned(keep_idx, 4) || (pos_ids && !aligned(pos_ids, 4)) ||
+        (status && !aligned(status, 4)))
+        return BKV_ERR_INVALID;
+    return hip_status(launch_kv_compact(v, keep_idx, budget, pos_ids, pos_stride,
+                                        Check{budget, -1, 1}, status,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, size_t* bytes) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!args || !bytes) return BKV_ERR_NULL;
+    PassLayout L;
+    e = pass_layout(v, args, &L);
+    if (e) return e;
+    *bytes = L.total;
+    return BKV_OK;
+}
+
+int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* workspace,
+                       size_t workspace_bytes, int32_t* status, bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!a) return BKV_ERR_NULL;
+    if (a->selector != BKV_SELECT_BEACON && a->selector != BKV_SELECT_RANDOM)
+        return BKV_ERR_INVALID;
+    PassLayout L;
+    e = pass_layout(v, a, &L);
+    if (e) return e;
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return BKV_ERR_WORKSPACE;
+    if (workspace && !aligned(workspace, 256)) return BKV_ERR_INVALID;
+    if (status && !aligned(status, 4)) return BKV_ERR_INVALID;
+    if (a->pos_ids && (a->pos_stride < v.max_blocks * kBlock || !aligned(a->pos_ids, 4)))
+        return BKV_ERR_INVALID;
+    if ((a->scores_out && !aligned(a->scores_out, 4)) || (a->keep_out && !aligned(a->keep_out, 4)))
+        return BKV_ERR_INVALID;
+    const bool beacon = a->selector == BKV_SELECT_BEACON;
+    if (beacon) {
+        if (!a->queries || !a->beacons || !a->counts) return BKV_ERR_NULL;
+        if (a->n_beacons < 1 || a->n_beacons > BKV_MAX_BEACONS || a->T < 1 || a->G < 1 ||
+            a->window < 0 || (int64_t)a->T * a->G > INT_MAX / kHeadDim)
+            return BKV_ERR_INVALID;
+        if (!aligned(a->queries, 16) || !aligned(a->beacons, 16) || !aligned(a->counts, 4) ||
+            (a->assign && !aligned(a->assign, 4)) || (a->lse && !aligned(a->lse, 4)))
+            return BKV_ERR_INVALID;
+    } else {
+        if (!a->request_ids || !a->pass_idx) return BKV_ERR_NULL;
+        if (!aligned(a->request_ids, 8) || !aligned(a->pass_idx, 4)) return BKV_ERR_INVALID;
+    }
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    void* sc = a->scores_out ? a->scores_out : ws + L.scores_off;
+    int32_t* keep = a->keep_out ? a->keep_out : reinterpret_cast<int32_t*>(ws + L.keep_off);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // every kernel applies every check, so a failing request is skipped by all steps
+    const Check all{a->budget, L.stride, 1};
+    const int HC = (int)head_caches(v);
+    hipError_t he;
+    if (beacon) {
+        he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
+                                  a->assign, &v, all, status, s);
+        if (he != hipSuccess) return BKV_ERR_HIP;
+        he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
+                                 static_cast<float*>(sc), L.stride, a->lse, all, status, s);
+        if (he != hipSuccess) return BKV_ERR_HIP;
+        he = launch_topk_select(v, sc, BKV_SCORE_F32, L.stride, a->budget, keep, all, status, s);
+    } else {
+        he = launch_random_score(v, a->seed, a->request_ids, a->pass_idx,
+                                 static_cast<uint32_t*>(sc), L.stride, all, status, s);
+        if (he != hipSuccess) return BKV_ERR_HIP;
+        he = launch_topk_select(v, sc, BKV_SCORE_U32, L.stride, a->budget, keep, all, status, s);
+    }
+    if (he != hipSuccess) return BKV_ERR_HIP;
+    he = launch_kv_compact(v, keep, a->budget, a->pos_ids, a->pos_stride, all, status, s);
+    return hip_status(he);
+}
+
+}  // extern "C"

@@ -1,0 +1,129 @@
+// bkv_internal.h -- shared device helpers of the HIP kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "beaconkv.h"
+
+namespace bkv {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 16;
+constexpr int kRowBytes = kHeadDim * 2;  // one bf16 key or value row
+constexpr int kWave = 64;
+
+// Kernel-argument copy of a bkv_cache (plain values, passed by value).
+struct CacheView {
+    int32_t L, R, H, max_blocks;
+    int64_t num_blocks;
+    const uint64_t* k_pools;
+    const uint64_t* v_pools;
+    const int32_t* block_table;
+    const int32_t* seq_len;
+    const int32_t* prompt_len;
+};
+
+struct HeadIdx {
+    int layer, req, head;
+};
+
+__device__ __forceinline__ HeadIdx split_hc(const CacheView& c, int hc) {
+    HeadIdx x;
+    x.head = hc % c.H;
+    const int lr = hc / c.H;
+    x.req = lr % c.R;
+    x.layer = lr / c.R;
+    return x;
+}
+
+__device__ __forceinline__ void raise_status(int32_t* status, int bits) {
+    if (status && bits) atomicOr(status, bits);
+}
+
+// Which per-request checks a kernel applies.  A standalone entry point checks
+// what its own kernel reads; inside a whole pass every kernel applies the union
+// of all checks, so a request that fails any of them is skipped by every step.
+struct Check {
+    int budget;     // < 0: no budget check
+    int cand_cap;   // < 0: no candidate-capacity check (N - P <= cand_cap)
+    int blocks;     // non-zero: validate pool alignment and every block id in use
+};
+
+// Validates request r.  Every thread of the block must call it (it
+// synchronises); the result is uniform.  Errors are OR-ed into *status by
+// thread 0.
+__device__ inline bool request_ok(const CacheView& c, int layer, int r, const Check& ck,
+                                  int32_t* status) {
+    const int N = c.seq_len[r];
+    const int P = c.prompt_len[r];
+    int err = 0;
+    if (P < 0 || N < P || N > c.max_blocks * kBlock) err |= 1 << BKV_ERR_LENGTH;
+    if (ck.budget >= 0 && P > ck.budget) err |= 1 << BKV_ERR_BUDGET;
+    if (ck.cand_cap >= 0 && !(err & (1 << BKV_ERR_LENGTH)) && N - P > ck.cand_cap)
+        err |= 1 << BKV_ERR_LENGTH;
+    bool bad = false;
+    if (ck.blocks) {
+        if (((c.k_pools[layer] | c.v_pools[layer]) & 15u) != 0) err |= 1 << BKV_ERR_INVALID;
+        const int nb = (err & (1 << BKV_ERR_LENGTH)) ? 0 : (N + kBlock - 1) / kBlock;
+        const int32_t* row = c.block_table + (size_t)r * c.max_blocks;
+        for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+            const int b = row[i];
+            bad |= (b < 0) || ((int64_t)b >= c.num_blocks);
+        }
+    }
+    bad = __syncthreads_or(bad);
+    if (bad) err |= 1 << BKV_ERR_BLOCK_TABLE;
+    if (err && threadIdx.x == 0) raise_status(status, err);
+    return err == 0;
+}
+
+// Address of the bf16 row of (block, head, row-in-block) in a layer pool.
+__device__ __forceinline__ size_t row_offset(int blk, int H, int h, int off) {
+    return (((size_t)blk * H + h) * kBlock + off) * kRowBytes;
+}
+
+// 16-byte loads/stores at a byte address in the global address space.  Pool
+// addresses arrive as integers; casting them straight to global pointers lets
+// the compiler emit global_load/store instead of generic flat accesses (which
+// would also wait on the LDS counter).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u32x4 global_cu32x4;
+typedef __attribute__((address_space(1))) u32x4 global_u32x4;
+__device__ __forceinline__ u32x4 load16(uint64_t addr) { return *(global_cu32x4*)addr; }
+__device__ __forceinline__ void store16(uint64_t addr, u32x4 v) { *(global_u32x4*)addr = v; }
+
+// Largest slot count of one request the kernels accept (block table staged in
+// LDS: 2048 blocks of 16 slots).
+constexpr int kMaxSlots = 32768;
+constexpr int kMaxBlocksPerReq = kMaxSlots / kBlock;
+
+// fp32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Host-side launchers (defined next to each kernel).  `cache` of the update
+// launcher is NULL for the standalone entry point (no request checks).
+hipError_t launch_beacon_update(int HC, int T, int G, int K, const uint16_t* q, float* beacons,
+                                int32_t* counts, int32_t* assign, const CacheView* cache,
+                                Check ck, int32_t* status, hipStream_t s);
+hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const int32_t* counts,
+                               int K, int window, float bonus, float* scores, int stride,
+                               float* lse, Check ck, int32_t* status, hipStream_t s);
+hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
+                               const int32_t* pass_idx, uint32_t* scores, int stride, Check ck,
+                               int32_t* status, hipStream_t s);
+hipError_t launch_topk_select(const CacheView& c, const void* scores, int kind, int stride,
+                              int budget, int32_t* keep, Check ck, int32_t* status,
+                              hipStream_t s);
+hipError_t launch_kv_compact(const CacheView& c, const int32_t* keep, int budget,
+                             int32_t* pos_ids, int pos_stride, Check ck, int32_t* status,
+                             hipStream_t s);
+
+}  // namespace bkv

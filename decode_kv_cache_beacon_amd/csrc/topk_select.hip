@@ -1,0 +1,167 @@
+// topk_select.hip -- per-head top-B selection with full prompt protection
+// (Random Attention article, section "Random Attention: 不判断重要性, 只随机保留":
+// prompt KV always kept, generated KV reduced to a per-head top-K; the budget
+// includes the prompt).
+//
+// One workgroup per head-cache.  The N - P candidate scores are staged in LDS
+// as unsigned 32-bit keys (non-negative fp32 scores order exactly like their
+// bit patterns).  An MSB-first radix select (four 8-bit digits, LDS histogram)
+// finds the (B-P)-th largest key T and how many keys equal to T must be kept;
+// equal keys are taken in slot order (earlier slot first).  Two block-wide
+// prefix scans (over "== T" and over "kept") then emit the kept slots in
+// ascending order, prompt first.  The selection is exact integer work, so the
+// result is bit-reproducible.
+
+#include "bkv_internal.h"
+
+namespace bkv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(v, o, kWave);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive prefix sum of one int per thread over the whole block, in thread
+// order.  Synchronises; s_wsum needs kWaves entries.
+__device__ int block_exclusive_scan(int v, int* s_wsum) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int w = threadIdx.x / kWave;
+    const int incl = wave_inclusive_scan(v);
+    if (lane == kWave - 1) s_wsum[w] = incl;
+    __syncthreads();
+    int off = 0;
+    for (int j = 0; j < w; ++j) off += s_wsum[j];
+    __syncthreads();  // s_wsum may be reused by the next scan
+    return off + incl - v;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
+                                                               const uint32_t* __restrict__ scores,
+                                                               int is_f32, int stride, int B,
+                                                               int32_t* __restrict__ keep, Check ck,
+                                                               int32_t* status) {
+    extern __shared__ uint32_t s_key[];  // [stride]
+    __shared__ int s_hist[256];
+    __shared__ int s_wsum[kWaves];
+    __shared__ uint32_t s_prefix;
+    __shared__ int s_need;
+
+    const int hc = blockIdx.x;
+    const HeadIdx x = split_hc(c, hc);
+    if (!request_ok(c, x.layer, x.req, ck, status)) return;
+    const int N = c.seq_len[x.req];
+    const int P = c.prompt_len[x.req];
+    int32_t* out = keep + (size_t)hc * B;
+    const int tid = threadIdx.x;
+
+    if (N <= B) {  // nothing to evict: keep every slot
+        for (int i = tid; i < B; i += kThreads) out[i] = (i < N) ? i : -1;
+        return;
+    }
+    const int m = N - P;  // candidates
+    const int k = B - P;  // candidates to keep, 0 <= k < m
+    for (int i = tid; i < P; i += kThreads) out[i] = i;
+    if (k == 0) return;
+
+    const uint32_t* src = scores + (size_t)hc * stride;
+    for (int i = tid; i < m; i += kThreads) {
+        uint32_t v = src[i];
+        if (is_f32 && (v >> 31)) v = 0;  // negative fp32 scores rank as 0
+        s_key[i] = v;
+    }
+
+    // MSB-first radix select of the k-th largest key.
+    uint32_t prefix = 0, mask = 0;
+    int need = k;  // rank still to locate inside the keys matching `prefix`
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += kThreads) s_hist[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < m; i += kThreads) {
+            const uint32_t v = s_key[i];
+            if ((v & mask) == prefix) atomicAdd(&s_hist[(v >> shift) & 255u], 1);
+        }
+        __syncthreads();
+        if (tid < kWave) {
+            // lane l owns digits 255-4l .. 252-4l (descending)
+            int cnt[4], local = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                cnt[j] = s_hist[255 - 4 * tid - j];
+                local += cnt[j];
+            }
+            const int incl = wave_inclusive_scan(local);
+            const int excl = incl - local;  // keys with a larger digit
+            if (excl < need && need <= incl) {
+                int rem = need - excl, above = excl, digit = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (rem <= cnt[j]) {
+                        digit = 255 - 4 * tid - j;
+                        break;
+                    }
+                    rem -= cnt[j];
+                    above += cnt[j];
+                }
+                s_prefix = prefix | ((uint32_t)digit << shift);
+                s_need = need - above;
+            }
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        need = s_need;
+        mask |= 0xFFu << shift;
+    }
+    const uint32_t T = prefix;  // the k-th largest key; `need` copies of T are kept
+
+    // Each thread owns one contiguous run of candidates (slot order).
+    const int seg = (m + kThreads - 1) / kThreads;
+    const int lo = min(tid * seg, m), hi = min(lo + seg, m);
+    int eq = 0;
+    for (int i = lo; i < hi; ++i) eq += (s_key[i] == T);
+    const int eq_before = block_exclusive_scan(eq, s_wsum);
+    int kept = 0, e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+        const uint32_t v = s_key[i];
+        const bool take = v > T || (v == T && e < need);
+        e += (v == T);
+        kept += take;
+    }
+    int o = P + block_exclusive_scan(kept, s_wsum);
+    e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+        const uint32_t v = s_key[i];
+        const bool take = v > T || (v == T && e < need);
+        e += (v == T);
+        if (take && o < B) out[o++] = P + i;  // o < B always holds; the bound is defensive
+    }
+}
+
+}  // namespace
+
+hipError_t launch_topk_select(const CacheView& c, const void* scores, int kind, int stride,
+                              int budget, int32_t* keep, Check ck, int32_t* status,
+                              hipStream_t s) {
+    const int HC = c.L * c.R * c.H;
+    if (HC == 0) return hipSuccess;
+    const size_t lds = (size_t)stride * sizeof(uint32_t);
+    if (lds > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(topk_select_kernel, dim3(HC), dim3(kThreads), lds, s, c,
+                       static_cast<const uint32_t*>(scores), kind == BKV_SCORE_F32 ? 1 : 0,
+                       stride, budget, keep, ck, status);
+    return hipGetLastError();
+}
+
+}  // namespace bkv

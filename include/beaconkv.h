@@ -1,0 +1,227 @@
+/*
+ * beaconkv.h -- C ABI of libbeaconkv.so: the decode-time KV-cache eviction
+ * pass (beacon maintenance, beacon scoring, random scoring, top-B selection,
+ * order-preserving compaction) as hand-written HIP kernels for MI355X
+ * (gfx950, CDNA4).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers owned by the caller (for example
+ *    the storage of torch tensors).  The library never allocates or frees
+ *    memory and keeps no global or static state; calls are reentrant.
+ *  - Work is enqueued asynchronously on the caller's HIP stream (`stream`,
+ *    a hipStream_t; NULL means the legacy default stream).  Outputs are valid
+ *    once that stream has been synchronised.
+ *  - Return value: BKV_OK, or a host-detected error code.  A host-detected
+ *    error enqueues nothing (atomic failure: no buffer is touched).
+ *  - `status` (nullable) is a caller-zeroed device int32.  Kernels OR the bit
+ *    (1 << code) into it for every error they detect from device-resident data
+ *    (lengths, block ids, keep lists).  A head-cache whose request fails such a
+ *    check is left untouched by that kernel (and, inside bkv_evict_pass, by
+ *    every kernel of the pass).
+ *  - Head-cache order: hc = (layer * n_requests + request) * n_kv_heads + head,
+ *    HC = n_layers * n_requests * n_kv_heads.  Per-head-cache arrays are
+ *    indexed [hc][...].
+ *  - bf16 values are passed as uint16_t bit patterns.
+ *  - Only head_dim == 128 and block_size == 16 are supported.
+ *
+ * The method (pages cited by title and section):
+ *  - BeaconKV explainer ("BeaconKV: 用"信标查询"指导 KV cache 压缩",
+ *    papers.ananclaw.com), section 3.2: each new decode query is assigned to
+ *    its nearest beacon and the beacons are updated incrementally; section
+ *    3.3: the beacon state is O(K), not O(sequence).
+ *  - BeaconKV abstract (chatpaper.ai): beacons are compact representatives of
+ *    global query clusters, used to anticipate which KV pairs are revisited.
+ *  - Random Attention article ("随机保留 KV Cache 竟不输精心设计的 eviction
+ *    策略?", aiinking.com), section "Random Attention: 不判断重要性, 只随机保留":
+ *    the prompt's KV is always kept, the generated KV is sampled independently
+ *    per head and the top-K kept, at the cost of one random draw and one
+ *    top-K; section "发现四": every selector ends in the same cache compaction,
+ *    run for a batch of requests at a synchronized point every 64 tokens.
+ *  Rules the pages leave open are fixed as follows (see each function):
+ *  cosine nearest beacon with ties to the lowest row, MacQueen fill of empty
+ *  rows, fp32 running-mean update; score(n) = max over live beacons of the
+ *  softmax over all N slots of bf16(b)·k/sqrt(d), plus `bonus` on the last
+ *  `window` slots; budget B includes the prompt; ties go to the earlier slot;
+ *  Philox4x64-10 (Salmon et al., SC'11) for the random selector.
+ */
+#ifndef BEACONKV_H
+#define BEACONKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BKV_ABI_VERSION 1
+
+typedef void* bkv_stream_t; /* hipStream_t */
+
+/* Return / status codes.  Device-detected codes appear in *status as bits. */
+enum {
+    BKV_OK = 0,
+    BKV_ERR_NULL = 1,        /* a required pointer is NULL */
+    BKV_ERR_INVALID = 2,     /* bad size, count, stride or alignment; or (device) a keep
+                                list that is not strictly ascending inside [0, N) */
+    BKV_ERR_BUDGET = 3,      /* (device) a request's prompt length exceeds the budget */
+    BKV_ERR_UNSUPPORTED = 4, /* head_dim != 128 or block_size != 16 */
+    BKV_ERR_WORKSPACE = 5,   /* workspace missing or smaller than bkv_workspace_size */
+    BKV_ERR_HIP = 6,         /* a HIP launch failed (hipGetLastError) */
+    BKV_ERR_LENGTH = 7,      /* (device) seq_len / prompt_len out of range */
+    BKV_ERR_BLOCK_TABLE = 8, /* (device) a block id outside [0, num_blocks) */
+};
+
+enum { BKV_SCORE_F32 = 0, BKV_SCORE_U32 = 1 };           /* score buffer element type */
+enum { BKV_SELECT_BEACON = 0, BKV_SELECT_RANDOM = 1 };   /* selector of bkv_evict_pass */
+
+#define BKV_MAX_BEACONS 256
+#define BKV_MAX_CANDIDATES 32768 /* largest score_stride bkv_topk_select accepts */
+
+/* A paged bf16 KV cache (vLLM-style pools, one K and one V pool per layer).
+ * Layer pool l holds bf16 [num_blocks][n_kv_heads][block_size][head_dim];
+ * slot n of request r, head h lives in block block_table[r][n / block_size]
+ * at row n % block_size.  A dense cache is an identity block table.  Every
+ * pool address must be 16-byte aligned. */
+typedef struct bkv_cache {
+    int32_t n_layers;
+    int32_t n_requests;
+    int32_t n_kv_heads;
+    int32_t head_dim;             /* must be 128 */
+    int32_t block_size;           /* must be 16 */
+    int32_t max_blocks;           /* columns of block_table */
+    int64_t num_blocks;           /* physical blocks in every layer pool */
+    const uint64_t* k_pools;      /* device [n_layers] device addresses of K pools */
+    const uint64_t* v_pools;      /* device [n_layers] device addresses of V pools */
+    const int32_t* block_table;   /* device [n_requests][max_blocks] */
+    const int32_t* seq_len;       /* device [n_requests] N: valid slots [0, N) */
+    const int32_t* prompt_len;    /* device [n_requests] P: prompt slots [0, P) */
+} bkv_cache;
+
+/* ABI version of the loaded library (BKV_ABI_VERSION when it was built). */
+int32_t bkv_abi_version(void);
+
+/* Static English text of a code; never NULL. */
+const char* bkv_status_string(int32_t code);
+
+/* a1 -- Beacon maintenance (BeaconKV explainer, section 3.2: nearest beacon,
+ * incremental update).  For each of HC head-caches, absorbs the T*G buffered
+ * decode queries queries[hc][t][g][:] (bf16, 128 wide) in (t, then g) order:
+ *   - if some row has count 0, the smallest such row j takes the query:
+ *     beacons[hc][j] = x exactly, counts[hc][j] = 1;
+ *   - otherwise j = the row of highest cosine(x, b_j) (ties -> lowest j; a
+ *     zero norm on either side counts as cosine 0), then counts[j] += 1 and
+ *     b_j = b_j + (x - b_j) / counts[j], with IEEE fp32 subtract, divide and
+ *     add (no fused multiply-add; bit-exact).
+ * beacons fp32 [HC][K][128] and counts int32 [HC][K] are updated in place;
+ * assign (nullable) int32 [HC][T*G] receives every chosen row.  Cosines are
+ * evaluated in fp32, so on a near tie the chosen row is the best to within
+ * fp32 rounding of the cosines.  1 <= K <= 256, T*G >= 1.  queries and
+ * beacons must be 16-byte aligned. */
+int32_t bkv_beacon_update(int32_t n_head_caches, int32_t T, int32_t G, int32_t head_dim,
+                          int32_t K, const uint16_t* queries, float* beacons, int32_t* counts,
+                          int32_t* assign, bkv_stream_t stream);
+
+/* a2/a3 -- Beacon scoring of every cached key (the traversal of the paged KV
+ * state that content-dependent selectors need; Random Attention article,
+ * section "发现四").  With live beacons J = {j : counts[hc][j] > 0} rounded to
+ * bf16 (round to nearest even) and s_jn = (bf16(b_j) . k_n) / sqrt(128)
+ * accumulated in fp32:
+ *   lse_j    = log sum_{n < N} exp(s_jn)                 (all N slots)
+ *   score(n) = max_{j in J} exp(s_jn - lse_j) + bonus * [n >= N - window]
+ * for n in [P, N), written to scores[hc * score_stride + (n - P)] (fp32).
+ * An empty J gives 0 + bonus.  lse (nullable) fp32 [HC][K] receives lse_j
+ * (natural log; NaN for rows outside J).  Requires N - P <= score_stride for
+ * every request (device-checked: BKV_ERR_LENGTH).  The keys are read twice
+ * (the second read is expected to hit the GPU caches). */
+int32_t bkv_beacon_score(const bkv_cache* cache, const float* beacons, const int32_t* counts,
+                         int32_t K, int32_t window, float bonus, float* scores,
+                         int32_t score_stride, float* lse, int32_t* status,
+                         bkv_stream_t stream);
+
+/* a4 -- Random-selector scores (Random Attention article, section "Random
+ * Attention": independent per-head random retention; no key is read).  For
+ * slot n in [P, N) of head-cache (layer, r, head):
+ *   scores[hc * score_stride + (n - P)] = high 32 bits of word (n mod 4) of
+ *   Philox4x64-10(counter = (n div 4, pass_idx[r], (layer << 32) | head,
+ *                  request_ids[r]), key = (seed, 0)).
+ * request_ids uint64 [n_requests], pass_idx int32 [n_requests] are device
+ * arrays; a new pass index gives fresh draws. */
+int32_t bkv_random_score(const bkv_cache* cache, uint64_t seed, const uint64_t* request_ids,
+                         const int32_t* pass_idx, uint32_t* scores, int32_t score_stride,
+                         int32_t* status, bkv_stream_t stream);
+
+/* a5 -- Top-B selection with full prompt protection (Random Attention article,
+ * section "Random Attention": the prompt is always kept, the rest is a per-head
+ * top-K).  The budget includes the prompt.  Per head-cache, keep_idx[hc][:]
+ * (int32 [HC][budget]) receives the kept slots in ascending order:
+ *   N <= budget : 0..N-1, then -1 padding;
+ *   P <= budget < N : [0, P) plus the budget - P best candidates of [P, N) by
+ *                     (score descending, slot ascending);
+ *   P > budget : device error BKV_ERR_BUDGET, row untouched.
+ * score_kind BKV_SCORE_F32 compares non-negative fp32 scores (negative values
+ * count as 0), BKV_SCORE_U32 unsigned 32-bit draws; candidates are read from
+ * scores[hc * score_stride + (n - P)].  score_stride <= BKV_MAX_CANDIDATES.
+ * The selection is an exact radix select: results are bit-reproducible. */
+int32_t bkv_topk_select(const bkv_cache* cache, const void* scores, int32_t score_kind,
+                        int32_t score_stride, int32_t budget, int32_t* keep_idx,
+                        int32_t* status, bkv_stream_t stream);
+
+/* a6 -- Cache compaction (Random Attention article, section "发现四": the one
+ * step every selector shares).  In place, for i < min(N, budget):
+ *   K[i] <- K[keep[i]], V[i] <- V[keep[i]]   (every layer pool, per head)
+ *   pos_ids[hc][i] <- pos_ids[hc][keep[i]]   (when pos_ids is not NULL)
+ * through the block table, preserving order.  The keep list must be strictly
+ * ascending inside [0, N) (device-checked: BKV_ERR_INVALID, head-cache left
+ * untouched); slots past min(N, budget) keep stale data and can be released by
+ * the caller (every head keeps the same count, so whole tail blocks free up).
+ * seq_len is not modified. */
+int32_t bkv_kv_compact(const bkv_cache* cache, const int32_t* keep_idx, int32_t budget,
+                       int32_t* pos_ids, int32_t pos_stride, int32_t* status,
+                       bkv_stream_t stream);
+
+/* a7 -- One whole eviction pass at a synchronized batch point: maintenance,
+ * scoring, selection and compaction for every layer, request and head. */
+typedef struct bkv_pass_args {
+    int32_t selector;          /* BKV_SELECT_BEACON or BKV_SELECT_RANDOM */
+    int32_t budget;            /* B, prompt included */
+    int32_t score_stride;      /* 0 -> max_blocks * block_size */
+    /* beacon selector */
+    int32_t n_beacons;         /* K */
+    int32_t T, G;              /* buffered decode steps, query heads per KV head */
+    int32_t window;            /* recent-window length W */
+    float bonus;               /* recent-window bonus */
+    const uint16_t* queries;   /* bf16 [HC][T][G][128] */
+    float* beacons;            /* fp32 [HC][K][128], updated */
+    int32_t* counts;           /* int32 [HC][K], updated */
+    int32_t* assign;           /* nullable int32 [HC][T*G] */
+    float* lse;                /* nullable fp32 [HC][K] */
+    /* random selector */
+    uint64_t seed;
+    const uint64_t* request_ids; /* device [n_requests] */
+    const int32_t* pass_idx;     /* device [n_requests] */
+    /* optional outputs / buffers */
+    int32_t* pos_ids;          /* nullable int32 [HC][pos_stride], compacted with the cache */
+    int32_t pos_stride;
+    void* scores_out;          /* nullable [HC][score_stride] scores; else workspace */
+    int32_t* keep_out;         /* nullable [HC][budget] keep lists; else workspace */
+} bkv_pass_args;
+
+/* Bytes of workspace bkv_evict_pass needs for these arguments (the score and
+ * keep buffers it is not given).  The workspace is a caller-owned device
+ * buffer aligned to 256 bytes. */
+int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, size_t* bytes);
+
+/* Runs, on `stream`: (beacon) a1 -> a2/a3 -> a5 -> a6, or (random) a4 -> a5 -> a6.
+ * A request that fails a device check (lengths, block ids, budget) is left
+ * entirely untouched -- beacons, counts, cache and pos_ids -- and flagged in
+ * *status. */
+int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* args, void* workspace,
+                       size_t workspace_bytes, int32_t* status, bkv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BEACONKV_H */

@@ -190,10 +190,9 @@ def kv_compact(rows, keep):
 def gather_paged(pool, block_row, head, n_slots, block_size=16):
     """Dense rows [n_slots][d] of one head from a paged pool [blocks][H][bs][d]."""
     pool = np.asarray(pool)
-    out = np.zeros((n_slots, pool.shape[-1]), pool.dtype)
-    for s in range(n_slots):
-        out[s] = pool[int(block_row[s // block_size]), head, s % block_size]
-    return out
+    slots = np.arange(n_slots)
+    blocks = np.asarray(block_row, np.int64)[slots // block_size]
+    return np.ascontiguousarray(pool[blocks, head, slots % block_size])
 
 
 # ---------------------------------------------------------------- whole pass

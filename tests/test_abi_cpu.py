@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: exports match the header, and host-side
+validation rejects bad arguments before anything is launched (CPU only)."""
+import ctypes
+import re
+import os
+
+import pytest
+
+from decode_kv_cache_beacon_amd import beaconkv as bk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "beaconkv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(bkv_\w+)\s*\(", src, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 9, names
+    lib = ctypes.CDLL(bk.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(bk.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 1
+    for code in range(0, 9):
+        s = bk.bkv_status_string(code)
+        assert s and s != "unknown status code"
+    assert bk.bkv_status_string(99) == "unknown status code"
+
+
+FAKE = 0x100000  # never dereferenced: validation fails before any launch
+
+
+def _cache(**kw):
+    c = dict(n_layers=2, n_requests=3, n_kv_heads=8, head_dim=128, block_size=16, max_blocks=10,
+             num_blocks=30, k_pools=FAKE, v_pools=FAKE, block_table=FAKE, seq_len=FAKE,
+             prompt_len=FAKE)
+    c.update(kw)
+    return bk.bkv_cache(**c)
+
+
+def _score(cache, K=64, stride=160, beacons=FAKE, counts=FAKE, scores=FAKE, window=64):
+    return bk._lib.bkv_beacon_score(ctypes.byref(cache), beacons, counts, K, window, 1.0, scores,
+                                    stride, None, None, None)
+
+
+def test_beacon_update_validation():
+    f = bk._lib.bkv_beacon_update
+    assert f(4, 8, 2, 64, 16, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_UNSUPPORTED
+    assert f(4, 8, 2, 128, 0, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert f(4, 8, 2, 128, 257, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert f(4, 0, 2, 128, 16, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert f(-1, 8, 2, 128, 16, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert f(4, 8, 2, 128, 16, None, FAKE, FAKE, None, None) == bk.BKV_ERR_NULL
+    assert f(4, 8, 2, 128, 16, FAKE + 4, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID  # misaligned
+    assert f(0, 8, 2, 128, 16, None, None, None, None, None) == bk.BKV_OK              # nothing to do
+
+
+def test_cache_validation():
+    assert _score(_cache(head_dim=64)) == bk.BKV_ERR_UNSUPPORTED
+    assert _score(_cache(block_size=32)) == bk.BKV_ERR_UNSUPPORTED
+    assert _score(_cache(k_pools=None)) == bk.BKV_ERR_NULL
+    assert _score(_cache(block_table=None)) == bk.BKV_ERR_NULL
+    assert _score(_cache(n_layers=0)) == bk.BKV_ERR_INVALID
+    assert _score(_cache(num_blocks=0)) == bk.BKV_ERR_INVALID
+    assert _score(_cache(seq_len=FAKE + 2)) == bk.BKV_ERR_INVALID
+    assert _score(_cache(n_layers=2**16, n_requests=2**12, n_kv_heads=8)) == bk.BKV_ERR_INVALID
+    assert bk._lib.bkv_beacon_score(None, FAKE, FAKE, 8, 64, 1.0, FAKE, 16, None, None,
+                                    None) == bk.BKV_ERR_NULL
+
+
+def test_score_argument_validation():
+    c = _cache()
+    assert _score(c, K=0) == bk.BKV_ERR_INVALID
+    assert _score(c, K=300) == bk.BKV_ERR_INVALID
+    assert _score(c, stride=0) == bk.BKV_ERR_INVALID
+    assert _score(c, window=-1) == bk.BKV_ERR_INVALID
+    assert _score(c, beacons=None) == bk.BKV_ERR_NULL
+    assert _score(c, beacons=FAKE + 8) == bk.BKV_ERR_INVALID
+    assert _score(_cache(max_blocks=4096)) == bk.BKV_ERR_INVALID   # > 32768 slots
+
+
+def test_select_compact_random_validation():
+    c = _cache()
+    sel = bk._lib.bkv_topk_select
+    assert sel(ctypes.byref(c), FAKE, 7, 160, 64, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert sel(ctypes.byref(c), FAKE, 0, 0, 64, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert sel(ctypes.byref(c), FAKE, 0, 40000, 64, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert sel(ctypes.byref(c), FAKE, 0, 160, 0, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert sel(ctypes.byref(c), None, 0, 160, 64, FAKE, None, None) == bk.BKV_ERR_NULL
+    cmp_ = bk._lib.bkv_kv_compact
+    assert cmp_(ctypes.byref(c), None, 64, None, 0, None, None) == bk.BKV_ERR_NULL
+    assert cmp_(ctypes.byref(c), FAKE, 0, None, 0, None, None) == bk.BKV_ERR_INVALID
+    assert cmp_(ctypes.byref(c), FAKE, 64, FAKE, 100, None, None) == bk.BKV_ERR_INVALID  # pos stride < 160
+    rnd = bk._lib.bkv_random_score
+    assert rnd(ctypes.byref(c), 1, None, FAKE, FAKE, 160, None, None) == bk.BKV_ERR_NULL
+    assert rnd(ctypes.byref(c), 1, FAKE, FAKE, FAKE, 0, None, None) == bk.BKV_ERR_INVALID
+
+
+def test_workspace_and_pass_validation():
+    c = _cache()
+    a = bk.bkv_pass_args()
+    a.selector, a.budget = bk.BKV_SELECT_RANDOM, 64
+    n = ctypes.c_size_t(0)
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
+    HC = 2 * 3 * 8
+    assert n.value >= HC * 160 * 4 + HC * 64 * 4
+    a.scores_out, a.keep_out = FAKE, FAKE
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value == 0
+    a.scores_out, a.keep_out = None, None
+    ev = bk._lib.bkv_evict_pass
+    assert ev(ctypes.byref(c), ctypes.byref(a), None, 0, None, None) == bk.BKV_ERR_WORKSPACE
+    a.request_ids = None
+    a.pass_idx = FAKE
+    big = 1 << 40
+    assert ev(ctypes.byref(c), ctypes.byref(a), FAKE, big, None, None) == bk.BKV_ERR_NULL
+    a.selector = 5
+    assert ev(ctypes.byref(c), ctypes.byref(a), FAKE, big, None, None) == bk.BKV_ERR_INVALID
+    a.selector = bk.BKV_SELECT_BEACON
+    a.queries = a.beacons = a.counts = FAKE
+    a.n_beacons, a.T, a.G = 0, 64, 4
+    assert ev(ctypes.byref(c), ctypes.byref(a), FAKE, big, None, None) == bk.BKV_ERR_INVALID
+    a.n_beacons = 64
+    a.budget = 0
+    assert ev(ctypes.byref(c), ctypes.byref(a), FAKE, big, None, None) == bk.BKV_ERR_INVALID
+    a.budget = 64
+    assert ev(ctypes.byref(c), ctypes.byref(a), FAKE + 16, big, None, None) == bk.BKV_ERR_INVALID
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(2, 4, 1, 128, dtype=torch.bfloat16)
+    b = torch.zeros(2, 8, 128)
+    c = torch.zeros(2, 8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        bk.bkv_beacon_update(q, b, c)

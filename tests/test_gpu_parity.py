@@ -1,0 +1,412 @@
+"""GPU parity: every kernel behind the C ABI against the CPU oracle, on the same
+seeded inputs (sizes the oracle finishes in seconds; several MFMA tiles and a
+ragged tail).  Bit-exact for draws, keep lists and moved bytes; 1e-3 relative
+for float scores; teacher-forced for beacon assignment."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_kv_cache_beacon_amd import synth
+from tests.gpu_util import (ASSIGN_TOL, check_scores, check_selection, device_cache, hc_index,
+                            host_pools, keep_rows)
+
+pytestmark = pytest.mark.gpu
+
+bk = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    global bk
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from decode_kv_cache_beacon_amd import beaconkv
+    bk = beaconkv
+    torch.cuda.init()
+    yield
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def small(name="serving_r128", **kw):
+    return synth.WORKLOADS[name].with_(**kw)
+
+
+def head_iter(cache):
+    L, R, H = cache.n_layers, cache.n_requests, cache.n_kv_heads
+    for layer in range(L):
+        for r in range(R):
+            for h in range(H):
+                yield hc_index(R, H, layer, r, h), layer, r, h
+
+
+def random_keep(cache, B, N, P, seed=7):
+    """Keep lists chosen by the oracle's random selector (inputs for compaction)."""
+    keep = np.full((cache.n_head_caches, B), -1, np.int32)
+    for hc, layer, r, h in head_iter(cache):
+        u = oracle.random_score(seed, r, 0, layer, h, N[r], P[r])
+        k = oracle.topk_select(u, N[r], P[r], B)
+        keep[hc, :len(k)] = k
+    return keep
+
+
+# ------------------------------------------------------------------ compaction
+@pytest.mark.parametrize("case", ["paged", "dense", "ragged"])
+def test_compact_matches_oracle_gather(case):
+    say("compact", case)
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=512, prompt_len=200, seq_len=576,
+               paged=case != "dense")
+    batch = synth.make_batch(wl)
+    N = [576, 555, 301] if case == "ragged" else [576] * 3
+    P = [200, 200, 37] if case == "ragged" else [200] * 3
+    B = 512
+    cache = device_cache(batch, N, P)
+    k_in, v_in = host_pools(cache)
+    bt = batch.block_table.numpy()
+    keep = random_keep(cache, B, N, P)
+    HC, S = cache.n_head_caches, cache.max_slots
+    pos = (np.arange(HC * S, dtype=np.int32).reshape(HC, S) * 7 + 3).astype(np.int32)
+    pos_dev = torch.from_numpy(pos).cuda()
+    bk.bkv_kv_compact(cache, torch.from_numpy(keep).cuda(), B, pos_ids=pos_dev)
+    k_out, v_out = host_pools(cache)
+    pos_out = pos_dev.cpu().numpy()
+    for hc, layer, r, h in head_iter(cache):
+        kp = keep_rows(keep[hc])
+        nk = len(kp)
+        for src, dst in ((k_in, k_out), (v_in, v_out)):
+            dense_in = oracle.gather_paged(src[layer], bt[r], h, N[r])
+            dense_out = oracle.gather_paged(dst[layer], bt[r], h, N[r])
+            assert np.array_equal(dense_out[:nk], oracle.kv_compact(dense_in, kp)), (hc, case)
+            assert np.array_equal(dense_out[nk:], dense_in[nk:]), (hc, "tail changed")
+        assert np.array_equal(pos_out[hc, :nk], pos[hc][kp])
+        assert np.array_equal(pos_out[hc, nk:], pos[hc, nk:])
+
+
+def test_compact_rejects_bad_keep_lists():
+    say("compact bad keep")
+    wl = small(n_layers=1, n_requests=2, n_kv_heads=2, budget=64, prompt_len=16, seq_len=128)
+    batch = synth.make_batch(wl)
+    cache = device_cache(batch)
+    k_in, _ = host_pools(cache)
+    keep = np.tile(np.arange(64, dtype=np.int32), (cache.n_head_caches, 1)) + 1
+    keep[0, 5], keep[0, 6] = keep[0, 6], keep[0, 5]      # not ascending
+    keep[3, 63] = 128                                      # outside [0, N)
+    st = bk.bkv_kv_compact(cache, torch.from_numpy(keep).cuda(), 64, check=False)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 1 << bk.BKV_ERR_INVALID
+    k_out, _ = host_pools(cache)
+    bt = batch.block_table.numpy()
+    for hc, layer, r, h in head_iter(cache):
+        a = oracle.gather_paged(k_in[layer], bt[r], h, 128)
+        b = oracle.gather_paged(k_out[layer], bt[r], h, 128)
+        if hc in (0, 3):
+            assert np.array_equal(a, b), hc                # refused: untouched
+        else:
+            assert np.array_equal(b[:64], a[1:65]), hc     # valid lists still applied
+
+
+# ------------------------------------------------------------------ random scores
+def test_random_scores_bit_exact():
+    say("philox")
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=4, budget=512, prompt_len=200, seq_len=576)
+    batch = synth.make_batch(wl)
+    N, P = [576, 555, 301], [200, 203, 0]
+    cache = device_cache(batch, N, P)
+    seed = 0xC0FFEE_1234_5678
+    rid = torch.tensor([11, 2**40 + 5, 3], dtype=torch.int64).cuda()
+    pss = torch.tensor([0, 7, 123456], dtype=torch.int32).cuda()
+    stride = 600
+    sc = torch.full((cache.n_head_caches, stride), -1, dtype=torch.int32).cuda()
+    bk.bkv_random_score(cache, seed, rid, pss, sc)
+    got = sc.cpu().numpy().view(np.uint32)
+    for hc, layer, r, h in head_iter(cache):
+        ref = oracle.random_score(seed, int(rid[r]), int(pss[r]), layer, h, N[r], P[r])
+        assert np.array_equal(got[hc, :N[r] - P[r]], ref), hc
+        assert np.all(got[hc, N[r] - P[r]:] == 0xFFFFFFFF), hc
+
+
+# ------------------------------------------------------------------ selection
+def test_select_bit_exact_on_draws_and_tied_floats():
+    say("select u32/f32")
+    wl = small(n_layers=1, n_requests=4, n_kv_heads=4, budget=512, prompt_len=200, seq_len=1500)
+    batch = synth.make_batch(wl)
+    N, P, B = [576, 1500, 700, 513], [200, 0, 511, 100], 512
+    cache = device_cache(batch, N, P)
+    stride = 1500
+    rid = torch.arange(4, dtype=torch.int64).cuda()
+    pss = torch.zeros(4, dtype=torch.int32).cuda()
+    u = torch.zeros((cache.n_head_caches, stride), dtype=torch.int32).cuda()
+    bk.bkv_random_score(cache, 99, rid, pss, u)
+    keep = torch.full((cache.n_head_caches, B), -7, dtype=torch.int32).cuda()
+    bk.bkv_topk_select(cache, u, B, keep)
+    un = u.cpu().numpy().view(np.uint32)
+    kn = keep.cpu().numpy()
+    for hc, layer, r, h in head_iter(cache):
+        ref = oracle.topk_select(un[hc, :N[r] - P[r]], N[r], P[r], B)
+        assert np.array_equal(keep_rows(kn[hc]), ref), hc
+    # fp32 scores with heavy ties (few distinct values) and window-like values
+    rng = np.random.default_rng(5)
+    f = (np.round(rng.random((cache.n_head_caches, stride)) * 6) / 6).astype(np.float32)
+    f[:, ::5] += 1.0
+    f[:, 7] = 0.0
+    fs = torch.from_numpy(f).cuda()
+    bk.bkv_topk_select(cache, fs, B, keep)
+    kn = keep.cpu().numpy()
+    for hc, layer, r, h in head_iter(cache):
+        ref = oracle.topk_select(f[hc, :N[r] - P[r]].astype(np.float64), N[r], P[r], B)
+        assert np.array_equal(keep_rows(kn[hc]), ref), hc
+
+
+def test_select_edge_cases():
+    say("select edges")
+    wl = small(n_layers=1, n_requests=5, n_kv_heads=2, budget=512, prompt_len=200, seq_len=608)
+    batch = synth.make_batch(wl)
+    # (N, P): normal, N <= B, P == B, P > B (refused), empty
+    N, P, B = [576, 300, 576, 600, 0], [200, 100, 512, 600, 0], 512
+    cache = device_cache(batch, N, P)
+    stride = 608
+    rng = np.random.default_rng(3)
+    f = rng.random((cache.n_head_caches, stride)).astype(np.float32)
+    keep = torch.full((cache.n_head_caches, B), -7, dtype=torch.int32).cuda()
+    st = bk.bkv_topk_select(cache, torch.from_numpy(f).cuda(), B, keep, check=False)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 1 << bk.BKV_ERR_BUDGET
+    kn = keep.cpu().numpy()
+    for hc, layer, r, h in head_iter(cache):
+        if r == 3:
+            assert np.all(kn[hc] == -7), "refused request must stay untouched"
+            continue
+        ref = oracle.topk_select(f[hc, :N[r] - P[r]].astype(np.float64), N[r], P[r], B)
+        assert np.array_equal(keep_rows(kn[hc]), ref), (hc, r)
+        assert np.all(kn[hc, len(ref):] == -1), (hc, r)
+
+
+def test_select_one_shot_32k_candidates():
+    say("select 32k")
+    wl = small(n_layers=1, n_requests=1, n_kv_heads=2, budget=2048, prompt_len=512,
+               seq_len=32768, n_clusters=4)
+    batch = synth.make_batch(wl)
+    cache = device_cache(batch)
+    stride = 32768
+    rid = torch.tensor([5], dtype=torch.int64).cuda()
+    pss = torch.tensor([3], dtype=torch.int32).cuda()
+    u = torch.zeros((cache.n_head_caches, stride), dtype=torch.int32).cuda()
+    bk.bkv_random_score(cache, 1, rid, pss, u)
+    keep = torch.zeros((cache.n_head_caches, 2048), dtype=torch.int32).cuda()
+    bk.bkv_topk_select(cache, u, 2048, keep)
+    un, kn = u.cpu().numpy().view(np.uint32), keep.cpu().numpy()
+    for hc in range(cache.n_head_caches):
+        ref = oracle.topk_select(un[hc, :32768 - 512], 32768, 512, 2048)
+        assert np.array_equal(kn[hc], ref), hc
+
+
+# ------------------------------------------------------------------ maintenance
+@pytest.mark.parametrize("K,prewarm,G,T", [(5, False, 4, 16), (64, True, 4, 64),
+                                           (128, True, 4, 64), (256, True, 8, 64),
+                                           (64, False, 1, 256), (40, True, 2, 33)])
+def test_beacon_update_teacher_forced(K, prewarm, G, T):
+    say("update", K, prewarm, G, T)
+    wl = small(n_layers=1, n_requests=2, n_kv_heads=2, n_beacons=K, group=G, steps=T,
+               prewarm=prewarm, budget=512, prompt_len=200, seq_len=576)
+    batch = synth.make_batch(wl)
+    q = batch.queries.cuda()
+    b = batch.beacons.cuda()
+    c = batch.counts.cuda()
+    HC = q.shape[0]
+    assign = torch.full((HC, T * G), -1, dtype=torch.int32).cuda()
+    bk.bkv_beacon_update(q, b, c, assign)
+    torch.cuda.synchronize()
+    qb = synth.bits(batch.queries)
+    bg, cg, ag = b.cpu().numpy(), c.cpu().numpy(), assign.cpu().numpy()
+    inexact = 0
+    for hc in range(HC):
+        ob, oc, gap = oracle.beacon_update_forced(qb[hc], batch.beacons[hc].numpy(),
+                                                  batch.counts[hc].numpy(), ag[hc])
+        assert np.all(np.isfinite(gap)) and gap.max() <= ASSIGN_TOL, (hc, gap.max())
+        inexact += int((gap > 0).sum())
+        assert np.array_equal(oc, cg[hc]), hc
+        assert np.array_equal(ob.view(np.int32), bg[hc].view(np.int32)), hc
+    say("update", K, "near-tie choices:", inexact)
+
+
+# ------------------------------------------------------------------ scoring
+def _score_case(wl, N, P, kill=(), window=64, bonus=1.0, mutate=None):
+    batch = synth.make_batch(wl)
+    if mutate:
+        mutate(batch)
+    cache = device_cache(batch, N, P)
+    b = batch.beacons.clone()
+    c = batch.counts.clone()
+    for hc, j in kill:
+        c[hc, j] = 0
+    K = b.shape[1]
+    stride = max(n - p for n, p in zip(N, P)) + 3
+    sc = torch.full((cache.n_head_caches, stride), float("nan")).cuda()
+    lse = torch.zeros((cache.n_head_caches, K)).cuda()
+    bk.bkv_beacon_score(cache, b.cuda(), c.cuda(), sc, window=window, bonus=bonus, lse=lse)
+    k_in, _ = host_pools(cache)
+    bt = batch.block_table.numpy()
+    scn, lsen = sc.cpu().numpy(), lse.cpu().numpy()
+    for hc, layer, r, h in head_iter(cache):
+        keys = oracle.gather_paged(k_in[layer], bt[r], h, N[r])
+        os_, ol = oracle.beacon_score(keys, b[hc].numpy(), c[hc].numpy(), P[r], window, bonus)
+        check_scores(scn[hc, :N[r] - P[r]], os_, f"hc {hc}")
+        assert np.all(np.isnan(scn[hc, N[r] - P[r]:])), "wrote past N - P"
+        live = c[hc].numpy() > 0
+        assert np.all(np.isnan(lsen[hc][~live]))
+        if live.any() and N[r] > 0:
+            assert np.max(np.abs(lsen[hc][live] - ol[live])) <= 1e-3, hc
+    return batch
+
+
+@pytest.mark.parametrize("K", [1, 5, 64, 128, 256])
+def test_beacon_score_parity(K):
+    say("score", K)
+    wl = small(n_layers=1, n_requests=3, n_kv_heads=2, n_beacons=K, budget=512, prompt_len=200,
+               seq_len=1040)
+    _score_case(wl, N=[1040, 577, 31], P=[200, 576, 0], kill=[(0, 0), (3, K - 1)])
+
+
+def test_beacon_score_no_live_beacons():
+    say("score empty J")
+    wl = small(n_layers=1, n_requests=1, n_kv_heads=2, n_beacons=64, prewarm=False,
+               budget=512, prompt_len=100, seq_len=300)
+    _score_case(wl, N=[300], P=[100])
+
+
+def test_beacon_score_extreme_logit_spread_uses_exact_fallback():
+    say("score rescue")
+    wl = small(n_layers=1, n_requests=2, n_kv_heads=2, n_beacons=64, budget=512, prompt_len=100,
+               seq_len=600)
+
+    def mutate(batch):
+        k = batch.k_pools[0].float()
+        bt = batch.block_table
+        # request 0: one late block of huge keys -> overflow of the running sum
+        k[bt[0, 30]] *= 40.0
+        batch.k_pools[0] = k.to(torch.bfloat16)
+        # request 1: beacon 0 enormous, beacon 1 tiny -> underflow of beacon 1
+        for h in range(2):
+            hc = 1 * 2 + h
+            batch.beacons[hc, 0] *= 60.0
+            batch.beacons[hc, 1] *= 1e-4
+    _score_case(wl, N=[600, 600], P=[100, 100], mutate=mutate)
+
+
+def test_beacon_score_one_shot_long():
+    say("score one-shot 4096")
+    _score_case(synth.WORKLOADS["tiny"].with_(prewarm=True), N=[4096], P=[512])
+
+
+# ------------------------------------------------------------------ whole pass
+def _pass_case(wl, N, P, B, selector, seed=17):
+    batch = synth.make_batch(wl)
+    cache = device_cache(batch, N, P)
+    k_in, v_in = host_pools(cache)
+    bt = batch.block_table.numpy()
+    HC, S = cache.n_head_caches, cache.max_slots
+    pos = np.tile(np.arange(S, dtype=np.int32), (HC, 1))
+    pos_dev = torch.from_numpy(pos).cuda()
+    keep = torch.full((HC, B), -7, dtype=torch.int32).cuda()
+    if selector == "beacon":
+        q, b, c = batch.queries.cuda(), batch.beacons.cuda(), batch.counts.cuda()
+        T, G = q.shape[1], q.shape[2]
+        assign = torch.zeros((HC, T * G), dtype=torch.int32).cuda()
+        sc = torch.zeros((HC, S)).cuda()
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                          window=64, bonus=1.0, assign=assign, pos_ids=pos_dev, scores_out=sc,
+                          keep_out=keep)
+    else:
+        rid = torch.arange(100, 100 + cache.n_requests, dtype=torch.int64).cuda()
+        pss = torch.full((cache.n_requests,), 4, dtype=torch.int32).cuda()
+        sc = torch.zeros((HC, S), dtype=torch.int32).cuda()
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=seed, request_ids=rid,
+                          pass_idx=pss, pos_ids=pos_dev, scores_out=sc, keep_out=keep)
+    torch.cuda.synchronize()
+    k_out, v_out = host_pools(cache)
+    kn, scn, posn = keep.cpu().numpy(), sc.cpu().numpy(), pos_dev.cpu().numpy()
+    qb = synth.bits(batch.queries)
+    mism = 0
+    for hc, layer, r, h in head_iter(cache):
+        keys = oracle.gather_paged(k_in[layer], bt[r], h, N[r])
+        vals = oracle.gather_paged(v_in[layer], bt[r], h, N[r])
+        kp = keep_rows(kn[hc])
+        if selector == "beacon":
+            ob, oc, gap = oracle.beacon_update_forced(qb[hc], batch.beacons[hc].numpy(),
+                                                      batch.counts[hc].numpy(),
+                                                      assign[hc].cpu().numpy())
+            assert gap.max() <= ASSIGN_TOL, hc
+            assert np.array_equal(ob.view(np.int32), b[hc].cpu().numpy().view(np.int32)), hc
+            assert np.array_equal(oc, c[hc].cpu().numpy()), hc
+            os_, _ = oracle.beacon_score(keys, ob, oc, P[r], 64, 1.0)
+            gs = scn[hc, :N[r] - P[r]]
+            check_scores(gs, os_, f"pass hc {hc}")
+            ref = oracle.topk_select(os_, N[r], P[r], B)
+            mism += check_selection(kp, ref, os_, N[r], P[r], B, f"pass hc {hc}")
+            own = oracle.topk_select(gs.astype(np.float64), N[r], P[r], B)
+            assert np.array_equal(kp, own), hc
+        else:
+            u = oracle.random_score(seed, 100 + r, 4, layer, h, N[r], P[r])
+            assert np.array_equal(scn[hc, :N[r] - P[r]].view(np.uint32), u), hc
+            assert np.array_equal(kp, oracle.topk_select(u, N[r], P[r], B)), hc
+        nk = len(kp)
+        ko = oracle.gather_paged(k_out[layer], bt[r], h, N[r])
+        vo = oracle.gather_paged(v_out[layer], bt[r], h, N[r])
+        assert np.array_equal(ko[:nk], oracle.kv_compact(keys, kp)), hc
+        assert np.array_equal(vo[:nk], oracle.kv_compact(vals, kp)), hc
+        assert np.array_equal(posn[hc, :nk], kp), hc
+    say(selector, "selection differences at boundary ties:", mism)
+
+
+@pytest.mark.parametrize("selector", ["beacon", "random"])
+def test_evict_pass_end_to_end(selector):
+    say("pass", selector)
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=512, prompt_len=200, seq_len=576)
+    _pass_case(wl, N=[576, 541, 400], P=[200, 333, 100], B=512, selector=selector)
+
+
+def test_evict_pass_tiny_one_shot():
+    say("pass tiny")
+    _pass_case(synth.WORKLOADS["tiny"], N=[4096], P=[512], B=1024, selector="beacon")
+
+
+def test_evict_pass_k256_group8():
+    say("pass K=256")
+    wl = small("qwen3_32b_r32", n_layers=1, n_requests=2, n_kv_heads=2, budget=1024,
+               seq_len=1088)
+    _pass_case(wl, N=[1088, 1000], P=[512, 512], B=1024, selector="beacon")
+
+
+def test_evict_pass_skips_invalid_request_entirely():
+    say("pass atomic skip")
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=256, prompt_len=100, seq_len=320)
+    batch = synth.make_batch(wl)
+    bt = batch.block_table.clone()
+    bt[2, 3] = wl.num_blocks + 5                         # request 2: bad block id
+    batch.block_table = bt
+    cache = device_cache(batch, [320, 320, 320], [100, 300, 100])   # request 1: P > B
+    k_in, v_in = host_pools(cache)
+    q, b, c = batch.queries.cuda(), batch.beacons.cuda(), batch.counts.cuda()
+    st = bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, 256, queries=q, beacons=b, counts=c,
+                           check=False)
+    torch.cuda.synchronize()
+    assert int(st.item()) == (1 << bk.BKV_ERR_BUDGET) | (1 << bk.BKV_ERR_BLOCK_TABLE)
+    k_out, v_out = host_pools(cache)
+    bn = b.cpu().numpy()
+    cn = c.cpu().numpy()
+    btn = batch.block_table.numpy()
+    for hc, layer, r, h in head_iter(cache):
+        if r in (1, 2):
+            assert np.array_equal(bn[hc].view(np.int32), batch.beacons[hc].numpy().view(np.int32))
+            assert np.array_equal(cn[hc], batch.counts[hc].numpy())
+        else:
+            assert cn[hc].sum() == batch.counts[hc].numpy().sum() + q.shape[1] * q.shape[2]
+    # request 1's blocks are untouched; request 0 was compacted
+    for layer in range(2):
+        for blk in btn[1]:
+            assert np.array_equal(k_in[layer][blk], k_out[layer][blk])
+            assert np.array_equal(v_in[layer][blk], v_out[layer][blk])
+    assert any(not np.array_equal(k_in[0][blk], k_out[0][blk]) for blk in btn[0])
