@@ -1,0 +1,364 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode-time KV-cache eviction pass on one MI355X.
+
+One step = one whole beacon eviction pass over every layer, request and KV
+head of the workload (maintenance -> scoring -> top-B selection -> in-place
+compaction), at the synchronized batch point where every request holds
+N = B + 64 slots.  Between steps, outside the timed region, 64 fresh K/V rows
+per head are written into slots [B, B+64) (what the next 64 decode tokens
+would append), so every timed pass sees a full cache.  Inputs are seeded
+synthetic data resident in HBM before timing starts.
+
+Prints exactly one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KV eviction passes/sec and achieved HBM GB/s (score+select+compact), % of peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, vendor figure
+# fp32 FMA on the vector ALUs without packed forms: 256 CU x 4 SIMD x 16 lanes
+# x 2 flop x 2.4 GHz (packed fp32 forms are not used by this library)
+VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "beacon_update": "beacon_update.hip",
+    "beacon_score": "beacon_score.hip",
+    "topk_select": "topk_select.hip",
+    "kv_compact": "kv_compact.hip",
+    "random_score": "random_score.hip",
+}
+
+
+def algorithmic_bytes(wl, N, P, moved_rows, hc_per_req):
+    """Bytes each kernel must move at least once per pass (see the design notes).
+
+    update : queries T*G*256 + beacons read+write 2*K*512 + counts 2*K*4
+    score  : keys N*256 + beacons K*512 + counts K*4 + block table ceil(N/16)*4
+             + scores written (N-P)*4
+    select : scores read (N-P)*4 + keep list written B*4
+    compact: moved rows 4*M*256 (K and V read and written) + keep list B*4
+    """
+    T, G, K, B = wl.steps, wl.group, wl.n_beacons, wl.budget
+    upd = sc = sel = 0
+    for n, p in zip(N, P):
+        upd += hc_per_req * (T * G * 256 + 2 * K * 512 + 2 * K * 4)
+        sc += hc_per_req * (n * 256 + K * 512 + K * 4 + -(-n // 16) * 4 + (n - p) * 4)
+        sel += hc_per_req * ((n - p) * 4 + B * 4)
+    cmp_ = 4 * moved_rows * 256 + len(N) * hc_per_req * B * 4
+    return {"beacon_update": upd, "beacon_score": sc, "topk_select": sel, "kv_compact": cmp_}
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle, as it stands, on one layer of the same workload (CPU-drawn
+    synthetic data of the same shapes), scaled to a full pass."""
+    import numpy as np
+
+    import oracle
+    from decode_kv_cache_beacon_amd import synth
+
+    swl = wl.with_(n_layers=min(2, wl.n_layers))
+    t0 = time.time()
+    batch = synth.make_batch(swl, "cpu")
+    kb = [synth.bits(k) for k in batch.k_pools]
+    vb = [synth.bits(v) for v in batch.v_pools]
+    bt = batch.block_table.numpy()
+    N = batch.seq_len.numpy()
+    P = batch.prompt_len.numpy()
+    R, H, L = swl.n_requests, swl.n_kv_heads, swl.n_layers
+    q = synth.bits(batch.queries)
+    b = batch.beacons.numpy()
+    c = batch.counts.numpy()
+    log(f"cpu baseline: sample generated in {time.time() - t0:.1f}s")
+    done, elapsed, chunk = 0, 0.0, 32
+    hc_total = L * R * H
+    while done < hc_total and elapsed < budget_s:
+        sl = slice(done, min(done + chunk, hc_total))
+        hcs = range(sl.start, sl.stop)     # hc = (layer * R + r) * H + h
+        keys = np.stack([oracle.gather_paged(kb[hc // (R * H)], bt[(hc // H) % R], hc % H,
+                                             wl.seq_len) for hc in hcs])
+        vals = np.stack([oracle.gather_paged(vb[hc // (R * H)], bt[(hc // H) % R], hc % H,
+                                             wl.seq_len) for hc in hcs])
+        Nh = np.array([N[(hc // H) % R] for hc in hcs], np.int32)
+        Ph = np.array([P[(hc // H) % R] for hc in hcs], np.int32)
+        t1 = time.perf_counter()
+        oracle.evict_batch(q[sl], b[sl], c[sl], keys, vals, Nh, Ph, wl.budget, wl.window,
+                           wl.bonus)
+        elapsed += time.perf_counter() - t1
+        done = sl.stop
+    per_hc = elapsed / done
+    pass_s = per_hc * wl.n_head_caches
+    return {
+        "value": 1.0 / pass_s,
+        "unit": "passes/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{done} of the {wl.n_head_caches} head-caches of one pass (the first "
+                   f"{done} of layers 0-{L - 1} in head-cache order, CPU-drawn data of the "
+                   f"same shapes), {elapsed:.1f} s of oracle time, scaled linearly to the "
+                   f"whole pass ({pass_s:.1f} s/pass)"),
+    }
+
+
+def stored_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(kernel)
+    src = os.path.join(ROOT, "decode_kv_cache_beacon_amd", "csrc", KERNEL_SOURCES[kernel])
+    if not e or e.get("source_sha") != source_hash(src):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="serving_r128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-random", action="store_true", help="skip the random-selector A/B")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 4 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the eviction pass has no cross-GPU work "
+              "(every head-cache is independent); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_kv_cache_beacon_amd import beaconkv as bk
+    from decode_kv_cache_beacon_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    B, W = wl.budget, wl.window
+    assert wl.seq_len == B + W and B % synth.BLOCK == 0 and W % synth.BLOCK == 0, \
+        "steady-state bench needs N = B + W with block-aligned B and W"
+
+    t0 = time.time()
+    batch = synth.make_batch(wl, dev)
+    torch.cuda.synchronize()
+    log(f"workload {wl.name}: generated on the GPU in {time.time() - t0:.1f}s")
+    cache = bk.PagedCache(batch.k_pools, batch.v_pools, batch.block_table, batch.seq_len,
+                          batch.prompt_len)
+    HC, R, H = cache.n_head_caches, cache.n_requests, cache.n_kv_heads
+    N = batch.seq_len.cpu().tolist()
+    P = batch.prompt_len.cpu().tolist()
+    stride = max(n - p for n, p in zip(N, P))
+    q, b, c = batch.queries, batch.beacons, batch.counts
+    scores = torch.zeros((HC, stride), dtype=torch.float32, device=dev)
+    keep = torch.zeros((HC, B), dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    # fresh rows for the W slots appended between passes (pool layout)
+    tail_blocks = batch.block_table[:, B // synth.BLOCK:(B + W) // synth.BLOCK].long()
+    nb_tail = W // synth.BLOCK
+    fresh = []
+    for layer in range(wl.n_layers):
+        fk, fv = synth.fresh_tail(wl, layer, 0, dev)          # [R, H, W, d]
+        shp = (R, H, nb_tail, synth.BLOCK, wl.head_dim)
+        fresh.append((fk.reshape(shp).permute(0, 2, 1, 3, 4).contiguous(),
+                      fv.reshape(shp).permute(0, 2, 1, 3, 4).contiguous()))
+
+    def refill():
+        for layer, (fk, fv) in enumerate(fresh):
+            cache.k_pools[layer][tail_blocks] = fk
+            cache.v_pools[layer][tail_blocks] = fv
+
+    ar = torch.arange(B, device=dev, dtype=torch.int32)
+
+    def moved_rows():
+        neq = keep != ar
+        first = torch.where(neq.any(1), neq.int().argmax(1), torch.full_like(neq[:, 0], B,
+                                                                            dtype=torch.long))
+        nk = min(N[0], B)
+        return (nk - first).clamp(min=0).sum()
+
+    stream = torch.cuda.current_stream()
+    names = ["beacon_update", "beacon_score", "topk_select", "kv_compact"]
+
+    def run_pass(events=None):
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                          window=W, bonus=wl.bonus, scores_out=scores, keep_out=keep,
+                          score_stride=stride, status=status, check=False,
+                          timing_events=events)
+
+    for _ in range(args.warmup):
+        refill()
+        run_pass()
+    torch.cuda.synchronize()
+    bk.check_status(status, "warmup passes")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    moved = []
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for s in range(args.steps):
+        refill()
+        run_pass(evs[s])
+        moved.append(moved_rows())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    bk.check_status(status, "timed passes")
+
+    per_kernel = {n: [] for n in names}
+    pass_ms = []
+    for e in evs:
+        pass_ms.append(e[0].elapsed_time(e[4]))
+        for i, n in enumerate(names):
+            per_kernel[n].append(e[i].elapsed_time(e[i + 1]))
+    ms = sum(pass_ms) / len(pass_ms)
+    kms = {n: sum(v) / len(v) for n, v in per_kernel.items()}
+    M = float(sum(int(m) for m in moved)) / len(moved)
+    hc_per_req = wl.n_layers * H
+    abytes = algorithmic_bytes(wl, N, P, M, hc_per_req)
+    total_bytes = sum(abytes.values())
+    ssc_bytes = total_bytes - abytes["beacon_update"]
+    ssc_ms = kms["beacon_score"] + kms["topk_select"] + kms["kv_compact"]
+    score_flops = 2.0 * 2 * wl.n_beacons * 128 * sum(N) * hc_per_req   # two logit passes
+    update_flops = 2.0 * wl.steps * wl.group * wl.n_beacons * 128 * HC
+
+    kernels = {}
+    for n in names:
+        gbps = abytes[n] / (kms[n] * 1e-3) / 1e9
+        kernels[n] = {"ms": round(kms[n], 4), "algorithmic_bytes": int(abytes[n]),
+                      "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    kernels["beacon_score"]["mfma_tflops"] = round(score_flops / (kms["beacon_score"] * 1e-3) / 1e12, 1)
+    kernels["beacon_update"]["valu_tflops"] = round(update_flops / (kms["beacon_update"] * 1e-3) / 1e12, 2)
+
+    dom = max(names, key=lambda n: kms[n])
+    if dom == "beacon_update":
+        ach = update_flops / (kms[dom] * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(ach, 2), "peak": round(VALU_FP32_PEAK_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(ach / VALU_FP32_PEAK_TFLOPS, 4)}
+    else:
+        ach = abytes[dom] / (kms[dom] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = stored_traffic(dom)
+
+    result = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms, 3),
+        "unit": "passes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian-mixture keys/queries, paged pools with permuted "
+                "block tables; generated on the GPU before timing)",
+        "config": {"workload": wl.name, "layers": wl.n_layers, "requests": R, "kv_heads": H,
+                   "query_heads_per_kv": wl.group, "head_dim": wl.head_dim,
+                   "beacons": wl.n_beacons, "budget": B, "prompt": P[0] if len(set(P)) == 1
+                   else f"U{{{min(P)}..{max(P)}}}", "seq_len_at_pass": N[0],
+                   "decode_steps_per_pass": wl.steps, "block_size": synth.BLOCK,
+                   "paged": wl.paged, "head_caches": HC},
+        "hbm_gbps": round(total_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "score_select_compact": {
+            "passes_per_s": round(1000.0 / ssc_ms, 3), "ms": round(ssc_ms, 4),
+            "gbps": round(ssc_bytes / (ssc_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(ssc_bytes / (ssc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "bytes_per_pass": int(total_bytes),
+        "moved_rows_per_pass": int(M),
+        "kernels": kernels,
+        "wall_ms_per_step_incl_append": round(wall * 1e3 / args.steps, 3),
+        "roofline": roof,
+    }
+
+    if not args.no_random:
+        rid = torch.arange(R, dtype=torch.int64, device=dev)
+        pss = torch.zeros(R, dtype=torch.int32, device=dev)
+        u = torch.zeros((HC, stride), dtype=torch.int32, device=dev)
+        rms, rk = [], {"random_score": [], "topk_select": [], "kv_compact": []}
+        rmoved = []
+        for s in range(args.warmup + args.steps):
+            pss.fill_(s + 1000)
+            refill()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed, request_ids=rid,
+                              pass_idx=pss, scores_out=u, keep_out=keep, score_stride=stride,
+                              status=status, check=False, timing_events=ev)
+            if s >= args.warmup:
+                rmoved.append(moved_rows())
+                rms.append(ev)
+        torch.cuda.synchronize()
+        bk.check_status(status, "random passes")
+        rpass = sum(e[0].elapsed_time(e[3]) for e in rms) / len(rms)
+        for i, n in enumerate(rk):
+            rk[n] = round(sum(e[i].elapsed_time(e[i + 1]) for e in rms) / len(rms), 4)
+        rM = float(sum(int(m) for m in rmoved)) / len(rmoved)
+        rbytes = 4 * rM * 256 + HC * (2 * stride * 4 + 2 * B * 4)
+        result["random_selector"] = {
+            "passes_per_s": round(1000.0 / rpass, 3), "ms": round(rpass, 4), "kernel_ms": rk,
+            "moved_rows_per_pass": int(rM),
+            "gbps": round(rbytes / (rpass * 1e-3) / 1e9, 1),
+            "hbm_frac": round(rbytes / (rpass * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    # reference: a plain device-to-device copy of 4 GiB (read + write), timed the same way
+    src = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    result["copy_reference_gbps"] = round(copy_gbps, 1)
+    del src, dst
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = {"read": src.numel() * 2, "written": dst.numel() * 2}
+        del src, dst
+
+    del batch
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

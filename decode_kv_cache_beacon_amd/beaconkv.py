@@ -54,6 +54,7 @@ class bkv_pass_args(ctypes.Structure):
         ("queries", _P), ("beacons", _P), ("counts", _P), ("assign", _P), ("lse", _P),
         ("seed", _u64), ("request_ids", _P), ("pass_idx", _P),
         ("pos_ids", _P), ("pos_stride", _i32), ("scores_out", _P), ("keep_out", _P),
+        ("timing_events", _P), ("n_timing_events", _i32),
     ]
 
 
@@ -384,11 +385,24 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
                    counts=None, window=64, bonus=1.0, assign=None, lse=None, seed=0,
                    request_ids=None, pass_idx=None, pos_ids=None, scores_out=None,
                    keep_out=None, score_stride=0, workspace=None, status=None, check=True,
-                   stream=None):
+                   stream=None, timing_events=None):
     """One whole eviction pass (beacon: update -> score -> select -> compact;
-    random: score -> select -> compact), every layer/request/head at once."""
+    random: score -> select -> compact), every layer/request/head at once.
+
+    timing_events: optional list of torch.cuda.Event(enable_timing=True), 5 for
+    the beacon selector and 4 for the random one, recorded around each kernel."""
     a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
                    seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride)
+    ev_arr = None
+    if timing_events is not None:
+        handles = []
+        for e in timing_events:
+            if e.cuda_event == 0:            # torch creates the HIP event lazily
+                e.record(stream or torch.cuda.current_stream())
+            handles.append(e.cuda_event)
+        ev_arr = (ctypes.c_void_p * len(handles))(*handles)
+        a.timing_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+        a.n_timing_events = len(handles)
     need = bkv_workspace_size(cache, a)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=cache.device)

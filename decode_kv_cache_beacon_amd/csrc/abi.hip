@@ -227,23 +227,41 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
     // every kernel applies every check, so a failing request is skipped by all steps
     const Check all{a->budget, L.stride, 1};
     const int HC = (int)head_caches(v);
-    hipError_t he;
+    const int n_marks = beacon ? 5 : 4;
+    const bool timed = a->timing_events && a->n_timing_events >= n_marks;
+    if (timed)
+        for (int i = 0; i < n_marks; ++i)
+            if (!a->timing_events[i]) return BKV_ERR_NULL;
+    int mark_i = 0;
+    auto mark = [&]() -> hipError_t {
+        return timed ? hipEventRecord(static_cast<hipEvent_t>(a->timing_events[mark_i++]), s)
+                     : hipSuccess;
+    };
+    hipError_t he = mark();
+    if (he != hipSuccess) return BKV_ERR_HIP;
     if (beacon) {
         he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
                                   a->assign, &v, all, status, s);
-        if (he != hipSuccess) return BKV_ERR_HIP;
-        he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
-                                 static_cast<float*>(sc), L.stride, a->lse, all, status, s);
-        if (he != hipSuccess) return BKV_ERR_HIP;
-        he = launch_topk_select(v, sc, BKV_SCORE_F32, L.stride, a->budget, keep, all, status, s);
+        if (he == hipSuccess) he = mark();
+        if (he == hipSuccess)
+            he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
+                                     static_cast<float*>(sc), L.stride, a->lse, all, status, s);
+        if (he == hipSuccess) he = mark();
+        if (he == hipSuccess)
+            he = launch_topk_select(v, sc, BKV_SCORE_F32, L.stride, a->budget, keep, all, status,
+                                    s);
     } else {
         he = launch_random_score(v, a->seed, a->request_ids, a->pass_idx,
                                  static_cast<uint32_t*>(sc), L.stride, all, status, s);
-        if (he != hipSuccess) return BKV_ERR_HIP;
-        he = launch_topk_select(v, sc, BKV_SCORE_U32, L.stride, a->budget, keep, all, status, s);
+        if (he == hipSuccess) he = mark();
+        if (he == hipSuccess)
+            he = launch_topk_select(v, sc, BKV_SCORE_U32, L.stride, a->budget, keep, all, status,
+                                    s);
     }
-    if (he != hipSuccess) return BKV_ERR_HIP;
-    he = launch_kv_compact(v, keep, a->budget, a->pos_ids, a->pos_stride, all, status, s);
+    if (he == hipSuccess) he = mark();
+    if (he == hipSuccess)
+        he = launch_kv_compact(v, keep, a->budget, a->pos_ids, a->pos_stride, all, status, s);
+    if (he == hipSuccess) he = mark();
     return hip_status(he);
 }
 

@@ -13,11 +13,14 @@
 //     v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Beacons are the A
 //     operand (rows), 32 keys form the B operand (columns), so each lane owns
 //     one key column and 16 beacon rows of the 32x32 result.
-//   - A wave keeps the bf16 A fragments of up to 4 row blocks (128 beacons) in
-//     registers for the whole head; with 256 beacons two wave groups split the
-//     rows.  Within a group the 4 waves take every 4th key tile.  Each lane
-//     loads its B fragment straight from the paged pool: 8 x 16 bytes of one
-//     256-byte key row (rows are found through the block table, staged in LDS).
+//   - A wave keeps the bf16 A fragments of its row blocks in registers for the
+//     whole head.  Beyond 32 beacons the rows are split between two groups of
+//     four waves (8 waves, two per SIMD, so one wave's MFMA work overlaps
+//     another's exp/VALU work); within a group the 4 waves take every 4th key
+//     tile.  Each lane loads its B fragment straight from the paged pool:
+//     8 x 16 bytes of one 256-byte key row (rows are found through the block
+//     table, staged in LDS), and the next tile is in flight while the current
+//     one is consumed.
 //   - Phase 1 (log-sum-exp per beacon): per lane and row a running sum of
 //     exp2(acc * log2(e)/sqrt(d) - M) with one reference M per wave taken from
 //     the wave's first tile; lanes, then waves, are merged in LDS.  If any live
@@ -56,17 +59,15 @@ struct Tile {
     bf16x8_t b[8];
 };
 
-// B fragment of key n: d in [16s + 8hh, 16s + 8hh + 8) for k-step s.
+// B fragment of key n: d in [16s + 8hh, 16s + 8hh + 8) for k-step s.  Lanes
+// past the last key re-read key N-1 (always in bounds); their results are
+// masked by the caller.
 __device__ __forceinline__ void load_key(Tile& t, uint64_t kbase, const int* s_bt, int H, int h,
                                          int n, int N, int hh) {
-    if (n < N) {
-        const uint64_t p = kbase + row_offset(s_bt[n >> 4], H, h, n & 15) + 16 * hh;
+    n = min(n, N - 1);
+    const uint64_t p = kbase + row_offset(s_bt[n >> 4], H, h, n & 15) + 16 * hh;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) t.b[s] = as_bf16x8(load16(p + 32 * s));
-    } else {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) t.b[s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-    }
+    for (int s = 0; s < 8; ++s) t.b[s] = as_bf16x8(load16(p + 32 * s));
 }
 
 __device__ __forceinline__ f32x16_t logits(const bf16x8_t (&a)[8], const Tile& t, f32x16_t c) {
@@ -171,6 +172,8 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
     const uint64_t kpool = c.k_pools[x.layer];
     const int ntiles = (N + 31) >> 5;
     const f32x16_t zero = {};
+    // with four row blocks per wave the registers do not allow a second tile
+    constexpr bool kPrefetch = MBW <= 2;
 
     // ---------------- phase 1: per-row log-sum-exp ----------------
     float Mw = -INFINITY;  // wave reference (log2 units)
@@ -196,25 +199,48 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) sum[m][i] = 0.f;
 
-    for (int tt = q; tt < ntiles; tt += kTileWaves) {
-        Tile t;
-        const int n = 32 * tt + col;
-        load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
-        const bool full = 32 * tt + 32 <= N;
+    {
+        auto consume = [&](const Tile& t, int tt) {
+            const int n = 32 * tt + col;
+            const bool full = 32 * tt + 32 <= N;
 #pragma unroll
-        for (int m = 0; m < MBW; ++m) {
-            if (mb0 + m >= MB) continue;
-            const f32x16_t acc = logits(A[m], t, zero);
-            if (full) {
+            for (int m = 0; m < MBW; ++m) {
+                if (mb0 + m >= MB) continue;
+                const f32x16_t acc = logits(A[m], t, zero);
+                if (full) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    sum[m][i] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -Mw));
-            } else {
+                    for (int i = 0; i < 16; ++i)
+                        sum[m][i] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -Mw));
+                } else {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -Mw));
-                    sum[m][i] += (n < N) ? e : 0.f;
+                    for (int i = 0; i < 16; ++i) {
+                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -Mw));
+                        sum[m][i] += (n < N) ? e : 0.f;
+                    }
                 }
+            }
+        };
+        if (kPrefetch) {
+            // two tiles alternate: one is consumed while the next is in flight
+            Tile ta, tb;
+            int tt = q;
+            if (tt < ntiles) load_key(ta, kpool, s_bt, c.H, x.head, 32 * tt + col, N, hh);
+            while (tt < ntiles) {
+                if (tt + kTileWaves < ntiles)
+                    load_key(tb, kpool, s_bt, c.H, x.head, 32 * (tt + kTileWaves) + col, N, hh);
+                consume(ta, tt);
+                tt += kTileWaves;
+                if (tt >= ntiles) break;
+                if (tt + kTileWaves < ntiles)
+                    load_key(ta, kpool, s_bt, c.H, x.head, 32 * (tt + kTileWaves) + col, N, hh);
+                consume(tb, tt);
+                tt += kTileWaves;
+            }
+        } else {
+            for (int tt = q; tt < ntiles; tt += kTileWaves) {
+                Tile t;
+                load_key(t, kpool, s_bt, c.H, x.head, 32 * tt + col, N, hh);
+                consume(t, tt);
             }
         }
     }
@@ -335,17 +361,19 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
         }
     float* out = scores + (size_t)hc * stride;
     const int iters = (ntiles + kTileWaves - 1) / kTileWaves;
-    for (int it = 0; it < iters; ++it) {
+    // one step of the score loop: tile tt of this wave (if any), merged across
+    // the row groups; every wave runs the same number of steps (barriers)
+    auto step = [&](int it, const Tile& cur, Tile& nxt) {
         const int tt = q + kTileWaves * it;
         const int n = 32 * tt + col;
         float mx = -INFINITY;
         if (tt < ntiles) {
-            Tile t;
-            load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
+            if (kPrefetch && tt + kTileWaves < ntiles)
+                load_key(nxt, kpool, s_bt, c.H, x.head, n + 32 * kTileWaves, N, hh);
 #pragma unroll
             for (int m = 0; m < MBW; ++m) {
                 if (mb0 + m >= MB) continue;
-                const f32x16_t acc = logits(A[m], t, Cf[m]);
+                const f32x16_t acc = logits(A[m], cur, Cf[m]);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
             }
@@ -361,6 +389,21 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
             const float sigma = __builtin_amdgcn_exp2f(mx * kCs);
             out[n - P] = sigma + ((n >= N - window) ? bonus : 0.f);
         }
+    };
+    if (kPrefetch) {
+        Tile ta, tb;
+        if (q < ntiles) load_key(ta, kpool, s_bt, c.H, x.head, 32 * q + col, N, hh);
+        for (int it = 0; it < iters; it += 2) {
+            step(it, ta, tb);
+            if (it + 1 < iters) step(it + 1, tb, ta);
+        }
+    } else {
+        for (int it = 0; it < iters; ++it) {
+            Tile t;
+            const int tt = q + kTileWaves * it;
+            if (tt < ntiles) load_key(t, kpool, s_bt, c.H, x.head, 32 * tt + col, N, hh);
+            step(it, t, t);
+        }
     }
 }
 
@@ -371,14 +414,16 @@ hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const i
                                float* lse, Check ck, int32_t* status, hipStream_t s) {
     const int HC = c.L * c.R * c.H;
     if (HC == 0) return hipSuccess;
+    // Two row groups of four waves (8 waves, 2 per SIMD) whenever K > 32, so
+    // that one wave's MFMA work overlaps another's exp/VALU work.
     if (K <= 32) {
         hipLaunchKernelGGL((beacon_score_kernel<1, 256>), dim3(HC), dim3(256), 0, s, c, beacons,
                            counts, K, window, bonus, scores, stride, lse, ck, status);
     } else if (K <= 64) {
-        hipLaunchKernelGGL((beacon_score_kernel<2, 256>), dim3(HC), dim3(256), 0, s, c, beacons,
+        hipLaunchKernelGGL((beacon_score_kernel<1, 512>), dim3(HC), dim3(512), 0, s, c, beacons,
                            counts, K, window, bonus, scores, stride, lse, ck, status);
     } else if (K <= 128) {
-        hipLaunchKernelGGL((beacon_score_kernel<4, 256>), dim3(HC), dim3(256), 0, s, c, beacons,
+        hipLaunchKernelGGL((beacon_score_kernel<2, 512>), dim3(HC), dim3(512), 0, s, c, beacons,
                            counts, K, window, bonus, scores, stride, lse, ck, status);
     } else {
         hipLaunchKernelGGL((beacon_score_kernel<4, 512>), dim3(HC), dim3(512), 0, s, c, beacons,

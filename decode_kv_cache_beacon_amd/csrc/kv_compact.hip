@@ -22,8 +22,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kChunksPerRow = kRowBytes / 16;               // 16 x 16-byte pieces
 constexpr int kRowsPerRound = kThreads / kChunksPerRow;     // 16 rows per instruction round
-constexpr int kRounds = 4;
-constexpr int kRowsPerIter = kRowsPerRound * kRounds;       // 64 rows per barrier
+constexpr int kRounds = 8;
+constexpr int kRowsPerIter = kRowsPerRound * kRounds;       // 128 rows per barrier
 
 __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CacheView c,
                                                               const int32_t* __restrict__ keep,

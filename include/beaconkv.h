@@ -206,6 +206,13 @@ typedef struct bkv_pass_args {
     int32_t pos_stride;
     void* scores_out;          /* nullable [HC][score_stride] scores; else workspace */
     int32_t* keep_out;         /* nullable [HC][budget] keep lists; else workspace */
+    /* optional profiling hook: caller-created hipEvent_t handles, recorded on
+     * `stream` before the first kernel and after every kernel of the pass
+     * (beacon: 5 events around update, score, select, compact; random: 4
+     * events around score, select, compact).  Ignored when NULL or when
+     * n_timing_events is smaller than that. */
+    void* const* timing_events;
+    int32_t n_timing_events;
 } bkv_pass_args;
 
 /* Bytes of workspace bkv_evict_pass needs for these arguments (the score and

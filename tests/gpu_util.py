@@ -17,11 +17,16 @@ from decode_kv_cache_beacon_amd import synth
 
 SCORE_RTOL = 1e-3
 SCORE_ATOL = 1e-30
-# The GPU forms each cosine as an fp32 dot product of 128 terms (two 64-term
-# halves) times an fp32 reciprocal square root: relative error below
-# ~(64 + 4) * 2^-24 of ||x|| ||b||, i.e. < 4.1e-6 in cosine.  Two cosines are
-# compared, so the chosen row is within 2 * 4.1e-6 of the best; 1e-5 bounds it.
-ASSIGN_TOL = 1e-5
+# Error budget of the GPU's cosine (relative to ||x|| ||b||, u = 2^-24), worst case:
+#   chunk-start dot: fp32 accumulation of 128 exact products (three bf16
+#   planes of the fp32 beacon) ..................................... ~130 u
+#   norm: fp32 sum of 128 squares + rsqrt ............................ ~35 u
+#   up to 31 running-mean advances of the dot inside a chunk, each one
+#   fp32 fma+mul plus the rounding of the real fp32 row update ...... ~155 u
+#   the same for the norm ............................................ ~155 u
+# total ~475 u = 2.8e-5 per cosine; the chosen row is then within 2 x 2.8e-5
+# of the best cosine.
+ASSIGN_TOL = 6e-5
 
 
 def hc_index(R, H, layer, req, head):

@@ -221,15 +221,16 @@ def test_beacon_update_teacher_forced(K, prewarm, G, T):
     torch.cuda.synchronize()
     qb = synth.bits(batch.queries)
     bg, cg, ag = b.cpu().numpy(), c.cpu().numpy(), assign.cpu().numpy()
-    inexact = 0
+    inexact, worst = 0, 0.0
     for hc in range(HC):
         ob, oc, gap = oracle.beacon_update_forced(qb[hc], batch.beacons[hc].numpy(),
                                                   batch.counts[hc].numpy(), ag[hc])
         assert np.all(np.isfinite(gap)) and gap.max() <= ASSIGN_TOL, (hc, gap.max())
         inexact += int((gap > 0).sum())
+        worst = max(worst, float(gap.max()))
         assert np.array_equal(oc, cg[hc]), hc
         assert np.array_equal(ob.view(np.int32), bg[hc].view(np.int32)), hc
-    say("update", K, "near-tie choices:", inexact)
+    say("update", K, "non-exact argmax choices:", inexact, "largest cosine gap:", worst)
 
 
 # ------------------------------------------------------------------ scoring
