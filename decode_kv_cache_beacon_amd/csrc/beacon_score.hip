@@ -8,29 +8,32 @@
 // The traversal of the paged keys is the extra pass a content-dependent
 // selector costs (Random Attention article, section "发现四").
 //
-// How (one workgroup per head-cache, gfx950):
+// How (one 8-wave workgroup per head-cache, gfx950):
 //   - The beacon.key logits are a [K x 128] x [128 x N] contraction: bf16 MFMA
 //     v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Beacons are the A
-//     operand (rows), 32 keys form the B operand (columns), so each lane owns
-//     one key column and 16 beacon rows of the 32x32 result.
-//   - A wave keeps the bf16 A fragments of its row blocks in registers for the
-//     whole head.  Beyond 32 beacons the rows are split between two groups of
-//     four waves (8 waves, two per SIMD, so one wave's MFMA work overlaps
-//     another's exp/VALU work); within a group the 4 waves take every 4th key
-//     tile.  Each lane loads its B fragment straight from the paged pool:
-//     8 x 16 bytes of one 256-byte key row (rows are found through the block
-//     table, staged in LDS), and the next tile is in flight while the current
-//     one is consumed.
+//     operand (rows, kept in registers for the whole head), 32 keys form the B
+//     operand (columns), so each lane owns one key column and 16 beacon rows of
+//     a 32x32 result.  Rows are split between two groups of four waves; wave
+//     (group g, phase q) consumes key tiles q, q+4, q+8, ...
+//   - Key tiles (32 keys = 8 KiB) stream through a 16-tile LDS ring filled by
+//     direct-to-LDS DMA (global_load_lds_dwordx4): each load instruction moves
+//     1 KiB of whole key rows, the ring is refilled three iterations ahead, and
+//     each tile serves both row groups.  A row's 16-byte chunks are
+//     XOR-swizzled by the row index so that the fragment reads are free of
+//     bank conflicts.  The four waves of group 1 issue all the DMA, so their
+//     vmcnt counts ring loads only; one barrier per iteration hands the tiles
+//     over.
 //   - Phase 1 (log-sum-exp per beacon): per lane and row a running sum of
 //     exp2(acc * log2(e)/sqrt(d) - M) with one reference M per wave taken from
 //     the wave's first tile; lanes, then waves, are merged in LDS.  If any live
 //     row's sum overflows or underflows (logit spread beyond the fp32 exponent
-//     range) the head is redone exactly: an all-key maximum per row first, then
-//     the sums against that maximum.
-//   - Phase 2 (score): the keys are read again (expected to hit L2/MALL) and
-//     the MFMA accumulator starts from C = -lse_j (in accumulator units), so
-//     the subtraction is free; the lane takes the max over its rows, the two
-//     lane halves are merged, and one exp2 per key gives sigma(n).
+//     range) the head is redone exactly with direct loads: an all-key maximum
+//     per row first, then the sums against that maximum.
+//   - Phase 2 (score): the keys stream through the ring again (the re-read is
+//     served by L2/MALL) and the MFMA accumulator starts from C = -lse_j (in
+//     accumulator units), so the subtraction is free; each lane takes the max
+//     over its rows, the two row groups are merged through LDS one iteration
+//     later, and one exp2 per key gives sigma(n).
 // Scaling by 1/sqrt(d) happens in fp32 after accumulation; the bf16 beacons
 // are never pre-scaled.
 
@@ -44,7 +47,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kCs = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
-constexpr int kTileWaves = 4;                                        // waves sharing a row group
+constexpr int kWaves = 8;
+constexpr int kQ = 4;                              // tile phases = waves per row group
+constexpr int kTileKeys = 32;
+constexpr int kTileBytes = kTileKeys * kRowBytes;  // 8 KiB
+constexpr int kDepth = 3;                          // ring refilled this many iterations ahead
+constexpr int kRingIters = kDepth + 1;
+constexpr int kRingTiles = kQ * kRingIters;        // 16 tiles = 128 KiB
+constexpr int kDmaPerTile = kTileBytes / 1024;     // instructions of 64 lanes x 16 B
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -55,13 +65,60 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 // Row (within its 32-row block) of accumulator element i for lane half hh.
 __device__ __forceinline__ int acc_row(int i, int hh) { return 8 * (i >> 2) + 4 * hh + (i & 3); }
 
+// Workgroup barrier without a memory fence.  The ring's DMA completion is
+// awaited explicitly (wait_ring) by the waves that issued it; this wave's own
+// LDS traffic is completed first, and the compiler may not move memory
+// operations across the barrier.  (A fenced __syncthreads would also wait for
+// every ring load still in flight and serialise the pipeline.)
+__device__ __forceinline__ void ring_barrier() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most 8*n of this wave's ring loads are in flight (n <= 2).
+__device__ __forceinline__ void wait_ring(int n) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (n <= 0)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    else if (n == 1)
+        __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else
+        __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// One 64-lane direct-to-LDS load: lane l copies 16 bytes from `g` to LDS
+// address m0 + 16 l.  Written as inline assembly so that the compiler, which
+// does not see these loads, does not make every later LDS access of the wave
+// wait for all of them; their completion is awaited by wait_ring only.  The
+// s_nop covers the wait state the hardware needs between writing M0 and an
+// LDS DMA that reads it.  M0 is reserved by the compiler, which sets it right
+// before each of its own uses; nothing else in this kernel reads it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint64_t g, uint32_t m0) {
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(g), "s"(m0)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 struct Tile {
     bf16x8_t b[8];
 };
 
-// B fragment of key n: d in [16s + 8hh, 16s + 8hh + 8) for k-step s.  Lanes
-// past the last key re-read key N-1 (always in bounds); their results are
-// masked by the caller.
+// Direct loads of one key's B fragment (d in [16s + 8hh, +8) for k-step s),
+// used by the exact fallback only.  Lanes past the last key re-read key N-1.
 __device__ __forceinline__ void load_key(Tile& t, uint64_t kbase, const int* s_bt, int H, int h,
                                          int n, int N, int hh) {
     n = min(n, N - 1);
@@ -94,18 +151,19 @@ __device__ __forceinline__ float half_max(float v) {
     return v;
 }
 
-template <int MBW, int kThreads>
-__global__ __launch_bounds__(kThreads) void beacon_score_kernel(
+template <int MBW>
+__global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
     CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
     int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
     Check ck, int32_t* status) {
+    __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kRingTiles * kTileBytes];
     __shared__ int s_bt[kMaxBlocksPerReq];
-    __shared__ float s_part[2 * kTileWaves][BKV_MAX_BEACONS];
-    __shared__ float s_M[2 * kTileWaves];
+    __shared__ float s_part[kWaves][BKV_MAX_BEACONS];
+    __shared__ float s_M[kWaves];
     __shared__ float s_lse2[BKV_MAX_BEACONS];
     __shared__ float s_ref[BKV_MAX_BEACONS];
     __shared__ int s_live[BKV_MAX_BEACONS];
-    __shared__ float s_pmax[kTileWaves][32];
+    __shared__ float s_pmax[2][kQ][32];
     __shared__ int s_rescue;
 
     const int hc = blockIdx.x;
@@ -119,12 +177,13 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
     const int lane = tid & (kWave - 1);
     const int hh = lane >> 5;
     const int col = lane & 31;
-    const int group = w / kTileWaves;
-    const int q = w % kTileWaves;
-    const int NG = blockDim.x / (kWave * kTileWaves);
+    const int group = w / kQ;
+    const int q = w % kQ;
+    const bool loader = group == 1;
     const int Kp = (K + 31) & ~31;
     const int MB = Kp / 32;
     const int mb0 = group * MBW;
+    const bool computes = mb0 < MB;
 
     const int nb = (N + kBlock - 1) / kBlock;
     const int32_t* bt = c.block_table + (size_t)x.req * c.max_blocks;
@@ -136,9 +195,58 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
 
     if (N == 0) {  // empty cache: nothing to score, every live lse is log(0)
         for (int j = tid; j < K; j += blockDim.x)
-            if (lse_out) lse_out[(size_t)hc * K + j] = s_live[j] ? -INFINITY : __int_as_float(0x7fc00000);
+            if (lse_out)
+                lse_out[(size_t)hc * K + j] = s_live[j] ? -INFINITY : __int_as_float(0x7fc00000);
         return;
     }
+
+    const uint64_t kpool = c.k_pools[x.layer];
+    const int ntiles = (N + kTileKeys - 1) / kTileKeys;
+    const int iters = (ntiles + kQ - 1) / kQ;
+    // last iteration in which this wave's phase has a tile (-1 if none)
+    const int jlast = (q < ntiles) ? (ntiles - 1 - q) / kQ : -1;
+
+    // DMA of key tile t into ring slot `slot` (issued by a group-1 wave).  Lane
+    // l of instruction i fills LDS bytes [1024 i + 16 l, +16) of the slot: row
+    // r = 4i + l/16, chunk position p = l%16, which holds global chunk
+    // p ^ (r & 15) of key 32t + r (key N-1 past the end).
+    const uint32_t ring0 = lds_addr(s_ring);
+    auto issue_tile = [&](int t, int slot) {
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(ring0 + slot * kTileBytes);
+#pragma unroll
+        for (int i = 0; i < kDmaPerTile; ++i) {
+            const int r = 4 * i + (lane >> 4);
+            const int ch = (lane & 15) ^ (r & 15);
+            const int n = min(kTileKeys * t + r, N - 1);
+            const uint64_t g = kpool + row_offset(s_bt[n >> 4], c.H, x.head, n & 15) + 16 * ch;
+            dma16(g, dst + 1024 * i);
+        }
+    };
+    auto slot_of = [&](int it) { return (it % kRingIters) * kQ + q; };
+    auto prologue = [&]() {
+        if (loader)
+            for (int j = 0; j < kDepth && j <= jlast; ++j) issue_tile(kQ * j + q, slot_of(j));
+    };
+    // this lane's key column from a ring slot: the B fragment of k-step s is
+    // global chunk 2s + hh of row `col`
+    auto read_tile = [&](Tile& t, int slot) {
+        const uint8_t* row = s_ring + slot * kTileBytes + col * kRowBytes;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const int p = (2 * s + hh) ^ (col & 15);
+            t.b[s] = *reinterpret_cast<const bf16x8_t*>(row + 16 * p);
+        }
+    };
+    // hand-over of iteration `it`: the loaders wait for their DMA of it, all
+    // waves pass the barrier (iteration it-1's reads are then done), and the
+    // slot read in it-1 is refilled with iteration it + kDepth
+    auto begin_iter = [&](int it) {
+        if (loader) wait_ring(min(kDepth - 1, jlast - it));
+        ring_barrier();
+        if (loader && it + kDepth <= jlast) issue_tile(kQ * (it + kDepth) + q, slot_of(it + kDepth));
+    };
+
+    prologue();  // the first tiles are in flight while the beacons are prepared
 
     // A fragments: beacon row 32*(mb0+m) + col, bf16 (RNE) of the fp32 state.
     bf16x8_t A[MBW][8];
@@ -164,87 +272,60 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
         uint32_t bits = 0;
         if (mb0 + m < MB) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) bits |= (uint32_t)(s_live[32 * (mb0 + m) + acc_row(i, hh)] != 0) << i;
+            for (int i = 0; i < 16; ++i)
+                bits |= (uint32_t)(s_live[32 * (mb0 + m) + acc_row(i, hh)] != 0) << i;
         }
         live_bits[m] = bits;
     }
-
-    const uint64_t kpool = c.k_pools[x.layer];
-    const int ntiles = (N + 31) >> 5;
     const f32x16_t zero = {};
-    // with four row blocks per wave the registers do not allow a second tile
-    constexpr bool kPrefetch = MBW <= 2;
 
     // ---------------- phase 1: per-row log-sum-exp ----------------
-    float Mw = -INFINITY;  // wave reference (log2 units)
-    if (q < ntiles) {
-        Tile t;
-        const int n = 32 * q + col;
-        load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int m = 0; m < MBW; ++m) {
-            if (mb0 + m >= MB) continue;
-            const f32x16_t acc = logits(A[m], t, zero);
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (((live_bits[m] >> i) & 1u) && n < N) mx = fmaxf(mx, acc[i]);
-        }
-        mx = wave_max(mx);
-        Mw = (mx == -INFINITY) ? 0.f : mx * kCs;
-    }
+    float Mw = -INFINITY;  // wave reference (log2 units), from the wave's first tile
     float sum[MBW][16];
 #pragma unroll
     for (int m = 0; m < MBW; ++m)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sum[m][i] = 0.f;
 
-    {
-        auto consume = [&](const Tile& t, int tt) {
-            const int n = 32 * tt + col;
-            const bool full = 32 * tt + 32 <= N;
+    for (int it = 0; it < iters; ++it) {
+        begin_iter(it);
+        if (!computes || it > jlast) continue;
+        const int tt = kQ * it + q;
+        const int n = kTileKeys * tt + col;
+        Tile t;
+        read_tile(t, slot_of(it));
+        if (it == 0) {  // the wave's reference: max live logit of its first tile
+            float mx = -INFINITY;
 #pragma unroll
             for (int m = 0; m < MBW; ++m) {
                 if (mb0 + m >= MB) continue;
                 const f32x16_t acc = logits(A[m], t, zero);
-                if (full) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        sum[m][i] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -Mw));
-                } else {
+                for (int i = 0; i < 16; ++i)
+                    if (((live_bits[m] >> i) & 1u) && n < N) mx = fmaxf(mx, acc[i]);
+            }
+            mx = wave_max(mx);
+            Mw = (mx == -INFINITY) ? 0.f : mx * kCs;
+        }
+        const bool full = kTileKeys * tt + kTileKeys <= N;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -Mw));
-                        sum[m][i] += (n < N) ? e : 0.f;
-                    }
+        for (int m = 0; m < MBW; ++m) {
+            if (mb0 + m >= MB) continue;
+            const f32x16_t acc = logits(A[m], t, zero);
+            if (full) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    sum[m][i] += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -Mw));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -Mw));
+                    sum[m][i] += (n < N) ? e : 0.f;
                 }
-            }
-        };
-        if (kPrefetch) {
-            // two tiles alternate: one is consumed while the next is in flight
-            Tile ta, tb;
-            int tt = q;
-            if (tt < ntiles) load_key(ta, kpool, s_bt, c.H, x.head, 32 * tt + col, N, hh);
-            while (tt < ntiles) {
-                if (tt + kTileWaves < ntiles)
-                    load_key(tb, kpool, s_bt, c.H, x.head, 32 * (tt + kTileWaves) + col, N, hh);
-                consume(ta, tt);
-                tt += kTileWaves;
-                if (tt >= ntiles) break;
-                if (tt + kTileWaves < ntiles)
-                    load_key(ta, kpool, s_bt, c.H, x.head, 32 * (tt + kTileWaves) + col, N, hh);
-                consume(tb, tt);
-                tt += kTileWaves;
-            }
-        } else {
-            for (int tt = q; tt < ntiles; tt += kTileWaves) {
-                Tile t;
-                load_key(t, kpool, s_bt, c.H, x.head, 32 * tt + col, N, hh);
-                consume(t, tt);
             }
         }
     }
-    // lanes -> waves -> rows
+    // lanes -> waves -> rows (no ring load is in flight from here on)
 #pragma unroll
     for (int m = 0; m < MBW; ++m) {
         if (mb0 + m >= MB) continue;
@@ -254,16 +335,16 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
             if (col == 0) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
         }
     }
-    if (lane == 0) s_M[w] = (q < ntiles) ? Mw : -INFINITY;
+    if (lane == 0) s_M[w] = (jlast >= 0 && computes) ? Mw : -INFINITY;
     __syncthreads();
     for (int j = tid; j < Kp; j += blockDim.x) {
         const int g = (j / 32) / MBW;
         float Mg = -INFINITY;
-        for (int k2 = 0; k2 < kTileWaves; ++k2) Mg = fmaxf(Mg, s_M[g * kTileWaves + k2]);
+        for (int k2 = 0; k2 < kQ; ++k2) Mg = fmaxf(Mg, s_M[g * kQ + k2]);
         float total = 0.f;
-        for (int k2 = 0; k2 < kTileWaves; ++k2) {
-            const float Mk = s_M[g * kTileWaves + k2];
-            if (Mk != -INFINITY) total += s_part[g * kTileWaves + k2][j] * exp2f(Mk - Mg);
+        for (int k2 = 0; k2 < kQ; ++k2) {
+            const float Mk = s_M[g * kQ + k2];
+            if (Mk != -INFINITY) total += s_part[g * kQ + k2][j] * exp2f(Mk - Mg);
         }
         const bool lv = s_live[j];
         const bool ok = total >= 0x1p-100f && total < INFINITY;
@@ -273,23 +354,25 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
     __syncthreads();
 
     if (s_rescue) {
-        // Exact fallback: per-row maximum over all keys first, then the sums
-        // against it (every term <= 1, the maximum term == 1).
+        // Exact fallback with direct loads: per-row maximum over all keys
+        // first, then the sums against it (every term <= 1, the maximum == 1).
 #pragma unroll
         for (int m = 0; m < MBW; ++m)
 #pragma unroll
             for (int i = 0; i < 16; ++i) sum[m][i] = -INFINITY;
-        for (int tt = q; tt < ntiles; tt += kTileWaves) {
-            Tile t;
-            const int n = 32 * tt + col;
-            load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
+        if (computes) {
+            for (int tt = q; tt < ntiles; tt += kQ) {
+                Tile t;
+                const int n = kTileKeys * tt + col;
+                load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
 #pragma unroll
-            for (int m = 0; m < MBW; ++m) {
-                if (mb0 + m >= MB) continue;
-                const f32x16_t acc = logits(A[m], t, zero);
+                for (int m = 0; m < MBW; ++m) {
+                    if (mb0 + m >= MB) continue;
+                    const f32x16_t acc = logits(A[m], t, zero);
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (n < N) sum[m][i] = fmaxf(sum[m][i], acc[i]);
+                    for (int i = 0; i < 16; ++i)
+                        if (n < N) sum[m][i] = fmaxf(sum[m][i], acc[i]);
+                }
             }
         }
 #pragma unroll
@@ -305,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
         for (int j = tid; j < Kp; j += blockDim.x) {
             const int g = (j / 32) / MBW;
             float R = -INFINITY;
-            for (int k2 = 0; k2 < kTileWaves; ++k2) R = fmaxf(R, s_part[g * kTileWaves + k2][j]);
+            for (int k2 = 0; k2 < kQ; ++k2) R = fmaxf(R, s_part[g * kQ + k2][j]);
             s_ref[j] = R * kCs;
         }
         __syncthreads();
@@ -318,9 +401,9 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
                 ref[i] = s_ref[32 * (mb0 + m) + acc_row(i, hh)];
                 acc_sum[i] = 0.f;
             }
-            for (int tt = q; tt < ntiles; tt += kTileWaves) {
+            for (int tt = q; tt < ntiles; tt += kQ) {
                 Tile t;
-                const int n = 32 * tt + col;
+                const int n = kTileKeys * tt + col;
                 load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
                 const f32x16_t acc = logits(A[m], t, zero);
 #pragma unroll
@@ -339,16 +422,18 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
         for (int j = tid; j < Kp; j += blockDim.x) {
             const int g = (j / 32) / MBW;
             float total = 0.f;
-            for (int k2 = 0; k2 < kTileWaves; ++k2) total += s_part[g * kTileWaves + k2][j];
+            for (int k2 = 0; k2 < kQ; ++k2) total += s_part[g * kQ + k2][j];
             s_lse2[j] = s_live[j] ? s_ref[j] + log2f(total) : INFINITY;
         }
         __syncthreads();
     }
 
-    if (lse_out) {
-        for (int j = tid; j < K; j += blockDim.x)
+    // written by group 0, which issues no ring loads
+    if (lse_out && group == 0) {
+        for (int j = tid; j < K; j += kQ * kWave)
             lse_out[(size_t)hc * K + j] = s_live[j] ? s_lse2[j] * kLn2 : __int_as_float(0x7fc00000);
     }
+    prologue();  // phase 2 streams the keys again
 
     // ---------------- phase 2: sigma(n) = exp(max_j s_jn - lse_j) ----------------
     f32x16_t Cf[MBW];
@@ -360,51 +445,39 @@ __global__ __launch_bounds__(kThreads) void beacon_score_kernel(
             Cf[m][i] = -l2 / kCs;
         }
     float* out = scores + (size_t)hc * stride;
-    const int iters = (ntiles + kTileWaves - 1) / kTileWaves;
-    // one step of the score loop: tile tt of this wave (if any), merged across
-    // the row groups; every wave runs the same number of steps (barriers)
-    auto step = [&](int it, const Tile& cur, Tile& nxt) {
-        const int tt = q + kTileWaves * it;
-        const int n = 32 * tt + col;
+    // Group 0 finishes a tile one iteration late, once group 1's partial
+    // maximum for it has passed the next barrier.
+    auto finalize = [&](int it, float mx) {
+        const int tt = kQ * it + q;
+        const int n = kTileKeys * tt + col;
+        if (it <= jlast && hh == 0 && n >= P && n < N) {
+            mx = fmaxf(mx, s_pmax[it & 1][q][col]);
+            const float sigma = __builtin_amdgcn_exp2f(mx * kCs);
+            out[n - P] = sigma + ((n >= N - window) ? bonus : 0.f);
+        }
+    };
+    float mx_prev = -INFINITY;
+    for (int it = 0; it < iters; ++it) {
+        begin_iter(it);
+        if (group == 0 && it > 0) finalize(it - 1, mx_prev);
         float mx = -INFINITY;
-        if (tt < ntiles) {
-            if (kPrefetch && tt + kTileWaves < ntiles)
-                load_key(nxt, kpool, s_bt, c.H, x.head, n + 32 * kTileWaves, N, hh);
+        if (it <= jlast && computes) {
+            Tile t;
+            read_tile(t, slot_of(it));
 #pragma unroll
             for (int m = 0; m < MBW; ++m) {
                 if (mb0 + m >= MB) continue;
-                const f32x16_t acc = logits(A[m], cur, Cf[m]);
+                const f32x16_t acc = logits(A[m], t, Cf[m]);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
             }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
         }
-        if (NG > 1) {  // merge the two row groups through LDS
-            if (group == 1 && hh == 0) s_pmax[q][col] = mx;
-            __syncthreads();
-            if (group == 0) mx = fmaxf(mx, s_pmax[q][col]);
-            __syncthreads();
-        }
-        if (group == 0 && hh == 0 && tt < ntiles && n >= P && n < N) {
-            const float sigma = __builtin_amdgcn_exp2f(mx * kCs);
-            out[n - P] = sigma + ((n >= N - window) ? bonus : 0.f);
-        }
-    };
-    if (kPrefetch) {
-        Tile ta, tb;
-        if (q < ntiles) load_key(ta, kpool, s_bt, c.H, x.head, 32 * q + col, N, hh);
-        for (int it = 0; it < iters; it += 2) {
-            step(it, ta, tb);
-            if (it + 1 < iters) step(it + 1, tb, ta);
-        }
-    } else {
-        for (int it = 0; it < iters; ++it) {
-            Tile t;
-            const int tt = q + kTileWaves * it;
-            if (tt < ntiles) load_key(t, kpool, s_bt, c.H, x.head, 32 * tt + col, N, hh);
-            step(it, t, t);
-        }
+        if (group == 1 && hh == 0) s_pmax[it & 1][q][col] = mx;
+        mx_prev = mx;
     }
+    ring_barrier();
+    if (group == 0) finalize(iters - 1, mx_prev);
 }
 
 }  // namespace
@@ -414,20 +487,16 @@ hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const i
                                float* lse, Check ck, int32_t* status, hipStream_t s) {
     const int HC = c.L * c.R * c.H;
     if (HC == 0) return hipSuccess;
-    // Two row groups of four waves (8 waves, 2 per SIMD) whenever K > 32, so
-    // that one wave's MFMA work overlaps another's exp/VALU work.
-    if (K <= 32) {
-        hipLaunchKernelGGL((beacon_score_kernel<1, 256>), dim3(HC), dim3(256), 0, s, c, beacons,
-                           counts, K, window, bonus, scores, stride, lse, ck, status);
-    } else if (K <= 64) {
-        hipLaunchKernelGGL((beacon_score_kernel<1, 512>), dim3(HC), dim3(512), 0, s, c, beacons,
-                           counts, K, window, bonus, scores, stride, lse, ck, status);
+    // row blocks per wave: 1 for K <= 64, 2 for K <= 128, 4 for K <= 256
+    if (K <= 64) {
+        hipLaunchKernelGGL(beacon_score_kernel<1>, dim3(HC), dim3(kWaves * kWave), 0, s, c,
+                           beacons, counts, K, window, bonus, scores, stride, lse, ck, status);
     } else if (K <= 128) {
-        hipLaunchKernelGGL((beacon_score_kernel<2, 512>), dim3(HC), dim3(512), 0, s, c, beacons,
-                           counts, K, window, bonus, scores, stride, lse, ck, status);
+        hipLaunchKernelGGL(beacon_score_kernel<2>, dim3(HC), dim3(kWaves * kWave), 0, s, c,
+                           beacons, counts, K, window, bonus, scores, stride, lse, ck, status);
     } else {
-        hipLaunchKernelGGL((beacon_score_kernel<4, 512>), dim3(HC), dim3(512), 0, s, c, beacons,
-                           counts, K, window, bonus, scores, stride, lse, ck, status);
+        hipLaunchKernelGGL(beacon_score_kernel<4>, dim3(HC), dim3(kWaves * kWave), 0, s, c,
+                           beacons, counts, K, window, bonus, scores, stride, lse, ck, status);
     }
     return hipGetLastError();
 }
