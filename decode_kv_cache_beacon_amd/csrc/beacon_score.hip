@@ -47,6 +47,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kCs = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
+constexpr float kInvCs = 7.842065147748378f;  // sqrt(128) / log2(e)
 constexpr int kWaves = 8;
 constexpr int kQ = 4;                              // tile phases = waves per row group
 constexpr int kTileKeys = 32;
@@ -93,21 +94,16 @@ __device__ __forceinline__ void wait_ring(int n) {
 // address m0 + 16 l.  Written as inline assembly so that the compiler, which
 // does not see these loads, does not make every later LDS access of the wave
 // wait for all of them; their completion is awaited by wait_ring only.  The
-// s_nop covers the wait state the hardware needs between writing M0 and an
-// LDS DMA that reads it.  M0 is reserved by the compiler, which sets it right
-// before each of its own uses; nothing else in this kernel reads it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
+// compiler sets M0 for the statement; the s_nop covers the wait state the
+// hardware needs between writing M0 and an LDS DMA that reads it.
 __device__ __forceinline__ void dma16(uint64_t g, uint32_t m0) {
     asm volatile(
-        "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
         "global_load_lds_dwordx4 %0, off"
         :
-        : "v"(g), "s"(m0)
-        : "memory", "m0");
+        : "v"(g), "{m0}"(m0)
+        : "memory");
 }
-#pragma clang diagnostic pop
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -133,22 +129,42 @@ __device__ __forceinline__ f32x16_t logits(const bf16x8_t (&a)[8], const Tile& t
     return c;
 }
 
+// Cross-lane reductions on the VALU (DPP and lane swaps, no LDS traffic).
+// DPP move of v (lanes without a source keep `old`).
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ float dpp(float v, float old) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), kCtrl,
+                                                      kRowMask, 0xF, false));
+}
+// op over the 32 lanes of each wave half; the result is valid in lanes 16-31
+// (lower half) and 48-63 (upper half): pairs within quads, quads within 8,
+// 8 within rows of 16 (mirrors), then row 0 into row 1 and row 2 into row 3.
+template <typename Op>
+__device__ __forceinline__ float half_reduce(float v, Op op) {
+    v = op(v, dpp<0xB1>(v, v));        // quad_perm [1,0,3,2]
+    v = op(v, dpp<0x4E>(v, v));        // quad_perm [2,3,0,1]
+    v = op(v, dpp<0x141>(v, v));       // row_half_mirror
+    v = op(v, dpp<0x140>(v, v));       // row_mirror
+    return op(v, dpp<0x142, 0xA>(v, v));  // row_bcast:15 into rows 1 and 3
+}
+constexpr int kHalfLead = 16;  // a lane (per half) holding the half_reduce result
+// max(v, v of lane l ^ 32), in every lane
+__device__ __forceinline__ float max_halves(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+struct AddOp {
+    __device__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+    __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+__device__ __forceinline__ float half_sum(float v) { return half_reduce(v, AddOp{}); }
+__device__ __forceinline__ float half_max(float v) { return half_reduce(v, MaxOp{}); }
+// maximum over the wave, uniform
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-// Sum (or max) over the 32 lanes of one lane half.
-__device__ __forceinline__ float half_sum(float v) {
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
-}
-__device__ __forceinline__ float half_max(float v) {
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    const float h = max_halves(half_max(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), kHalfLead));
 }
 
 template <int MBW>
@@ -163,7 +179,7 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
     __shared__ float s_lse2[BKV_MAX_BEACONS];
     __shared__ float s_ref[BKV_MAX_BEACONS];
     __shared__ int s_live[BKV_MAX_BEACONS];
-    __shared__ float s_pmax[2][kQ][32];
+    __shared__ float s_pmax[3][kQ][32];
     __shared__ int s_rescue;
 
     const int hc = blockIdx.x;
@@ -173,7 +189,7 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
     const int P = c.prompt_len[x.req];
 
     const int tid = threadIdx.x;
-    const int w = tid / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
     const int lane = tid & (kWave - 1);
     const int hh = lane >> 5;
     const int col = lane & 31;
@@ -202,31 +218,40 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
 
     const uint64_t kpool = c.k_pools[x.layer];
     const int ntiles = (N + kTileKeys - 1) / kTileKeys;
-    const int iters = (ntiles + kQ - 1) / kQ;
-    // last iteration in which this wave's phase has a tile (-1 if none)
+    const int iters = (ntiles + kQ - 1) / kQ;  // iterations per phase
+    const int G = 2 * iters;                    // the stream: phase 1, then phase 2
+    // last iteration of a phase in which this wave's phase q has a tile (-1 if none)
     const int jlast = (q < ntiles) ? (ntiles - 1 - q) / kQ : -1;
 
     // DMA of key tile t into ring slot `slot` (issued by a group-1 wave).  Lane
     // l of instruction i fills LDS bytes [1024 i + 16 l, +16) of the slot: row
     // r = 4i + l/16, chunk position p = l%16, which holds global chunk
-    // p ^ (r & 15) of key 32t + r (key N-1 past the end).
+    // p ^ (r & 15) of key 32t + r (key N-1 past the end, so a tile past the
+    // last one re-reads one cached row and is never consumed).
     const uint32_t ring0 = lds_addr(s_ring);
     auto issue_tile = [&](int t, int slot) {
         const uint32_t dst = __builtin_amdgcn_readfirstlane(ring0 + slot * kTileBytes);
+        // Every row of a tile lies in block 2t (rows 0-15) or 2t+1 (rows
+        // 16-31), clamped rows included, and a tile past the end reads the
+        // last block.
+        const int b_lo = __builtin_amdgcn_readfirstlane(s_bt[min(2 * t, nb - 1)]);
+        const int b_hi = __builtin_amdgcn_readfirstlane(s_bt[min(2 * t + 1, nb - 1)]);
+        const uint64_t base_lo = kpool + row_offset(b_lo, c.H, x.head, 0);
+        const uint64_t base_hi = kpool + row_offset(b_hi, c.H, x.head, 0);
 #pragma unroll
         for (int i = 0; i < kDmaPerTile; ++i) {
             const int r = 4 * i + (lane >> 4);
             const int ch = (lane & 15) ^ (r & 15);
             const int n = min(kTileKeys * t + r, N - 1);
-            const uint64_t g = kpool + row_offset(s_bt[n >> 4], c.H, x.head, n & 15) + 16 * ch;
-            dma16(g, dst + 1024 * i);
+            const uint32_t off = (uint32_t)(n & (kBlock - 1)) * kRowBytes + 16 * ch;
+            dma16((i < kDmaPerTile / 2 ? base_lo : base_hi) + off, dst + 1024 * i);
         }
     };
-    auto slot_of = [&](int it) { return (it % kRingIters) * kQ + q; };
-    auto prologue = [&]() {
-        if (loader)
-            for (int j = 0; j < kDepth && j <= jlast; ++j) issue_tile(kQ * j + q, slot_of(j));
-    };
+    // Stream iteration g covers tile 4j + q of phase 1 (g < iters, j = g) or
+    // phase 2 (j = g - iters).  Every loader issues one tile per iteration, so
+    // a wave's outstanding loads are always whole iterations.
+    auto slot_of = [&](int g) { return (g % kRingIters) * kQ + q; };
+    auto tile_of = [&](int g) { return kQ * (g < iters ? g : g - iters) + q; };
     // this lane's key column from a ring slot: the B fragment of k-step s is
     // global chunk 2s + hh of row `col`
     auto read_tile = [&](Tile& t, int slot) {
@@ -237,38 +262,68 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
             t.b[s] = *reinterpret_cast<const bf16x8_t*>(row + 16 * p);
         }
     };
-    // hand-over of iteration `it`: the loaders wait for their DMA of it, all
-    // waves pass the barrier (iteration it-1's reads are then done), and the
-    // slot read in it-1 is refilled with iteration it + kDepth
-    auto begin_iter = [&](int it) {
-        if (loader) wait_ring(min(kDepth - 1, jlast - it));
+    // hand-over of iteration g: the loaders wait for their DMA of g, all waves
+    // pass the barrier (iteration g-1's reads are then done), and the slot read
+    // in g-1 is refilled with iteration g + kDepth
+    auto begin_iter = [&](int g) {
+        if (loader) wait_ring(min(kDepth - 1, G - 1 - g));
         ring_barrier();
-        if (loader && it + kDepth <= jlast) issue_tile(kQ * (it + kDepth) + q, slot_of(it + kDepth));
+        if (loader && g + kDepth < G) issue_tile(tile_of(g + kDepth), slot_of(g + kDepth));
     };
 
-    prologue();  // the first tiles are in flight while the beacons are prepared
-
     // A fragments: beacon row 32*(mb0+m) + col, bf16 (RNE) of the fp32 state.
+    // Dead rows load row 0 (present whenever the block is) and are zeroed.
+    // The loads of the first blocks (both of two, one of four) go out before
+    // the first ring tiles, so that waiting for them does not also wait for
+    // the tiles.
     bf16x8_t A[MBW][8];
+    auto load_block = [&](int m, float4 (&r)[8][2]) {
+        const int j = 32 * (mb0 + m) + col;
+        const float* br = beacons + ((size_t)hc * K + (s_live[j] ? j : 0)) * kHeadDim + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            r[s][0] = *reinterpret_cast<const float4*>(br + 16 * s);
+            r[s][1] = *reinterpret_cast<const float4*>(br + 16 * s + 4);
+        }
+    };
+    auto convert_block = [&](int m, const float4 (&r)[8][2]) {
+        const uint32_t keep = s_live[32 * (mb0 + m) + col] ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+            const float4 lo = r[s][0], hi = r[s][1];
+            u32x4 pk;
+            pk.x = ((uint32_t)to_bf16_rne(lo.x) | ((uint32_t)to_bf16_rne(lo.y) << 16)) & keep;
+            pk.y = ((uint32_t)to_bf16_rne(lo.z) | ((uint32_t)to_bf16_rne(lo.w) << 16)) & keep;
+            pk.z = ((uint32_t)to_bf16_rne(hi.x) | ((uint32_t)to_bf16_rne(hi.y) << 16)) & keep;
+            pk.w = ((uint32_t)to_bf16_rne(hi.z) | ((uint32_t)to_bf16_rne(hi.w) << 16)) & keep;
+            A[m][s] = as_bf16x8(pk);
+        }
+    };
+    constexpr int kPre = MBW <= 2 ? MBW : 1;
+    float4 raw[kPre][8][2];
+#pragma unroll
+    for (int m = 0; m < kPre; ++m)
+        if (mb0 + m < MB) load_block(m, raw[m]);
+    if (loader)  // the first ring tiles are in flight while the beacons are prepared
+        for (int g = 0; g < kDepth && g < G; ++g) issue_tile(tile_of(g), slot_of(g));
+#pragma unroll
+    for (int m = 0; m < MBW; ++m) {
+        if (mb0 + m < MB) {
+            if (m < kPre) {
+                convert_block(m, raw[m < kPre ? m : 0]);
+            } else {
+                float4 r[8][2];
+                load_block(m, r);
+                convert_block(m, r);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 8; ++s) A[m][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        }
+    }
     uint32_t live_bits[MBW];
 #pragma unroll
     for (int m = 0; m < MBW; ++m) {
-        const int j = 32 * (mb0 + m) + col;
-        const bool lv = (mb0 + m < MB) && s_live[j];
-        const float* br = beacons + ((size_t)hc * K + (lv ? j : 0)) * kHeadDim + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            u32x4 pk = {0u, 0u, 0u, 0u};
-            if (lv) {
-                const float4 lo = *reinterpret_cast<const float4*>(br + 16 * s);
-                const float4 hi = *reinterpret_cast<const float4*>(br + 16 * s + 4);
-                pk.x = (uint32_t)to_bf16_rne(lo.x) | ((uint32_t)to_bf16_rne(lo.y) << 16);
-                pk.y = (uint32_t)to_bf16_rne(lo.z) | ((uint32_t)to_bf16_rne(lo.w) << 16);
-                pk.z = (uint32_t)to_bf16_rne(hi.x) | ((uint32_t)to_bf16_rne(hi.y) << 16);
-                pk.w = (uint32_t)to_bf16_rne(hi.z) | ((uint32_t)to_bf16_rne(hi.w) << 16);
-            }
-            A[m][s] = as_bf16x8(pk);
-        }
         uint32_t bits = 0;
         if (mb0 + m < MB) {
 #pragma unroll
@@ -288,7 +343,7 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
         for (int i = 0; i < 16; ++i) sum[m][i] = 0.f;
 
     for (int it = 0; it < iters; ++it) {
-        begin_iter(it);
+        begin_iter(it);  // stream iteration g = it
         if (!computes || it > jlast) continue;
         const int tt = kQ * it + q;
         const int n = kTileKeys * tt + col;
@@ -325,18 +380,19 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
             }
         }
     }
-    // lanes -> waves -> rows (no ring load is in flight from here on)
+    // lanes -> waves -> rows.  The first phase-2 tiles are in flight, so the
+    // exchange uses ring barriers (LDS only) rather than fenced ones.
 #pragma unroll
     for (int m = 0; m < MBW; ++m) {
         if (mb0 + m >= MB) continue;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float v = half_sum(sum[m][i]);
-            if (col == 0) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
+            if (col == kHalfLead) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
         }
     }
     if (lane == 0) s_M[w] = (jlast >= 0 && computes) ? Mw : -INFINITY;
-    __syncthreads();
+    ring_barrier();
     for (int j = tid; j < Kp; j += blockDim.x) {
         const int g = (j / 32) / MBW;
         float Mg = -INFINITY;
@@ -351,7 +407,7 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
         if (lv && !ok) s_rescue = 1;
         s_lse2[j] = lv ? Mg + log2f(total) : INFINITY;
     }
-    __syncthreads();
+    ring_barrier();
 
     if (s_rescue) {
         // Exact fallback with direct loads: per-row maximum over all keys
@@ -381,7 +437,7 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float v = half_max(sum[m][i]);
-                if (col == 0) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
+                if (col == kHalfLead) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
             }
         }
         __syncthreads();
@@ -415,7 +471,7 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float v = half_sum(acc_sum[i]);
-                if (col == 0) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
+                if (col == kHalfLead) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
             }
         }
         __syncthreads();
@@ -433,7 +489,6 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
         for (int j = tid; j < K; j += kQ * kWave)
             lse_out[(size_t)hc * K + j] = s_live[j] ? s_lse2[j] * kLn2 : __int_as_float(0x7fc00000);
     }
-    prologue();  // phase 2 streams the keys again
 
     // ---------------- phase 2: sigma(n) = exp(max_j s_jn - lse_j) ----------------
     f32x16_t Cf[MBW];
@@ -442,28 +497,30 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float l2 = (mb0 + m < MB) ? s_lse2[32 * (mb0 + m) + acc_row(i, hh)] : INFINITY;
-            Cf[m][i] = -l2 / kCs;
+            Cf[m][i] = -l2 * kInvCs;
         }
     float* out = scores + (size_t)hc * stride;
-    // Group 0 finishes a tile one iteration late, once group 1's partial
-    // maximum for it has passed the next barrier.
-    auto finalize = [&](int it, float mx) {
-        const int tt = kQ * it + q;
-        const int n = kTileKeys * tt + col;
-        if (it <= jlast && hh == 0 && n >= P && n < N) {
-            mx = fmaxf(mx, s_pmax[it & 1][q][col]);
+    // Group 1's partial maximum of tile j passes through s_pmax[j % 3]; group 0
+    // finishes tile j once that has crossed a barrier.
+    auto finalize = [&](int j, float mx) {
+        const int n = kTileKeys * (kQ * j + q) + col;
+        if (j <= jlast && hh == 0 && n >= P && n < N) {
+            mx = fmaxf(mx, s_pmax[j % 3][q][col]);
             const float sigma = __builtin_amdgcn_exp2f(mx * kCs);
             out[n - P] = sigma + ((n >= N - window) ? bonus : 0.f);
         }
     };
+    auto publish = [&](int j, float mx) {
+        if (group == 1 && hh == 0) s_pmax[j % 3][q][col] = mx;
+    };
     float mx_prev = -INFINITY;
     for (int it = 0; it < iters; ++it) {
-        begin_iter(it);
+        begin_iter(iters + it);  // stream iteration g = iters + it
         if (group == 0 && it > 0) finalize(it - 1, mx_prev);
         float mx = -INFINITY;
         if (it <= jlast && computes) {
             Tile t;
-            read_tile(t, slot_of(it));
+            read_tile(t, slot_of(iters + it));
 #pragma unroll
             for (int m = 0; m < MBW; ++m) {
                 if (mb0 + m >= MB) continue;
@@ -471,9 +528,9 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, acc[i]);
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = max_halves(mx);
         }
-        if (group == 1 && hh == 0) s_pmax[it & 1][q][col] = mx;
+        publish(it, mx);
         mx_prev = mx;
     }
     ring_barrier();
