@@ -146,6 +146,112 @@ def stored_traffic(kernel):
     return e.get("bytes_per_launch")
 
 
+# kernel symbol fragment -> kernel id
+KERNEL_SYMBOLS = {
+    "beacon_update_kernel": "beacon_update",
+    "beacon_score_kernel": "beacon_score",
+    "topk_select_kernel": "topk_select",
+    "kv_compact_kernel": "kv_compact",
+    "random_score_kernel": "random_score",
+}
+COPY_SYMBOL = "__amd_rocclr_copyBuffer"
+PROFILE_CMDS = {
+    "trace": ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -f csv -d <prof-dir> "
+              "-o bench -- python3 <repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline"),
+    "pmc": ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} -f csv -d <pmc-dir>/{c} -o {c} -- "
+            "python3 <repo>/bench.py --steps 2 --warmup 0 --no-random --no-cpu-baseline"),
+    "summary": "python bench.py --summarize-profiles <prof-dir> <pmc-dir>",
+}
+
+
+def summarize_profiles(prof_dir, pmc_dir, workload):
+    """Write the committed summaries from rocprofv3 output: per-kernel
+    durations (kernel trace), HBM bytes per launch from FETCH_SIZE and
+    WRITE_SIZE, each scaled by what the counter reads for the 4 GiB device
+    copy the benchmark also runs, and profiles/traffic.json for the roofline."""
+    import csv
+    import glob
+    import statistics
+
+    def kid(name):
+        return next((v for k, v in KERNEL_SYMBOLS.items() if k in name), None)
+
+    rows = list(csv.DictReader(open(glob.glob(os.path.join(prof_dir, "*kernel_trace.csv"))[0])))
+    dur = {}
+    for r in rows:
+        k = kid(r["Kernel_Name"])
+        if k:
+            dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
+    out = os.path.join(ROOT, "profiles")
+    os.makedirs(out, exist_ok=True)
+    lines = [f"# Kernel durations, workload {workload}", "",
+             "rocprofv3 kernel trace of one benchmark run (5 timed + 1 warm-up beacon passes, "
+             "then the same number of random-selector passes; top-B selection and compaction "
+             "run in both).", "", "Command:", "", "    " + PROFILE_CMDS["trace"], "",
+             "| kernel | launches | mean ms | min ms | max ms |", "|---|---|---|---|---|"]
+    for k in KERNEL_SOURCES:
+        if k in dur:
+            d = dur[k]
+            lines.append(f"| {k} | {len(d)} | {statistics.mean(d):.3f} | {min(d):.3f} | "
+                         f"{max(d):.3f} |")
+    with open(os.path.join(out, f"{workload}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    counters = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        path = glob.glob(os.path.join(pmc_dir, c, "*counter_collection.csv"))[0]
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != c:
+                continue
+            name = r["Kernel_Name"]
+            k = "copy" if COPY_SYMBOL in name else kid(name)
+            if k:
+                per.setdefault(k, []).append(float(r["Counter_Value"]))
+        counters[c] = per
+    # the 4 GiB device copy: the largest copyBuffer dispatches
+    copy_bytes = 1 << 32
+    big = max(counters["WRITE_SIZE"]["copy"])
+    n_big = sum(1 for v in counters["WRITE_SIZE"]["copy"] if v >= 0.99 * big)
+    fetch_copy = sorted(counters["FETCH_SIZE"]["copy"])[-n_big:]
+    write_copy = sorted(counters["WRITE_SIZE"]["copy"])[-n_big:]
+    f_read = copy_bytes / (statistics.mean(fetch_copy) * 1024)
+    f_write = copy_bytes / (statistics.mean(write_copy) * 1024)
+    traffic = {"_calibration": {
+        "copy_bytes_read": copy_bytes, "copy_bytes_written": copy_bytes,
+        "copy_fetch_kib": statistics.mean(fetch_copy), "copy_write_kib": statistics.mean(write_copy),
+        "read_factor": f_read, "write_factor": f_write, "workload": workload,
+        "commands": [PROFILE_CMDS["pmc"].format(c="FETCH_SIZE"),
+                     PROFILE_CMDS["pmc"].format(c="WRITE_SIZE"), PROFILE_CMDS["summary"]]}}
+    lines = [f"# HBM traffic per launch, workload {workload}", "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the dispatches of the beacon "
+             "passes) from two rocprofv3 counter runs, each scaled by what the same counter reads "
+             f"for a plain 4 GiB device copy: read factor {f_read:.4f}, write factor "
+             f"{f_write:.4f}.", "", "Commands:", "",
+             "    " + PROFILE_CMDS["pmc"].format(c="FETCH_SIZE"),
+             "    " + PROFILE_CMDS["pmc"].format(c="WRITE_SIZE"),
+             "    " + PROFILE_CMDS["summary"], "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | written GB | total GB | "
+             "source hash |", "|---|---|---|---|---|---|---|"]
+    for k in KERNEL_SOURCES:
+        if k not in counters["FETCH_SIZE"] or k not in counters["WRITE_SIZE"]:
+            continue
+        fk = statistics.mean(counters["FETCH_SIZE"][k])
+        wk = statistics.mean(counters["WRITE_SIZE"][k])
+        rb, wb = fk * 1024 * f_read, wk * 1024 * f_write
+        sha = kernel_source_hash(k)
+        traffic[k] = {"fetch_kib": fk, "write_kib": wk, "bytes_read": rb, "bytes_written": wb,
+                      "bytes_per_launch": rb + wb, "source_sha": sha}
+        lines.append(f"| {k} | {fk:.0f} | {wk:.0f} | {rb / 1e9:.2f} | {wb / 1e9:.2f} | "
+                     f"{(rb + wb) / 1e9:.2f} | {sha} |")
+    with open(os.path.join(out, f"{workload}_hbm_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(out, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    print(f"wrote profiles/{workload}_kernel_trace.md, profiles/{workload}_hbm_counters.md, "
+          "profiles/traffic.json")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,7 +263,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 4 GiB device copy (for counter calibration)")
+    ap.add_argument("--summarize-profiles", nargs=2, metavar=("PROF_DIR", "PMC_DIR"),
+                    help="write profiles/ summaries from rocprofv3 output and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, args.workload)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

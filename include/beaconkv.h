@@ -83,7 +83,10 @@ enum { BKV_SELECT_BEACON = 0, BKV_SELECT_RANDOM = 1 };   /* selector of bkv_evic
  * Layer pool l holds bf16 [num_blocks][n_kv_heads][block_size][head_dim];
  * slot n of request r, head h lives in block block_table[r][n / block_size]
  * at row n % block_size.  A dense cache is an identity block table.  Every
- * pool address must be 16-byte aligned. */
+ * pool address must be 16-byte aligned.  A request holds at most
+ * max_blocks * block_size <= 32768 slots (the kernels stage a request's block
+ * table in LDS); n_layers * n_requests * n_kv_heads and num_blocks must fit
+ * in int32.  Violations return BKV_ERR_INVALID before anything is enqueued. */
 typedef struct bkv_cache {
     int32_t n_layers;
     int32_t n_requests;

@@ -1,0 +1,114 @@
+"""Full-size parity: one whole beacon eviction pass over the 36-layer, 128-request
+serving workload (36864 head-caches, 2112 cached keys each, budget 2048,
+128 beacons, 256 buffered queries per head-cache), launched exactly as the
+benchmark launches it (one bkv_evict_pass over all head-caches, scores in a
+[HC, 1088] buffer; the assignment output is also requested here so the
+maintenance step can be replayed).
+
+The oracle cannot replay 36864 head-caches in seconds, so it checks a spread
+sample of them one by one (first and last head-caches, and a seeded draw over
+layers, requests and heads), to the same bars as the small cases; properties
+that hold for every head-cache are checked on all of them on the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_kv_cache_beacon_amd import synth
+from tests.gpu_util import ASSIGN_TOL, check_scores, check_selection, keep_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def gather_head(pool, bt_row, h, N):
+    """uint16 [N, 128] rows of head h of one request (device gather, host copy)."""
+    blocks = bt_row[: (N + synth.BLOCK - 1) // synth.BLOCK].long()
+    rows = pool[blocks, h].reshape(-1, pool.shape[-1])[:N]
+    return synth.bits(rows)
+
+
+def test_full_size_serving_pass():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from decode_kv_cache_beacon_amd import beaconkv as bk
+
+    wl = synth.WORKLOADS["serving_r128"]
+    dev = torch.device("cuda")
+    say("full size", wl.name, "generate")
+    batch = synth.make_batch(wl, dev)
+    cache = bk.PagedCache(batch.k_pools, batch.v_pools, batch.block_table, batch.seq_len,
+                          batch.prompt_len)
+    L, R, H = cache.n_layers, cache.n_requests, cache.n_kv_heads
+    HC, B, K, W = cache.n_head_caches, wl.budget, wl.n_beacons, wl.window
+    N = batch.seq_len.cpu().numpy()
+    P = batch.prompt_len.cpu().numpy()
+    stride = int((N - P).max())
+    T, G = wl.steps, wl.group
+
+    rng = np.random.default_rng(2024)
+    sample = sorted({0, HC - 1, *rng.choice(HC, 22, replace=False).tolist()})
+    before = {}
+    bt = batch.block_table
+    for hc in sample:
+        layer, r, h = hc // (R * H), (hc // H) % R, hc % H
+        before[hc] = dict(
+            keys=gather_head(batch.k_pools[layer], bt[r], h, int(N[r])),
+            vals=gather_head(batch.v_pools[layer], bt[r], h, int(N[r])),
+            q=synth.bits(batch.queries[hc]),
+            b=batch.beacons[hc].cpu().numpy().copy(),
+            c=batch.counts[hc].cpu().numpy().copy())
+    count_sum0 = batch.counts.sum(1).cpu()
+
+    scores = torch.zeros((HC, stride), dtype=torch.float32, device=dev)
+    keep = torch.full((HC, B), -7, dtype=torch.int32, device=dev)
+    assign = torch.zeros((HC, T * G), dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    say("full size pass")
+    bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=batch.queries,
+                      beacons=batch.beacons, counts=batch.counts, window=W, bonus=wl.bonus,
+                      assign=assign, scores_out=scores, keep_out=keep, score_stride=stride,
+                      status=status, check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+
+    # properties of every head-cache
+    say("full size properties")
+    kp = keep.cpu().numpy()
+    for r in range(R):
+        rows = kp[np.arange(L * H) // H * (R * H) + r * H + np.arange(L * H) % H]
+        nk = min(int(N[r]), B)
+        assert (rows[:, : int(P[r])] == np.arange(int(P[r]))).all()
+        assert (np.diff(rows[:, :nk], axis=1) > 0).all() and (rows[:, :nk] < N[r]).all()
+    assert torch.equal(batch.counts.sum(1).cpu(), count_sum0 + T * G)
+    a = assign.cpu()
+    assert int(a.min()) >= 0 and int(a.max()) < K
+    sc = scores.cpu().numpy()
+    assert np.isfinite(sc).all() and (sc >= 0).all()
+
+    # the sample, one head-cache at a time
+    sn = scores.cpu().numpy()
+    for hc in sample:
+        layer, r, h = hc // (R * H), (hc // H) % R, hc % H
+        n, p = int(N[r]), int(P[r])
+        x = before[hc]
+        say("full size head-cache", hc, "layer", layer, "request", r, "head", h)
+        ob, oc, gap = oracle.beacon_update_forced(x["q"], x["b"], x["c"], a[hc].numpy())
+        assert gap.max() <= ASSIGN_TOL, hc
+        assert np.array_equal(ob.view(np.int32), batch.beacons[hc].cpu().numpy().view(np.int32))
+        assert np.array_equal(oc, batch.counts[hc].cpu().numpy())
+        os_, _ = oracle.beacon_score(x["keys"], ob, oc, p, W, wl.bonus)
+        gs = sn[hc, : n - p]
+        check_scores(gs, os_, f"full size hc {hc}")
+        k = keep_rows(kp[hc])
+        check_selection(k, oracle.topk_select(os_, n, p, B), os_, n, p, B, f"hc {hc}")
+        assert np.array_equal(k, oracle.topk_select(gs.astype(np.float64), n, p, B)), hc
+        nk = len(k)
+        ko = gather_head(batch.k_pools[layer], bt[r], h, n)
+        vo = gather_head(batch.v_pools[layer], bt[r], h, n)
+        assert np.array_equal(ko[:nk], oracle.kv_compact(x["keys"], k)), hc
+        assert np.array_equal(vo[:nk], oracle.kv_compact(x["vals"], k)), hc
