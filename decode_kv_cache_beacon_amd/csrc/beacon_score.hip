@@ -8,32 +8,37 @@
 // The traversal of the paged keys is the extra pass a content-dependent
 // selector costs (Random Attention article, section "发现四").
 //
-// How (one 8-wave workgroup per head-cache, gfx950):
+// How (one 8-wave workgroup per head-cache, two workgroups per CU, gfx950):
 //   - The beacon.key logits are a [K x 128] x [128 x N] contraction: bf16 MFMA
 //     v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Beacons are the A
 //     operand (rows, kept in registers for the whole head), 32 keys form the B
 //     operand (columns), so each lane owns one key column and 16 beacon rows of
-//     a 32x32 result.  Rows are split between two groups of four waves; wave
-//     (group g, phase q) consumes key tiles q, q+4, q+8, ...
-//   - Key tiles (32 keys = 8 KiB) stream through a 16-tile LDS ring filled by
+//     a 32x32 result.  The rows are split between four groups of two waves
+//     (32 rows per wave up to K = 128, 64 beyond); wave (group g, phase q)
+//     consumes key tiles q, q+2, q+4, ...
+//   - Key tiles (32 keys = 8 KiB) stream through an 8-tile LDS ring filled by
 //     direct-to-LDS DMA (global_load_lds_dwordx4): each load instruction moves
 //     1 KiB of whole key rows, the ring is refilled three iterations ahead, and
-//     each tile serves both row groups.  A row's 16-byte chunks are
+//     each tile serves all four row groups.  A row's 16-byte chunks are
 //     XOR-swizzled by the row index so that the fragment reads are free of
-//     bank conflicts.  The four waves of group 1 issue all the DMA, so their
-//     vmcnt counts ring loads only; one barrier per iteration hands the tiles
-//     over.
+//     bank conflicts.  The two waves of the last group issue all the DMA, so
+//     their vmcnt counts ring loads only; one barrier per iteration hands the
+//     tiles over.  The load stream runs on from phase 1 into phase 2.
+//   - Two workgroups share a CU (64 KiB ring each, at most 128 registers per
+//     wave), so one head-cache's set-up (request checks, block table, beacon
+//     loads) overlaps the other's streaming, and the SIMDs interleave four
+//     waves' MFMA and exponential work.
 //   - Phase 1 (log-sum-exp per beacon): per lane and row a running sum of
 //     exp2(acc * log2(e)/sqrt(d) - M) with one reference M per wave taken from
-//     the wave's first tile; lanes, then waves, are merged in LDS.  If any live
-//     row's sum overflows or underflows (logit spread beyond the fp32 exponent
-//     range) the head is redone exactly with direct loads: an all-key maximum
-//     per row first, then the sums against that maximum.
+//     the wave's first tile; lanes (DPP), then waves (LDS) are merged.  If any
+//     live row's sum overflows or underflows (logit spread beyond the fp32
+//     exponent range) the head is redone exactly with direct loads: an all-key
+//     maximum per row first, then the sums against that maximum.
 //   - Phase 2 (score): the keys stream through the ring again (the re-read is
-//     served by L2/MALL) and the MFMA accumulator starts from C = -lse_j (in
-//     accumulator units), so the subtraction is free; each lane takes the max
-//     over its rows, the two row groups are merged through LDS one iteration
-//     later, and one exp2 per key gives sigma(n).
+//     mostly served by the memory-side cache) and the MFMA accumulator starts
+//     from C = -lse_j (in accumulator units), so the subtraction is free; each
+//     lane takes the max over its rows, the row groups are merged through LDS
+//     one iteration later, and one exp2 per key gives sigma(n).
 // Scaling by 1/sqrt(d) happens in fp32 after accumulation; the bf16 beacons
 // are never pre-scaled.
 
@@ -49,12 +54,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kCs = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
 constexpr float kInvCs = 7.842065147748378f;  // sqrt(128) / log2(e)
 constexpr int kWaves = 8;
-constexpr int kQ = 4;                              // tile phases = waves per row group
+constexpr int kGroups = 4;                         // row groups
+constexpr int kQ = kWaves / kGroups;               // tile phases = waves per row group
 constexpr int kTileKeys = 32;
 constexpr int kTileBytes = kTileKeys * kRowBytes;  // 8 KiB
 constexpr int kDepth = 3;                          // ring refilled this many iterations ahead
 constexpr int kRingIters = kDepth + 1;
-constexpr int kRingTiles = kQ * kRingIters;        // 16 tiles = 128 KiB
+constexpr int kRingTiles = kQ * kRingIters;        // 8 tiles = 64 KiB
 constexpr int kDmaPerTile = kTileBytes / 1024;     // instructions of 64 lanes x 16 B
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -167,19 +173,21 @@ __device__ __forceinline__ float wave_max(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), kHalfLead));
 }
 
+// Two workgroups share a CU (16 waves) while a wave needs at most 128
+// registers, so one head-cache's set-up overlaps another's streaming.
 template <int MBW>
-__global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
+__global__ __launch_bounds__(kWaves * kWave, MBW == 1 ? 4 : 2) void beacon_score_kernel(
     CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
     int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
     Check ck, int32_t* status) {
     __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kRingTiles * kTileBytes];
     __shared__ int s_bt[kMaxBlocksPerReq];
-    __shared__ float s_part[kWaves][BKV_MAX_BEACONS];
+    __shared__ float s_part[kWaves][32 * MBW];  // per wave, its own rows
     __shared__ float s_M[kWaves];
     __shared__ float s_lse2[BKV_MAX_BEACONS];
     __shared__ float s_ref[BKV_MAX_BEACONS];
     __shared__ int s_live[BKV_MAX_BEACONS];
-    __shared__ float s_pmax[3][kQ][32];
+    __shared__ float s_pmax[3][kGroups - 1][kQ][32];
     __shared__ int s_rescue;
 
     const int hc = blockIdx.x;
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
     const int col = lane & 31;
     const int group = w / kQ;
     const int q = w % kQ;
-    const bool loader = group == 1;
+    const bool loader = group == kGroups - 1;
     const int Kp = (K + 31) & ~31;
     const int MB = Kp / 32;
     const int mb0 = group * MBW;
@@ -388,19 +396,21 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float v = half_sum(sum[m][i]);
-            if (col == kHalfLead) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
+            if (col == kHalfLead) s_part[w][32 * m + acc_row(i, hh)] = v;
         }
     }
     if (lane == 0) s_M[w] = (jlast >= 0 && computes) ? Mw : -INFINITY;
     ring_barrier();
+    // row j belongs to group g = (j / 32) / MBW, at local row lj of its waves
     for (int j = tid; j < Kp; j += blockDim.x) {
         const int g = (j / 32) / MBW;
+        const int lj = j - 32 * MBW * g;
         float Mg = -INFINITY;
         for (int k2 = 0; k2 < kQ; ++k2) Mg = fmaxf(Mg, s_M[g * kQ + k2]);
         float total = 0.f;
         for (int k2 = 0; k2 < kQ; ++k2) {
             const float Mk = s_M[g * kQ + k2];
-            if (Mk != -INFINITY) total += s_part[g * kQ + k2][j] * exp2f(Mk - Mg);
+            if (Mk != -INFINITY) total += s_part[g * kQ + k2][lj] * exp2f(Mk - Mg);
         }
         const bool lv = s_live[j];
         const bool ok = total >= 0x1p-100f && total < INFINITY;
@@ -437,14 +447,15 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float v = half_max(sum[m][i]);
-                if (col == kHalfLead) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
+                if (col == kHalfLead) s_part[w][32 * m + acc_row(i, hh)] = v;
             }
         }
         __syncthreads();
         for (int j = tid; j < Kp; j += blockDim.x) {
             const int g = (j / 32) / MBW;
+            const int lj = j - 32 * MBW * g;
             float R = -INFINITY;
-            for (int k2 = 0; k2 < kQ; ++k2) R = fmaxf(R, s_part[g * kQ + k2][j]);
+            for (int k2 = 0; k2 < kQ; ++k2) R = fmaxf(R, s_part[g * kQ + k2][lj]);
             s_ref[j] = R * kCs;
         }
         __syncthreads();
@@ -471,14 +482,15 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const float v = half_sum(acc_sum[i]);
-                if (col == kHalfLead) s_part[w][32 * (mb0 + m) + acc_row(i, hh)] = v;
+                if (col == kHalfLead) s_part[w][32 * m + acc_row(i, hh)] = v;
             }
         }
         __syncthreads();
         for (int j = tid; j < Kp; j += blockDim.x) {
             const int g = (j / 32) / MBW;
+            const int lj = j - 32 * MBW * g;
             float total = 0.f;
-            for (int k2 = 0; k2 < kQ; ++k2) total += s_part[g * kQ + k2][j];
+            for (int k2 = 0; k2 < kQ; ++k2) total += s_part[g * kQ + k2][lj];
             s_lse2[j] = s_live[j] ? s_ref[j] + log2f(total) : INFINITY;
         }
         __syncthreads();
@@ -500,18 +512,19 @@ __global__ __launch_bounds__(kWaves * kWave) void beacon_score_kernel(
             Cf[m][i] = -l2 * kInvCs;
         }
     float* out = scores + (size_t)hc * stride;
-    // Group 1's partial maximum of tile j passes through s_pmax[j % 3]; group 0
-    // finishes tile j once that has crossed a barrier.
+    // The other groups' partial maxima of tile j pass through s_pmax[j % 3];
+    // group 0 finishes tile j once they have crossed a barrier.
     auto finalize = [&](int j, float mx) {
         const int n = kTileKeys * (kQ * j + q) + col;
         if (j <= jlast && hh == 0 && n >= P && n < N) {
-            mx = fmaxf(mx, s_pmax[j % 3][q][col]);
+#pragma unroll
+            for (int g = 0; g < kGroups - 1; ++g) mx = fmaxf(mx, s_pmax[j % 3][g][q][col]);
             const float sigma = __builtin_amdgcn_exp2f(mx * kCs);
             out[n - P] = sigma + ((n >= N - window) ? bonus : 0.f);
         }
     };
     auto publish = [&](int j, float mx) {
-        if (group == 1 && hh == 0) s_pmax[j % 3][q][col] = mx;
+        if (group > 0 && hh == 0) s_pmax[j % 3][group - 1][q][col] = mx;
     };
     float mx_prev = -INFINITY;
     for (int it = 0; it < iters; ++it) {
@@ -544,15 +557,12 @@ hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const i
                                float* lse, Check ck, int32_t* status, hipStream_t s) {
     const int HC = c.L * c.R * c.H;
     if (HC == 0) return hipSuccess;
-    // row blocks per wave: 1 for K <= 64, 2 for K <= 128, 4 for K <= 256
-    if (K <= 64) {
+    // row blocks per wave: 1 for K <= 128, 2 for K <= 256
+    if (K <= 4 * 32) {
         hipLaunchKernelGGL(beacon_score_kernel<1>, dim3(HC), dim3(kWaves * kWave), 0, s, c,
                            beacons, counts, K, window, bonus, scores, stride, lse, ck, status);
-    } else if (K <= 128) {
-        hipLaunchKernelGGL(beacon_score_kernel<2>, dim3(HC), dim3(kWaves * kWave), 0, s, c,
-                           beacons, counts, K, window, bonus, scores, stride, lse, ck, status);
     } else {
-        hipLaunchKernelGGL(beacon_score_kernel<4>, dim3(HC), dim3(kWaves * kWave), 0, s, c,
+        hipLaunchKernelGGL(beacon_score_kernel<2>, dim3(HC), dim3(kWaves * kWave), 0, s, c,
                            beacons, counts, K, window, bonus, scores, stride, lse, ck, status);
     }
     return hipGetLastError();
