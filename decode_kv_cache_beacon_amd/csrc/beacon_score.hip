@@ -8,26 +8,24 @@
 // The traversal of the paged keys is the extra pass a content-dependent
 // selector costs (Random Attention article, section "发现四").
 //
-// How (one 8-wave workgroup per head-cache, two workgroups per CU, gfx950):
+// How (one workgroup per head-cache, two workgroups per CU, gfx950):
 //   - The beacon.key logits are a [K x 128] x [128 x N] contraction: bf16 MFMA
 //     v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  Beacons are the A
 //     operand (rows, kept in registers for the whole head), 32 keys form the B
 //     operand (columns), so each lane owns one key column and 16 beacon rows of
-//     a 32x32 result.  The rows are split between four groups of two waves
-//     (32 rows per wave up to K = 128, 64 beyond); wave (group g, phase q)
-//     consumes key tiles q, q+2, q+4, ...
-//   - Key tiles (32 keys = 8 KiB) stream through an 8-tile LDS ring filled by
-//     direct-to-LDS DMA (global_load_lds_dwordx4): each load instruction moves
-//     1 KiB of whole key rows, the ring is refilled three iterations ahead, and
-//     each tile serves all four row groups.  A row's 16-byte chunks are
-//     XOR-swizzled by the row index so that the fragment reads are free of
-//     bank conflicts.  The two waves of the last group issue all the DMA, so
-//     their vmcnt counts ring loads only; one barrier per iteration hands the
-//     tiles over.  The load stream runs on from phase 1 into phase 2.
-//   - Two workgroups share a CU (64 KiB ring each, at most 128 registers per
-//     wave), so one head-cache's set-up (request checks, block table, beacon
-//     loads) overlaps the other's streaming, and the SIMDs interleave four
-//     waves' MFMA and exponential work.
+//     a 32x32 result.  The rows are split between NG groups of NQ waves (32 or
+//     64 rows per wave); wave (group g, phase q) consumes key tiles q, q+NQ,
+//     q+2NQ, ...  Each tile is read from LDS once per group.
+//   - Key tiles (32 keys = 8 KiB) stream through an LDS ring of 4 NQ tiles
+//     filled by direct-to-LDS DMA (global_load_lds_dwordx4): each load
+//     instruction moves 1 KiB of whole key rows, the ring is refilled three
+//     iterations ahead, and each tile serves all row groups.  A row's 16-byte
+//     chunks are XOR-swizzled by the row index so that the fragment reads are
+//     free of bank conflicts.  The waves of the last group issue all the DMA,
+//     so their vmcnt counts ring loads only; one barrier per iteration hands
+//     the tiles over.  The load stream runs on from phase 1 into phase 2.
+//   - Two workgroups share a CU, so one head-cache's set-up (request checks,
+//     block table, beacon loads) overlaps the other's streaming.
 //   - Phase 1 (log-sum-exp per beacon): per lane and row a running sum of
 //     exp2(acc * log2(e)/sqrt(d) - M) with one reference M per wave taken from
 //     the wave's first tile; lanes (DPP), then waves (LDS) are merged.  If any
@@ -53,14 +51,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kCs = 1.4426950408889634f * 0.08838834764831845f;  // log2(e) / sqrt(128)
 constexpr float kInvCs = 7.842065147748378f;  // sqrt(128) / log2(e)
-constexpr int kWaves = 8;
-constexpr int kGroups = 4;                         // row groups
-constexpr int kQ = kWaves / kGroups;               // tile phases = waves per row group
 constexpr int kTileKeys = 32;
 constexpr int kTileBytes = kTileKeys * kRowBytes;  // 8 KiB
 constexpr int kDepth = 3;                          // ring refilled this many iterations ahead
 constexpr int kRingIters = kDepth + 1;
-constexpr int kRingTiles = kQ * kRingIters;        // 8 tiles = 64 KiB
 constexpr int kDmaPerTile = kTileBytes / 1024;     // instructions of 64 lanes x 16 B
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -173,13 +167,15 @@ __device__ __forceinline__ float wave_max(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), kHalfLead));
 }
 
-// Two workgroups share a CU (16 waves) while a wave needs at most 128
-// registers, so one head-cache's set-up overlaps another's streaming.
-template <int MBW>
-__global__ __launch_bounds__(kWaves * kWave, MBW == 1 ? 4 : 2) void beacon_score_kernel(
+// NG row groups of NQ waves (NQ tile phases), MBW 32-row blocks per wave, and
+// a register budget for WPE waves per SIMD.
+template <int NG, int NQ, int MBW, int WPE>
+__global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
     CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
     int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
     Check ck, int32_t* status) {
+    constexpr int kGroups = NG, kQ = NQ, kWaves = NG * NQ;
+    constexpr int kRingTiles = kQ * kRingIters;
     __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kRingTiles * kTileBytes];
     __shared__ int s_bt[kMaxBlocksPerReq];
     __shared__ float s_part[kWaves][32 * MBW];  // per wave, its own rows
@@ -552,19 +548,34 @@ __global__ __launch_bounds__(kWaves * kWave, MBW == 1 ? 4 : 2) void beacon_score
 
 }  // namespace
 
+template <int NG, int NQ, int MBW, int WPE>
+void launch_cfg(const CacheView& c, const float* beacons, const int32_t* counts, int K,
+                int window, float bonus, float* scores, int stride, float* lse, Check ck,
+                int32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL((beacon_score_kernel<NG, NQ, MBW, WPE>), dim3(c.L * c.R * c.H),
+                       dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, window, bonus, scores,
+                       stride, lse, ck, status);
+}
+
 hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const int32_t* counts,
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, Check ck, int32_t* status, hipStream_t s) {
-    const int HC = c.L * c.R * c.H;
-    if (HC == 0) return hipSuccess;
-    // row blocks per wave: 1 for K <= 128, 2 for K <= 256
-    if (K <= 4 * 32) {
-        hipLaunchKernelGGL(beacon_score_kernel<1>, dim3(HC), dim3(kWaves * kWave), 0, s, c,
-                           beacons, counts, K, window, bonus, scores, stride, lse, ck, status);
-    } else {
-        hipLaunchKernelGGL(beacon_score_kernel<2>, dim3(HC), dim3(kWaves * kWave), 0, s, c,
-                           beacons, counts, K, window, bonus, scores, stride, lse, ck, status);
-    }
+    if (c.L * c.R * c.H == 0) return hipSuccess;
+    // Layouts measured at 2112 keys per head-cache (two workgroups per CU in
+    // each case):
+    //   K <= 64 : 2 groups x 2 phases, 32 rows per wave (4 waves per workgroup)
+    //   K <= 128: 2 groups x 2 phases, 64 rows per wave; every tile is read
+    //             from LDS by two waves (four 32-row waves took 5% longer)
+    //   K <= 256: 4 groups x 2 phases, 64 rows per wave
+    if (K <= 64)
+        launch_cfg<2, 2, 1, 2>(c, beacons, counts, K, window, bonus, scores, stride, lse, ck,
+                               status, s);
+    else if (K <= 128)
+        launch_cfg<2, 2, 2, 2>(c, beacons, counts, K, window, bonus, scores, stride, lse, ck,
+                               status, s);
+    else
+        launch_cfg<4, 2, 2, 2>(c, beacons, counts, K, window, bonus, scores, stride, lse, ck,
+                               status, s);
     return hipGetLastError();
 }
 
