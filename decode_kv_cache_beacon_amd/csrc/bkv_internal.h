@@ -92,6 +92,13 @@ typedef __attribute__((address_space(1))) const u32x4 global_cu32x4;
 typedef __attribute__((address_space(1))) u32x4 global_u32x4;
 __device__ __forceinline__ u32x4 load16(uint64_t addr) { return *(global_cu32x4*)addr; }
 __device__ __forceinline__ void store16(uint64_t addr, u32x4 v) { *(global_u32x4*)addr = v; }
+// Streaming (non-temporal) variants for data touched once.
+__device__ __forceinline__ u32x4 load16_nt(uint64_t addr) {
+    return __builtin_nontemporal_load((global_cu32x4*)addr);
+}
+__device__ __forceinline__ void store16_nt(uint64_t addr, u32x4 v) {
+    __builtin_nontemporal_store(v, (global_u32x4*)addr);
+}
 
 // Largest slot count of one request the kernels accept (block table staged in
 // LDS: 2048 blocks of 16 slots).

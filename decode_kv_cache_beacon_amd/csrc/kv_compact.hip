@@ -12,7 +12,8 @@
 // least) are never touched.
 //
 // Memory: a row is 256 contiguous bytes; 16 lanes move one row with 16-byte
-// accesses, so each wave instruction moves 4 whole rows (1 KiB).
+// accesses, so each wave instruction moves 4 whole rows (1 KiB).  The rows
+// are touched once, so loads and stores are non-temporal.
 
 #include "bkv_internal.h"
 
@@ -85,8 +86,8 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CacheView c,
         for (int u = 0; u < kRounds; ++u) {
             const int s = src[u];
             const uint64_t off = row_offset(s_bt[s >> 4], c.H, x.head, s & 15) + piece;
-            kr[u] = load16(kbase + off);
-            vr[u] = load16(vbase + off);
+            kr[u] = load16_nt(kbase + off);
+            vr[u] = load16_nt(vbase + off);
         }
 #pragma unroll
         for (int u = 0; u < kRounds; ++u) pr[u] = pos_lane ? pos[src[u]] : 0;
@@ -96,8 +97,8 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CacheView c,
             const int i = base + rsub + u * kRowsPerRound;
             if (i < nk) {
                 const uint64_t off = row_offset(s_bt[i >> 4], c.H, x.head, i & 15) + piece;
-                store16(kbase + off, kr[u]);
-                store16(vbase + off, vr[u]);
+                store16_nt(kbase + off, kr[u]);
+                store16_nt(vbase + off, vr[u]);
                 if (pos_lane) pos[i] = pr[u];
             }
         }
