@@ -222,10 +222,16 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
 
     const uint64_t kpool = c.k_pools[x.layer];
     const int ntiles = (N + kTileKeys - 1) / kTileKeys;
-    const int iters = (ntiles + kQ - 1) / kQ;  // iterations per phase
-    const int G = 2 * iters;                    // the stream: phase 1, then phase 2
+    const int iters = (ntiles + kQ - 1) / kQ;  // phase-1 iterations (all keys)
+    // Phase 2 scores only the candidates [P, N): its tiles start at the one
+    // holding slot P.
+    const int t2 = P / kTileKeys;
+    const int ntiles2 = ntiles - t2;
+    const int iters2 = (ntiles2 + kQ - 1) / kQ;
+    const int G = iters + iters2;               // the stream: phase 1, then phase 2
     // last iteration of a phase in which this wave's phase q has a tile (-1 if none)
     const int jlast = (q < ntiles) ? (ntiles - 1 - q) / kQ : -1;
+    const int jlast2 = (q < ntiles2) ? (ntiles2 - 1 - q) / kQ : -1;
 
     // DMA of key tile t into ring slot `slot` (issued by a group-1 wave).  Lane
     // l of instruction i fills LDS bytes [1024 i + 16 l, +16) of the slot: row
@@ -251,11 +257,12 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
             dma16((i < kDmaPerTile / 2 ? base_lo : base_hi) + off, dst + 1024 * i);
         }
     };
-    // Stream iteration g covers tile 4j + q of phase 1 (g < iters, j = g) or
-    // phase 2 (j = g - iters).  Every loader issues one tile per iteration, so
-    // a wave's outstanding loads are always whole iterations.
+    // Stream iteration g covers tile NQ j + q of phase 1 (g < iters, j = g)
+    // or tile t2 + NQ j + q of phase 2 (j = g - iters).  Every loader issues
+    // one tile per iteration, so a wave's outstanding loads are always whole
+    // iterations.
     auto slot_of = [&](int g) { return (g % kRingIters) * kQ + q; };
-    auto tile_of = [&](int g) { return kQ * (g < iters ? g : g - iters) + q; };
+    auto tile_of = [&](int g) { return g < iters ? kQ * g + q : t2 + kQ * (g - iters) + q; };
     // this lane's key column from a ring slot: the B fragment of k-step s is
     // global chunk 2s + hh of row `col`
     auto read_tile = [&](Tile& t, int slot) {
@@ -511,8 +518,8 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
     // The other groups' partial maxima of tile j pass through s_pmax[j % 3];
     // group 0 finishes tile j once they have crossed a barrier.
     auto finalize = [&](int j, float mx) {
-        const int n = kTileKeys * (kQ * j + q) + col;
-        if (j <= jlast && hh == 0 && n >= P && n < N) {
+        const int n = kTileKeys * (t2 + kQ * j + q) + col;
+        if (j <= jlast2 && hh == 0 && n >= P && n < N) {
 #pragma unroll
             for (int g = 0; g < kGroups - 1; ++g) mx = fmaxf(mx, s_pmax[j % 3][g][q][col]);
             const float sigma = __builtin_amdgcn_exp2f(mx * kCs);
@@ -523,11 +530,11 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
         if (group > 0 && hh == 0) s_pmax[j % 3][group - 1][q][col] = mx;
     };
     float mx_prev = -INFINITY;
-    for (int it = 0; it < iters; ++it) {
+    for (int it = 0; it < iters2; ++it) {
         begin_iter(iters + it);  // stream iteration g = iters + it
         if (group == 0 && it > 0) finalize(it - 1, mx_prev);
         float mx = -INFINITY;
-        if (it <= jlast && computes) {
+        if (it <= jlast2 && computes) {
             Tile t;
             read_tile(t, slot_of(iters + it));
 #pragma unroll
@@ -543,7 +550,7 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
         mx_prev = mx;
     }
     ring_barrier();
-    if (group == 0) finalize(iters - 1, mx_prev);
+    if (group == 0 && iters2 > 0) finalize(iters2 - 1, mx_prev);
 }
 
 }  // namespace

@@ -271,6 +271,15 @@ def test_beacon_score_parity(K):
     _score_case(wl, N=[1040, 577, 31], P=[200, 576, 0], kill=[(0, 0), (3, K - 1)])
 
 
+def test_beacon_score_prompt_boundaries():
+    """Phase 2 starts at the tile holding slot P: no candidates (P = N, with N
+    on and off a tile boundary), and P on a tile boundary."""
+    say("score prompt boundaries")
+    wl = small(n_layers=1, n_requests=4, n_kv_heads=2, n_beacons=128, budget=1024,
+               prompt_len=200, seq_len=640)
+    _score_case(wl, N=[640, 333, 128, 97], P=[640, 333, 96, 32])
+
+
 def test_beacon_score_no_live_beacons():
     say("score empty J")
     wl = small(n_layers=1, n_requests=1, n_kv_heads=2, n_beacons=64, prewarm=False,
