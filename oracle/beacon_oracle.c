@@ -108,14 +108,20 @@ static int nearest_beacon(const uint16_t* x, const float* beacons, int K, int d,
 
 /* Absorb observation x into beacon row j.  count 0 -> the row becomes x;
  * otherwise the running mean b += (x - b) / c with c the incremented count,
- * each operation an IEEE fp32 operation. */
-static void absorb(const uint16_t* x, float* b, int32_t* count, int d) {
+ * each operation an IEEE fp32 operation.  With a count cap C > 0 the
+ * incremented count is clamped to C, so once a row has absorbed C
+ * observations each new one moves it by 1/C of the difference: an
+ * exponential moving average that keeps the beacon evolving during decoding
+ * (BeaconKV explainer, section 3.2: beacons are not frozen, or early beacons
+ * would be useless for late queries).  C = 0: no cap. */
+static void absorb(const uint16_t* x, float* b, int32_t* count, int d, int cap) {
     if (*count == 0) {
         for (int i = 0; i < d; ++i) b[i] = (float)bf16_value(x[i]);
         *count = 1;
         return;
     }
     *count += 1;
+    if (cap > 0 && *count > cap) *count = cap;
     const float cf = (float)(*count);
     for (int i = 0; i < d; ++i) {
         float xi = (float)bf16_value(x[i]);
@@ -127,12 +133,12 @@ static void absorb(const uint16_t* x, float* b, int32_t* count, int d) {
 
 /* Process the T*G buffered decode queries q[T][G][d] in (t, g) order. */
 void oracle_beacon_update(int T, int G, int d, int K, const uint16_t* q,
-                          float* beacons, int32_t* counts, int32_t* assign) {
+                          float* beacons, int32_t* counts, int32_t* assign, int cap) {
     for (int s = 0; s < T * G; ++s) {
         const uint16_t* x = q + (size_t)s * d;
         int j = first_empty(counts, K);
         if (j < 0) j = nearest_beacon(x, beacons, K, d, NULL);
-        absorb(x, beacons + (size_t)j * d, counts + j, d);
+        absorb(x, beacons + (size_t)j * d, counts + j, d, cap);
         if (assign) assign[s] = j;
     }
 }
@@ -145,7 +151,7 @@ void oracle_beacon_update(int T, int G, int d, int K, const uint16_t* q,
  * replayed. */
 int oracle_beacon_update_forced(int T, int G, int d, int K, const uint16_t* q,
                                 float* beacons, int32_t* counts,
-                                const int32_t* forced, double* gap) {
+                                const int32_t* forced, double* gap, int cap) {
     for (int s = 0; s < T * G; ++s) {
         const uint16_t* x = q + (size_t)s * d;
         int f = forced[s];
@@ -162,7 +168,7 @@ int oracle_beacon_update_forced(int T, int G, int d, int K, const uint16_t* q,
             double cf = cosine(x, beacons + (size_t)f * d, d);
             gap[s] = best - cf;
         }
-        absorb(x, beacons + (size_t)f * d, counts + f, d);
+        absorb(x, beacons + (size_t)f * d, counts + f, d, cap);
     }
     return T * G;
 }
@@ -362,7 +368,7 @@ int oracle_evict_batch(int H, int T, int G, int d, int K, int B, int W,
         const int n = N[h], p = P[h];
         float* bh = beacons + (size_t)h * K * d;
         int32_t* ch = counts + (size_t)h * K;
-        oracle_beacon_update(T, G, d, K, q + (size_t)h * T * G * d, bh, ch, NULL);
+        oracle_beacon_update(T, G, d, K, q + (size_t)h * T * G * d, bh, ch, NULL, 0);
         double* sc = (double*)malloc(sizeof(double) * (size_t)(n - p > 0 ? n - p : 1));
         oracle_beacon_score(n, p, d, K, keys + (size_t)h * Nmax * d, bh, ch, W,
                             bonus, sc, NULL);

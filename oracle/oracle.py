@@ -57,9 +57,9 @@ def lib():
         i32, i64, u64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
         L.oracle_bf16_round.argtypes = [ctypes.c_float]
         L.oracle_bf16_round.restype = ctypes.c_uint16
-        L.oracle_beacon_update.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        L.oracle_beacon_update.argtypes = [i32, i32, i32, i32, P, P, P, P, i32]
         L.oracle_beacon_update.restype = None
-        L.oracle_beacon_update_forced.argtypes = [i32, i32, i32, i32, P, P, P, P, P]
+        L.oracle_beacon_update_forced.argtypes = [i32, i32, i32, i32, P, P, P, P, P, i32]
         L.oracle_beacon_update_forced.restype = i32
         L.oracle_beacon_score.argtypes = [i32, i32, i32, i32, P, P, P, i32, f64, P, P]
         L.oracle_beacon_score.restype = None
@@ -96,9 +96,11 @@ def bf16_round(x: float) -> int:
 
 
 # ---------------------------------------------------------------- maintenance
-def beacon_update(q_bits, beacons, counts):
+def beacon_update(q_bits, beacons, counts, cap=0):
     """Absorb queries q[T][G][d] (bf16 bits) in (t, g) order.
 
+    cap > 0 clamps every incremented count to cap (exponential moving average
+    once a row is full); 0 is the plain running mean.
     Returns (beacons', counts', assign[T*G]); inputs are not modified.
     """
     q = _c(q_bits, np.uint16)
@@ -108,11 +110,11 @@ def beacon_update(q_bits, beacons, counts):
     K = b.shape[0]
     assert b.shape == (K, d) and c.shape == (K,)
     a = np.zeros(T * G, np.int32)
-    lib().oracle_beacon_update(T, G, d, K, _ptr(q), _ptr(b), _ptr(c), _ptr(a))
+    lib().oracle_beacon_update(T, G, d, K, _ptr(q), _ptr(b), _ptr(c), _ptr(a), int(cap))
     return b, c, a
 
 
-def beacon_update_forced(q_bits, beacons, counts, forced):
+def beacon_update_forced(q_bits, beacons, counts, forced, cap=0):
     """Replay a given assignment sequence; returns (beacons', counts', gap).
 
     gap[s] = best cosine - cosine of the forced row (0 for an exact argmax,
@@ -126,7 +128,8 @@ def beacon_update_forced(q_bits, beacons, counts, forced):
     f = _c(forced, np.int32).reshape(-1)
     assert f.shape == (T * G,)
     gap = np.zeros(T * G, np.float64)
-    lib().oracle_beacon_update_forced(T, G, d, K, _ptr(q), _ptr(b), _ptr(c), _ptr(f), _ptr(gap))
+    lib().oracle_beacon_update_forced(T, G, d, K, _ptr(q), _ptr(b), _ptr(c), _ptr(f), _ptr(gap),
+                                      int(cap))
     return b, c, gap
 
 

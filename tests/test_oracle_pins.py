@@ -152,6 +152,63 @@ def test_running_mean_tracks_exact_mean():
         assert np.max(np.abs(b[j] - mean)) <= tol, (j, np.max(np.abs(b[j] - mean)), tol)
 
 
+# ---------------------------------------------- capped count (beacon forgetting)
+def test_cap_at_least_the_counts_reached_is_the_plain_mean():
+    T, G, d, K = 16, 4, 32, 6
+    q = bf16_bits(RNG.standard_normal((T, G, d)))
+    b0 = RNG.standard_normal((K, d)).astype(np.float32)
+    c0 = np.array([0, 3, 1, 7, 0, 2], np.int32)
+    b, c, a = oracle.beacon_update(q, b0, c0)
+    bc, cc, ac = oracle.beacon_update(q, b0, c0, cap=int(c0.max()) + T * G)
+    assert np.array_equal(a, ac) and np.array_equal(c, cc)
+    assert np.array_equal(b.view(np.int32), bc.view(np.int32))
+
+
+def test_cap_hand_computed_values():
+    # count 5 above a cap of 2: the next observation uses c = 2, the count
+    # becomes 2: b = 1 + (4 - 1)/2 = 2.5; the next: b = 2.5 + (0 - 2.5)/2 = 1.25
+    q = bf16_bits(np.array([[[4.0, 1.0]], [[0.0, 1.0]]]))
+    b, c, _ = oracle.beacon_update(q, np.array([[1.0, 1.0]], np.float32),
+                                   np.array([5], np.int32), cap=2)
+    assert c[0] == 2 and b[0, 0] == 1.25 and b[0, 1] == 1.0
+    # an empty row is still filled exactly, whatever the cap
+    b, c, _ = oracle.beacon_update(q[:1], np.array([[9.0, 9.0]], np.float32),
+                                   np.array([0], np.int32), cap=1)
+    assert c[0] == 1 and b[0, 0] == 4.0 and b[0, 1] == 1.0
+    # cap 1 on a filled row: b + (x - b) / 1, one IEEE operation each
+    b, c, _ = oracle.beacon_update(q[:1], np.array([[0.3, 0.7]], np.float32),
+                                   np.array([4], np.int32), cap=1)
+    f = np.float32
+    assert c[0] == 1
+    assert b[0, 0] == f(f(0.3) + f(f(4.0) - f(0.3))) and b[0, 1] == f(f(0.7) + f(f(1.0) - f(0.7)))
+
+
+def test_capped_row_decays_geometrically_toward_a_repeated_query():
+    # a full row (count == cap C) fed m copies of x: b_m - x = (1 - 1/C)^m (b_0 - x)
+    d, C, m = 16, 4, 30
+    x = bf16_bits(RNG.standard_normal(d))
+    b0 = RNG.standard_normal((1, d)).astype(np.float32)
+    q = np.tile(x, (m, 1, 1))
+    b, c, a = oracle.beacon_update(q, b0, np.array([C], np.int32), cap=C)
+    assert c[0] == C and (a == 0).all()
+    xv = bf16_values(x).astype(np.float64)
+    want = xv + (1 - 1 / C) ** m * (b0[0].astype(np.float64) - xv)
+    scale = max(np.abs(xv).max(), np.abs(b0).max())
+    assert np.max(np.abs(b[0] - want)) <= 4 * m * 2**-24 * scale
+
+
+def test_counts_never_exceed_the_cap():
+    T, G, d, K, C = 32, 4, 16, 5, 6
+    q = bf16_bits(RNG.standard_normal((T, G, d)))
+    b0 = RNG.standard_normal((K, d)).astype(np.float32)
+    c0 = np.array([0, 2, 9, 6, 1], np.int32)
+    _, c, a = oracle.beacon_update(q, b0, c0, cap=C)
+    for j in range(K):
+        hits = int((a == j).sum())
+        want = c0[j] if hits == 0 else min(c0[j] + hits, C) if c0[j] < C else C
+        assert c[j] == want, (j, c[j], want)
+
+
 def test_assignment_is_exact_argmax_on_tiny_inputs():
     for trial in range(6):
         T, G, d, K = 6, 2, 6, 5
