@@ -261,6 +261,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-random", action="store_true", help="skip the random-selector A/B")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--count-cap", type=int, default=16,
+                    help="also time the maintenance kernel with this count cap (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 4 GiB device copy (for counter calibration)")
     ap.add_argument("--summarize-profiles", nargs=2, metavar=("PROF_DIR", "PMC_DIR"),
@@ -452,6 +454,30 @@ def main():
             "moved_rows_per_pass": int(rM),
             "gbps": round(rbytes / (rpass * 1e-3) / 1e9, 1),
             "hbm_frac": round(rbytes / (rpass * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    # beacon forgetting: the maintenance kernel with a count cap (moving
+    # average once a row is full), timed alone on the same queries and state
+    if args.count_cap > 0:
+        times = {}
+        for cap in (0, args.count_cap):
+            bb, cc = b.clone(), c.clone()
+            bk.bkv_beacon_update(q, bb, cc, count_cap=cap)           # warm-up
+            evs2 = []
+            for _ in range(5):
+                bb.copy_(b)
+                cc.copy_(c)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                bk.bkv_beacon_update(q, bb, cc, count_cap=cap)
+                e1.record()
+                evs2.append((e0, e1))
+            torch.cuda.synchronize()
+            times[cap] = round(sum(x.elapsed_time(y) for x, y in evs2) / len(evs2), 4)
+            del bb, cc
+        result["beacon_forgetting"] = {
+            "count_cap": args.count_cap, "update_ms": times[args.count_cap],
+            "update_ms_uncapped": times[0],
+            "note": "maintenance kernel alone, same queries and starting state, mean of 5"}
 
     # reference: a plain device-to-device copy of 4 GiB (read + write), timed the same way
     src = torch.empty(1 << 31, dtype=torch.int16, device=dev)

@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
-BKV_ABI_VERSION = 1
+BKV_ABI_VERSION = 2
 BKV_OK, BKV_ERR_NULL, BKV_ERR_INVALID, BKV_ERR_BUDGET, BKV_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BKV_ERR_WORKSPACE, BKV_ERR_HIP, BKV_ERR_LENGTH, BKV_ERR_BLOCK_TABLE = 5, 6, 7, 8
 BKV_SCORE_F32, BKV_SCORE_U32 = 0, 1
@@ -51,7 +51,8 @@ class bkv_pass_args(ctypes.Structure):
     _fields_ = [
         ("selector", _i32), ("budget", _i32), ("score_stride", _i32),
         ("n_beacons", _i32), ("T", _i32), ("G", _i32), ("window", _i32), ("bonus", _f32),
-        ("queries", _P), ("beacons", _P), ("counts", _P), ("assign", _P), ("lse", _P),
+        ("queries", _P), ("beacons", _P), ("counts", _P), ("assign", _P), ("count_cap", _i32),
+        ("lse", _P),
         ("seed", _u64), ("request_ids", _P), ("pass_idx", _P),
         ("pos_ids", _P), ("pos_stride", _i32), ("scores_out", _P), ("keep_out", _P),
         ("timing_events", _P), ("n_timing_events", _i32),
@@ -62,7 +63,7 @@ _lib.bkv_abi_version.argtypes = []
 _lib.bkv_abi_version.restype = _i32
 _lib.bkv_status_string.argtypes = [_i32]
 _lib.bkv_status_string.restype = ctypes.c_char_p
-_lib.bkv_beacon_update.argtypes = [_i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _P]
+_lib.bkv_beacon_update.argtypes = [_i32, _i32, _i32, _i32, _i32, _P, _P, _P, _P, _i32, _P]
 _lib.bkv_beacon_update.restype = _i32
 _lib.bkv_beacon_score.argtypes = [ctypes.POINTER(bkv_cache), _P, _P, _i32, _i32, _f32, _P, _i32,
                                   _P, _P, _P]
@@ -220,8 +221,9 @@ class PagedCache:
 
 
 # ---------------------------------------------------------------- entry points
-def bkv_beacon_update(queries, beacons, counts, assign=None, stream=None):
-    """queries bf16 [HC,T,G,128]; beacons fp32 [HC,K,128]; counts int32 [HC,K] (in place)."""
+def bkv_beacon_update(queries, beacons, counts, assign=None, count_cap=0, stream=None):
+    """queries bf16 [HC,T,G,128]; beacons fp32 [HC,K,128]; counts int32 [HC,K] (in place);
+    count_cap > 0 clamps the counts (moving average once a row is full)."""
     _need(queries, "queries", torch.bfloat16)
     if queries.dim() != 4 or queries.shape[3] != HEAD_DIM:
         raise ValueError("queries must be [HC, T, G, 128]")
@@ -234,7 +236,7 @@ def bkv_beacon_update(queries, beacons, counts, assign=None, stream=None):
     if assign is not None:
         _need(assign, "assign", torch.int32, (HC, T * G))
     code = _lib.bkv_beacon_update(HC, T, G, HEAD_DIM, K, _ptr(queries), _ptr(beacons),
-                                  _ptr(counts), _ptr(assign), _stream(stream))
+                                  _ptr(counts), _ptr(assign), int(count_cap), _stream(stream))
     _check(code, "bkv_beacon_update")
 
 
@@ -330,7 +332,7 @@ def bkv_kv_compact(cache: PagedCache, keep, budget, pos_ids=None, status=None, c
 
 def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, window, bonus,
                assign, lse, seed, request_ids, pass_idx, pos_ids, scores_out, keep_out,
-               score_stride):
+               score_stride, count_cap=0):
     HC, R = cache.n_head_caches, cache.n_requests
     a = bkv_pass_args()
     a.selector = selector
@@ -345,6 +347,7 @@ def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, wi
         _need(counts, "counts", torch.int32, (HC, K))
         a.n_beacons, a.T, a.G = K, queries.shape[1], queries.shape[2]
         a.window, a.bonus = int(window), float(bonus)
+        a.count_cap = int(count_cap)
         a.queries, a.beacons, a.counts = queries.data_ptr(), beacons.data_ptr(), counts.data_ptr()
         if assign is not None:
             _need(assign, "assign", torch.int32, (HC, a.T * a.G))
@@ -385,14 +388,15 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
                    counts=None, window=64, bonus=1.0, assign=None, lse=None, seed=0,
                    request_ids=None, pass_idx=None, pos_ids=None, scores_out=None,
                    keep_out=None, score_stride=0, workspace=None, status=None, check=True,
-                   stream=None, timing_events=None):
+                   stream=None, timing_events=None, count_cap=0):
     """One whole eviction pass (beacon: update -> score -> select -> compact;
     random: score -> select -> compact), every layer/request/head at once.
 
     timing_events: optional list of torch.cuda.Event(enable_timing=True), 5 for
     the beacon selector and 4 for the random one, recorded around each kernel."""
     a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
-                   seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride)
+                   seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride,
+                   count_cap)
     ev_arr = None
     if timing_events is not None:
         handles = []

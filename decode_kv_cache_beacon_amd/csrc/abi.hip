@@ -97,9 +97,10 @@ const char* bkv_status_string(int32_t code) {
 
 int32_t bkv_beacon_update(int32_t n_head_caches, int32_t T, int32_t G, int32_t head_dim, int32_t K,
                           const uint16_t* queries, float* beacons, int32_t* counts,
-                          int32_t* assign, bkv_stream_t stream) {
+                          int32_t* assign, int32_t count_cap, bkv_stream_t stream) {
     if (head_dim != kHeadDim) return BKV_ERR_UNSUPPORTED;
-    if (n_head_caches < 0 || T < 1 || G < 1 || K < 1 || K > BKV_MAX_BEACONS) return BKV_ERR_INVALID;
+    if (n_head_caches < 0 || T < 1 || G < 1 || K < 1 || K > BKV_MAX_BEACONS || count_cap < 0)
+        return BKV_ERR_INVALID;
     if ((int64_t)T * G > INT_MAX / kHeadDim) return BKV_ERR_INVALID;
     if (n_head_caches == 0) return BKV_OK;
     if (!queries || !beacons || !counts) return BKV_ERR_NULL;
@@ -107,7 +108,7 @@ int32_t bkv_beacon_update(int32_t n_head_caches, int32_t T, int32_t G, int32_t h
         (assign && !aligned(assign, 4)))
         return BKV_ERR_INVALID;
     return hip_status(launch_beacon_update(n_head_caches, T, G, K, queries, beacons, counts, assign,
-                                           nullptr, Check{-1, -1, 0}, nullptr,
+                                           count_cap, nullptr, Check{-1, -1, 0}, nullptr,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -210,6 +211,7 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
     if (beacon) {
         if (!a->queries || !a->beacons || !a->counts) return BKV_ERR_NULL;
         if (a->n_beacons < 1 || a->n_beacons > BKV_MAX_BEACONS || a->T < 1 || a->G < 1 ||
+            a->count_cap < 0 ||
             a->window < 0 || (int64_t)a->T * a->G > INT_MAX / kHeadDim)
             return BKV_ERR_INVALID;
         if (!aligned(a->queries, 16) || !aligned(a->beacons, 16) || !aligned(a->counts, 4) ||
@@ -241,7 +243,7 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
     if (he != hipSuccess) return BKV_ERR_HIP;
     if (beacon) {
         he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
-                                  a->assign, &v, all, status, s);
+                                  a->assign, a->count_cap, &v, all, status, s);
         if (he == hipSuccess) he = mark();
         if (he == hipSuccess)
             he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,

@@ -118,7 +118,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // Host-side launchers (defined next to each kernel).  `cache` of the update
 // launcher is NULL for the standalone entry point (no request checks).
 hipError_t launch_beacon_update(int HC, int T, int G, int K, const uint16_t* q, float* beacons,
-                                int32_t* counts, int32_t* assign, const CacheView* cache,
+                                int32_t* counts, int32_t* assign, int cap, const CacheView* cache,
                                 Check ck, int32_t* status, hipStream_t s);
 hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const int32_t* counts,
                                int K, int window, float bonus, float* scores, int stride,

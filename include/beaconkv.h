@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 1
+#define BKV_ABI_VERSION 2
 
 typedef void* bkv_stream_t; /* hipStream_t */
 
@@ -117,14 +117,18 @@ const char* bkv_status_string(int32_t code);
  *     zero norm on either side counts as cosine 0), then counts[j] += 1 and
  *     b_j = b_j + (x - b_j) / counts[j], with IEEE fp32 subtract, divide and
  *     add (no fused multiply-add; bit-exact).
+ * count_cap > 0 clamps every incremented count to count_cap (a full row then
+ * moves by 1/count_cap of each new query's difference, an exponential moving
+ * average that keeps beacons evolving during decoding; explainer section
+ * 3.2); 0 keeps the plain running mean.  A fill still sets count 1.
  * beacons fp32 [HC][K][128] and counts int32 [HC][K] are updated in place;
  * assign (nullable) int32 [HC][T*G] receives every chosen row.  Cosines are
  * evaluated in fp32, so on a near tie the chosen row is the best to within
- * fp32 rounding of the cosines.  1 <= K <= 256, T*G >= 1.  queries and
- * beacons must be 16-byte aligned. */
+ * fp32 rounding of the cosines.  1 <= K <= 256, T*G >= 1, count_cap >= 0.
+ * queries and beacons must be 16-byte aligned. */
 int32_t bkv_beacon_update(int32_t n_head_caches, int32_t T, int32_t G, int32_t head_dim,
                           int32_t K, const uint16_t* queries, float* beacons, int32_t* counts,
-                          int32_t* assign, bkv_stream_t stream);
+                          int32_t* assign, int32_t count_cap, bkv_stream_t stream);
 
 /* a2/a3 -- Beacon scoring of every cached key (the traversal of the paged KV
  * state that content-dependent selectors need; Random Attention article,
@@ -199,6 +203,7 @@ typedef struct bkv_pass_args {
     float* beacons;            /* fp32 [HC][K][128], updated */
     int32_t* counts;           /* int32 [HC][K], updated */
     int32_t* assign;           /* nullable int32 [HC][T*G] */
+    int32_t count_cap;         /* 0: running mean; > 0: counts clamp there */
     float* lse;                /* nullable fp32 [HC][K] */
     /* random selector */
     uint64_t seed;

@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 1
+    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 2
     for code in range(0, 9):
         s = bk.bkv_status_string(code)
         assert s and s != "unknown status code"
@@ -52,14 +52,15 @@ def _score(cache, K=64, stride=160, beacons=FAKE, counts=FAKE, scores=FAKE, wind
 
 def test_beacon_update_validation():
     f = bk._lib.bkv_beacon_update
-    assert f(4, 8, 2, 64, 16, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_UNSUPPORTED
-    assert f(4, 8, 2, 128, 0, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID
-    assert f(4, 8, 2, 128, 257, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID
-    assert f(4, 0, 2, 128, 16, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID
-    assert f(-1, 8, 2, 128, 16, FAKE, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID
-    assert f(4, 8, 2, 128, 16, None, FAKE, FAKE, None, None) == bk.BKV_ERR_NULL
-    assert f(4, 8, 2, 128, 16, FAKE + 4, FAKE, FAKE, None, None) == bk.BKV_ERR_INVALID  # misaligned
-    assert f(0, 8, 2, 128, 16, None, None, None, None, None) == bk.BKV_OK              # nothing to do
+    assert f(4, 8, 2, 64, 16, FAKE, FAKE, FAKE, None, 0, None) == bk.BKV_ERR_UNSUPPORTED
+    assert f(4, 8, 2, 128, 0, FAKE, FAKE, FAKE, None, 0, None) == bk.BKV_ERR_INVALID
+    assert f(4, 8, 2, 128, 257, FAKE, FAKE, FAKE, None, 0, None) == bk.BKV_ERR_INVALID
+    assert f(4, 0, 2, 128, 16, FAKE, FAKE, FAKE, None, 0, None) == bk.BKV_ERR_INVALID
+    assert f(-1, 8, 2, 128, 16, FAKE, FAKE, FAKE, None, 0, None) == bk.BKV_ERR_INVALID
+    assert f(4, 8, 2, 128, 16, FAKE, FAKE, FAKE, None, -1, None) == bk.BKV_ERR_INVALID  # cap < 0
+    assert f(4, 8, 2, 128, 16, None, FAKE, FAKE, None, 0, None) == bk.BKV_ERR_NULL
+    assert f(4, 8, 2, 128, 16, FAKE + 4, FAKE, FAKE, None, 0, None) == bk.BKV_ERR_INVALID  # misaligned
+    assert f(0, 8, 2, 128, 16, None, None, None, None, 0, None) == bk.BKV_OK   # nothing to do
 
 
 def test_cache_validation():

@@ -204,11 +204,13 @@ def test_select_one_shot_32k_candidates():
 
 
 # ------------------------------------------------------------------ maintenance
-@pytest.mark.parametrize("K,prewarm,G,T", [(5, False, 4, 16), (64, True, 4, 64),
-                                           (128, True, 4, 64), (256, True, 8, 64),
-                                           (64, False, 1, 256), (40, True, 2, 33)])
-def test_beacon_update_teacher_forced(K, prewarm, G, T):
-    say("update", K, prewarm, G, T)
+@pytest.mark.parametrize("K,prewarm,G,T,cap", [
+    (5, False, 4, 16, 0), (64, True, 4, 64, 0), (128, True, 4, 64, 0), (256, True, 8, 64, 0),
+    (64, False, 1, 256, 0), (40, True, 2, 33, 0),
+    # capped counts (moving average once a row is full)
+    (128, True, 4, 64, 16), (64, True, 4, 64, 8), (5, False, 4, 16, 1), (40, True, 2, 33, 3)])
+def test_beacon_update_teacher_forced(K, prewarm, G, T, cap):
+    say("update", K, prewarm, G, T, "cap", cap)
     wl = small(n_layers=1, n_requests=2, n_kv_heads=2, n_beacons=K, group=G, steps=T,
                prewarm=prewarm, budget=512, prompt_len=200, seq_len=576)
     batch = synth.make_batch(wl)
@@ -217,14 +219,14 @@ def test_beacon_update_teacher_forced(K, prewarm, G, T):
     c = batch.counts.cuda()
     HC = q.shape[0]
     assign = torch.full((HC, T * G), -1, dtype=torch.int32).cuda()
-    bk.bkv_beacon_update(q, b, c, assign)
+    bk.bkv_beacon_update(q, b, c, assign, count_cap=cap)
     torch.cuda.synchronize()
     qb = synth.bits(batch.queries)
     bg, cg, ag = b.cpu().numpy(), c.cpu().numpy(), assign.cpu().numpy()
     inexact, worst = 0, 0.0
     for hc in range(HC):
         ob, oc, gap = oracle.beacon_update_forced(qb[hc], batch.beacons[hc].numpy(),
-                                                  batch.counts[hc].numpy(), ag[hc])
+                                                  batch.counts[hc].numpy(), ag[hc], cap=cap)
         assert np.all(np.isfinite(gap)) and gap.max() <= ASSIGN_TOL, (hc, gap.max())
         inexact += int((gap > 0).sum())
         worst = max(worst, float(gap.max()))
