@@ -18,7 +18,8 @@
  *    section "Random Attention: 不判断重要性, 只随机保留": prompt KV is always
  *    kept; generated KV is sampled independently per head and the top-K kept;
  *    one random draw plus one top-K per eviction.  Section "发现四" for the
- *    shared cache-compaction step.
+ *    shared cache-compaction step; section "发现二" for the variant in which
+ *    every head uses one common set of positions.
  *  - Where the pages leave a rule open, the readings fixed for this build are
  *    applied (softmax-max beacon score with a recent-window bonus, online
  *    k-means running-mean update, cosine nearest beacon, Philox4x64-10).
@@ -325,6 +326,28 @@ int oracle_topk_select(int N, int P, int B, const double* scores, int32_t* keep)
     free(c);
     free(kept);
     return o;
+}
+
+/* Shared positions (Random Attention article, section "发现二": forcing all
+ * heads onto one common set of positions leaves accuracy almost unchanged).
+ * One selection serves the H KV heads of one (layer, request).  Reading taken
+ * here: a candidate's merged score is the largest of its H per-head scores,
+ * and the prompt-protected top-B above runs once on the merged scores.  For
+ * the random selector the heads share one draw (H = 1 here, the draw of head
+ * 0).  scores is [H][N - P] row-major; keep as for oracle_topk_select. */
+int oracle_shared_select(int H, int N, int P, int B, const double* scores, int32_t* keep) {
+    if (H < 1 || P < 0 || N < P) return -1;
+    const int m = N - P;
+    double* merged = (double*)malloc(sizeof(double) * (size_t)(m > 0 ? m : 1));
+    for (int i = 0; i < m; ++i) {
+        double best = scores[i];
+        for (int h = 1; h < H; ++h)
+            if (scores[(size_t)h * m + i] > best) best = scores[(size_t)h * m + i];
+        merged[i] = best;
+    }
+    int n = oracle_topk_select(N, P, B, merged, keep);
+    free(merged);
+    return n;
 }
 
 /* ------------------------------------------------------------------ */

@@ -10,8 +10,9 @@ the paged cache layout with its own numpy indexing.
 Pages followed: the BeaconKV explainer (papers.ananclaw.com), section 3.2, for
 nearest-beacon assignment and incremental beacon update; the Random Attention
 article (aiinking.com), section "Random Attention: 不判断重要性, 只随机保留",
-for prompt protection and per-head top-K of random scores, and section "发现四"
-for the shared compaction step.  Rules the pages leave open follow the readings
+for prompt protection and per-head top-K of random scores, section "发现四"
+for the shared compaction step, and section "发现二" for one common set of
+positions shared by all heads.  Rules the pages leave open follow the readings
 fixed for this build (listed in the design notes of the repository).
 """
 from __future__ import annotations
@@ -69,6 +70,8 @@ def lib():
         L.oracle_random_score.restype = None
         L.oracle_topk_select.argtypes = [i32, i32, i32, P, P]
         L.oracle_topk_select.restype = i32
+        L.oracle_shared_select.argtypes = [i32, i32, i32, i32, P, P]
+        L.oracle_shared_select.restype = i32
         L.oracle_kv_compact.argtypes = [i32, P, i64, P, P]
         L.oracle_kv_compact.restype = None
         L.oracle_num_threads.argtypes = []
@@ -171,6 +174,27 @@ def topk_select(scores, N, P, B):
     assert s.shape == (N - P,)
     keep = np.zeros(max(min(N, B), 1), np.int32)
     n = lib().oracle_topk_select(int(N), int(P), int(B), _ptr(s) if s.size else None, _ptr(keep))
+    if n < 0:
+        raise ValueError(f"selection refused: P={P} exceeds budget B={B} or bad lengths")
+    return keep[:n]
+
+
+def shared_select(scores, N, P, B):
+    """One selection for all heads of a (layer, request).
+
+    scores[H][N-P]: per-head candidate scores (H = 1 for one shared random
+    draw).  The merged score of a candidate is its largest per-head score; the
+    prompt-protected top-B then runs once on the merged scores.
+    """
+    s = np.asarray(scores).astype(np.float64)
+    if s.ndim == 1:
+        s = s[None, :]
+    s = _c(s, np.float64)
+    H = s.shape[0]
+    assert s.shape == (H, N - P)
+    keep = np.zeros(max(min(N, B), 1), np.int32)
+    n = lib().oracle_shared_select(H, int(N), int(P), int(B), _ptr(s) if s.size else None,
+                                   _ptr(keep))
     if n < 0:
         raise ValueError(f"selection refused: P={P} exceeds budget B={B} or bad lengths")
     return keep[:n]

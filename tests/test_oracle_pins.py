@@ -399,6 +399,44 @@ def test_topk_on_uint32_draws_is_exact():
     assert list(keep) == [0, 1, 3, 4, 6]
 
 
+# --------------------------------------------------------------- shared positions
+def test_shared_select_hand_computed_merge():
+    # Two heads disagree on slots 1 and 2 and agree on a middling slot 3.  The
+    # largest per-head score keeps 1 and 2; a mean would keep 3 and 1, a
+    # minimum 3 and 4, and reading the [H][m] rows transposed keeps 1 and 3.
+    s = np.array([[0.9, 0.1, 0.6, 0.2],
+                  [0.1, 0.9, 0.6, 0.3]])
+    assert list(oracle.shared_select(s, 5, 1, 3)) == [0, 1, 2]
+    # three heads, uint32 draws: merged = [7, 9, 4, 9, 2] -> keep slots 2+1, 2+3 and 2+0
+    u = np.array([[7, 1, 4, 0, 2], [0, 9, 0, 0, 0], [3, 0, 0, 9, 1]], np.uint32)
+    assert list(oracle.shared_select(u, 7, 2, 5)) == [0, 1, 2, 3, 5]
+
+
+def test_shared_select_matches_exhaustive_dominance_on_merged_scores():
+    for trial in range(30):
+        H = int(RNG.integers(1, 5))
+        P = int(RNG.integers(0, 4))
+        m = int(RNG.integers(1, 10))
+        B = P + int(RNG.integers(0, m))
+        N = P + m
+        s = RNG.integers(0, 4, (H, m)).astype(np.float64) if trial % 2 else RNG.random((H, m))
+        merged = [max(s[h][i] for h in range(H)) for i in range(m)]
+        found = brute.topk_by_dominance(merged, P, B)
+        assert len(found) == 1
+        assert list(oracle.shared_select(s, N, P, B)) == list(range(P)) + found[0], trial
+
+
+def test_shared_select_reduces_to_per_head_selection():
+    N, P, B = 2112, 1024, 2048
+    s = RNG.random(N - P)
+    per_head = oracle.topk_select(s, N, P, B)
+    assert np.array_equal(oracle.shared_select(s[None], N, P, B), per_head)      # one head
+    assert np.array_equal(oracle.shared_select(np.stack([s] * 8), N, P, B), per_head)  # equal heads
+    assert list(oracle.shared_select(np.ones((3, 5)), 8, 3, 10)) == list(range(8))   # N <= B
+    with pytest.raises(ValueError):
+        oracle.shared_select(np.ones((3, 5)), 8, 3, 2)                             # P > B
+
+
 # --------------------------------------------------------------- compaction
 def test_compaction_is_numpy_gather():
     rows = RNG.integers(0, 2**16, (300, 128), dtype=np.uint16)
