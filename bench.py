@@ -157,9 +157,11 @@ KERNEL_SYMBOLS = {
 COPY_SYMBOL = "__amd_rocclr_copyBuffer"
 PROFILE_CMDS = {
     "trace": ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -f csv -d <prof-dir> "
-              "-o bench -- python3 <repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline"),
+              "-o bench -- python3 <repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline "
+              "--no-shared --count-cap 0"),
     "pmc": ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} -f csv -d <pmc-dir>/{c} -o {c} -- "
-            "python3 <repo>/bench.py --steps 2 --warmup 0 --no-random --no-cpu-baseline"),
+            "python3 <repo>/bench.py --steps 2 --warmup 0 --no-random --no-cpu-baseline "
+            "--no-shared --count-cap 0"),
     "summary": "python bench.py --summarize-profiles <prof-dir> <pmc-dir>",
 }
 
@@ -260,6 +262,8 @@ def main():
     ap.add_argument("--workload", default="serving_r128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-random", action="store_true", help="skip the random-selector A/B")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the shared-position (one selection per layer and request) passes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--count-cap", type=int, default=16,
                     help="also time the maintenance kernel with this count cap (0: skip)")
@@ -322,12 +326,14 @@ def main():
 
     ar = torch.arange(B, device=dev, dtype=torch.int32)
 
-    def moved_rows():
-        neq = keep != ar
+    def moved_rows(kp=None, heads=1):
+        """Rows the compaction moved: from the first changed slot on, per keep row."""
+        kp = keep if kp is None else kp
+        neq = kp != ar
         first = torch.where(neq.any(1), neq.int().argmax(1), torch.full_like(neq[:, 0], B,
                                                                             dtype=torch.long))
         nk = min(N[0], B)
-        return (nk - first).clamp(min=0).sum()
+        return (nk - first).clamp(min=0).sum() * heads
 
     stream = torch.cuda.current_stream()
     names = ["beacon_update", "beacon_score", "topk_select", "kv_compact"]
@@ -454,6 +460,48 @@ def main():
             "moved_rows_per_pass": int(rM),
             "gbps": round(rbytes / (rpass * 1e-3) / 1e9, 1),
             "hbm_frac": round(rbytes / (rpass * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    # shared positions: one selection per (layer, request) for all its heads
+    if not args.no_shared:
+        LR = wl.n_layers * R
+        keep_s = torch.zeros((LR, B), dtype=torch.int32, device=dev)
+        rid = torch.arange(R, dtype=torch.int64, device=dev)
+        pss = torch.zeros(R, dtype=torch.int32, device=dev)
+        us = torch.zeros((LR, stride), dtype=torch.int32, device=dev)
+        shared = {}
+        for sel in ("beacon", "random"):
+            n_ev = 5 if sel == "beacon" else 4
+            runs, smoved = [], []
+            for s in range(args.warmup + args.steps):
+                refill()
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+                if sel == "beacon":
+                    bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b,
+                                      counts=c, window=W, bonus=wl.bonus, scores_out=scores,
+                                      keep_out=keep_s, score_stride=stride, status=status,
+                                      check=False, timing_events=ev, shared_positions=True)
+                else:
+                    pss.fill_(s + 2000)
+                    bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed,
+                                      request_ids=rid, pass_idx=pss, scores_out=us,
+                                      keep_out=keep_s, score_stride=stride, status=status,
+                                      check=False, timing_events=ev, shared_positions=True)
+                if s >= args.warmup:
+                    smoved.append(moved_rows(keep_s, H))
+                    runs.append(ev)
+            torch.cuda.synchronize()
+            bk.check_status(status, f"shared-position {sel} passes")
+            kn_ = (["beacon_update", "beacon_score"] if sel == "beacon" else ["random_score"]) + \
+                ["topk_select", "kv_compact"]
+            tpass = sum(e[0].elapsed_time(e[-1]) for e in runs) / len(runs)
+            shared[sel] = {
+                "passes_per_s": round(1000.0 / tpass, 3), "ms": round(tpass, 4),
+                "kernel_ms": {n: round(sum(e[i].elapsed_time(e[i + 1]) for e in runs) / len(runs), 4)
+                              for i, n in enumerate(kn_)},
+                "moved_rows_per_pass": int(float(sum(int(m) for m in smoved)) / len(smoved))}
+        shared["note"] = ("one keep list per (layer, request) for all KV heads: beacon scores "
+                          "merged by their maximum over heads, random draws one row")
+        result["shared_positions"] = shared
 
     # beacon forgetting: the maintenance kernel with a count cap (moving
     # average once a row is full), timed alone on the same queries and state

@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
-BKV_ABI_VERSION = 2
+BKV_ABI_VERSION = 3
 BKV_OK, BKV_ERR_NULL, BKV_ERR_INVALID, BKV_ERR_BUDGET, BKV_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BKV_ERR_WORKSPACE, BKV_ERR_HIP, BKV_ERR_LENGTH, BKV_ERR_BLOCK_TABLE = 5, 6, 7, 8
 BKV_SCORE_F32, BKV_SCORE_U32 = 0, 1
@@ -49,7 +49,7 @@ class bkv_cache(ctypes.Structure):
 
 class bkv_pass_args(ctypes.Structure):
     _fields_ = [
-        ("selector", _i32), ("budget", _i32), ("score_stride", _i32),
+        ("selector", _i32), ("budget", _i32), ("score_stride", _i32), ("shared_positions", _i32),
         ("n_beacons", _i32), ("T", _i32), ("G", _i32), ("window", _i32), ("bonus", _f32),
         ("queries", _P), ("beacons", _P), ("counts", _P), ("assign", _P), ("count_cap", _i32),
         ("lse", _P),
@@ -68,11 +68,15 @@ _lib.bkv_beacon_update.restype = _i32
 _lib.bkv_beacon_score.argtypes = [ctypes.POINTER(bkv_cache), _P, _P, _i32, _i32, _f32, _P, _i32,
                                   _P, _P, _P]
 _lib.bkv_beacon_score.restype = _i32
-_lib.bkv_random_score.argtypes = [ctypes.POINTER(bkv_cache), _u64, _P, _P, _P, _i32, _P, _P]
+_lib.bkv_random_score.argtypes = [ctypes.POINTER(bkv_cache), _u64, _P, _P, _i32, _P, _i32, _P,
+                                  _P]
 _lib.bkv_random_score.restype = _i32
 _lib.bkv_topk_select.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i32, _i32, _P, _P, _P]
 _lib.bkv_topk_select.restype = _i32
-_lib.bkv_kv_compact.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _P, _i32, _P, _P]
+_lib.bkv_topk_select_shared.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i32, _i32, _i32, _P,
+                                        _P, _P]
+_lib.bkv_topk_select_shared.restype = _i32
+_lib.bkv_kv_compact.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i32, _P, _i32, _P, _P]
 _lib.bkv_kv_compact.restype = _i32
 _lib.bkv_workspace_size.argtypes = [ctypes.POINTER(bkv_cache), ctypes.POINTER(bkv_pass_args),
                                     ctypes.POINTER(_sz)]
@@ -82,8 +86,8 @@ _lib.bkv_evict_pass.argtypes = [ctypes.POINTER(bkv_cache), ctypes.POINTER(bkv_pa
 _lib.bkv_evict_pass.restype = _i32
 
 EXPORTS = ("bkv_abi_version", "bkv_status_string", "bkv_beacon_update", "bkv_beacon_score",
-           "bkv_random_score", "bkv_topk_select", "bkv_kv_compact", "bkv_workspace_size",
-           "bkv_evict_pass")
+           "bkv_random_score", "bkv_topk_select", "bkv_topk_select_shared", "bkv_kv_compact",
+           "bkv_workspace_size", "bkv_evict_pass")
 
 
 class BkvError(RuntimeError):
@@ -265,36 +269,41 @@ def bkv_beacon_score(cache: PagedCache, beacons, counts, scores, window=64, bonu
     return st
 
 
-def bkv_random_score(cache: PagedCache, seed, request_ids, pass_idx, scores, status=None,
-                     check=True, stream=None):
-    """scores uint32 draws (stored in an int32 tensor) [HC, stride]."""
-    HC, R = cache.n_head_caches, cache.n_requests
+def bkv_random_score(cache: PagedCache, seed, request_ids, pass_idx, scores, shared=False,
+                     status=None, check=True, stream=None):
+    """scores uint32 draws (stored in an int32 tensor) [HC, stride], or
+    [n_layers * n_requests, stride] with shared=True (one draw row per layer and request)."""
+    R = cache.n_requests
+    rows = cache.n_layers * R if shared else cache.n_head_caches
     _need(request_ids, "request_ids", torch.int64, (R,))
     _need(pass_idx, "pass_idx", torch.int32, (R,))
     _need(scores, "scores", torch.int32)
-    if scores.dim() != 2 or scores.shape[0] != HC:
-        raise ValueError("scores must be [HC, stride]")
+    if scores.dim() != 2 or scores.shape[0] != rows:
+        raise ValueError(f"scores must be [{rows}, stride]")
     st, own = _status(status, cache.device)
     c = cache.struct()
     code = _lib.bkv_random_score(ctypes.byref(c), int(seed) & (2**64 - 1), _ptr(request_ids),
-                                 _ptr(pass_idx), _ptr(scores), scores.shape[1], _ptr(st),
-                                 _stream(stream))
+                                 _ptr(pass_idx), int(bool(shared)), _ptr(scores),
+                                 scores.shape[1], _ptr(st), _stream(stream))
     _check(code, "bkv_random_score")
     if own and check:
         check_status(st, "bkv_random_score", stream)
     return st
 
 
+def _score_kind(scores):
+    if scores.dtype == torch.float32:
+        return BKV_SCORE_F32
+    if scores.dtype == torch.int32:
+        return BKV_SCORE_U32
+    raise ValueError("scores must be float32 or int32 (uint32 bit patterns)")
+
+
 def bkv_topk_select(cache: PagedCache, scores, budget, keep, status=None, check=True,
                     stream=None):
     """scores fp32 (beacon) or int32-stored uint32 (random) [HC, stride]; keep int32 [HC, budget]."""
     HC = cache.n_head_caches
-    if scores.dtype == torch.float32:
-        kind = BKV_SCORE_F32
-    elif scores.dtype == torch.int32:
-        kind = BKV_SCORE_U32
-    else:
-        raise ValueError("scores must be float32 or int32 (uint32 bit patterns)")
+    kind = _score_kind(scores)
     _need(scores, "scores", scores.dtype)
     if scores.dim() != 2 or scores.shape[0] != HC:
         raise ValueError("scores must be [HC, stride]")
@@ -309,11 +318,37 @@ def bkv_topk_select(cache: PagedCache, scores, budget, keep, status=None, check=
     return st
 
 
+def bkv_topk_select_shared(cache: PagedCache, scores, budget, keep, status=None, check=True,
+                           stream=None):
+    """One selection per (layer, request) for all its heads.
+
+    scores [n_layers * n_requests * S, stride] with S = n_kv_heads (per-head
+    scores, merged by their maximum) or S = 1 (one shared draw row);
+    keep int32 [n_layers * n_requests, budget]."""
+    LR = cache.n_layers * cache.n_requests
+    kind = _score_kind(scores)
+    _need(scores, "scores", scores.dtype)
+    if scores.dim() != 2 or scores.shape[0] % LR:
+        raise ValueError("scores must be [n_layers * n_requests * S, stride]")
+    S = scores.shape[0] // LR
+    _need(keep, "keep", torch.int32, (LR, budget))
+    st, own = _status(status, cache.device)
+    c = cache.struct()
+    code = _lib.bkv_topk_select_shared(ctypes.byref(c), _ptr(scores), kind, scores.shape[1], S,
+                                       int(budget), _ptr(keep), _ptr(st), _stream(stream))
+    _check(code, "bkv_topk_select_shared")
+    if own and check:
+        check_status(st, "bkv_topk_select_shared", stream)
+    return st
+
+
 def bkv_kv_compact(cache: PagedCache, keep, budget, pos_ids=None, status=None, check=True,
-                   stream=None):
-    """In-place compaction of every layer pool; pos_ids int32 [HC, >= max_slots] optional."""
+                   stream=None, keep_shared=False):
+    """In-place compaction of every layer pool; pos_ids int32 [HC, >= max_slots] optional.
+    keep int32 [HC, budget], or [n_layers * n_requests, budget] with keep_shared=True."""
     HC = cache.n_head_caches
-    _need(keep, "keep", torch.int32, (HC, budget))
+    rows = cache.n_layers * cache.n_requests if keep_shared else HC
+    _need(keep, "keep", torch.int32, (rows, budget))
     pos_stride = 0
     if pos_ids is not None:
         _need(pos_ids, "pos_ids", torch.int32)
@@ -322,8 +357,8 @@ def bkv_kv_compact(cache: PagedCache, keep, budget, pos_ids=None, status=None, c
         pos_stride = pos_ids.shape[1]
     st, own = _status(status, cache.device)
     c = cache.struct()
-    code = _lib.bkv_kv_compact(ctypes.byref(c), _ptr(keep), int(budget), _ptr(pos_ids),
-                               pos_stride, _ptr(st), _stream(stream))
+    code = _lib.bkv_kv_compact(ctypes.byref(c), _ptr(keep), int(budget), int(bool(keep_shared)),
+                               _ptr(pos_ids), pos_stride, _ptr(st), _stream(stream))
     _check(code, "bkv_kv_compact")
     if own and check:
         check_status(st, "bkv_kv_compact", stream)
@@ -332,12 +367,14 @@ def bkv_kv_compact(cache: PagedCache, keep, budget, pos_ids=None, status=None, c
 
 def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, window, bonus,
                assign, lse, seed, request_ids, pass_idx, pos_ids, scores_out, keep_out,
-               score_stride, count_cap=0):
+               score_stride, count_cap=0, shared_positions=False):
     HC, R = cache.n_head_caches, cache.n_requests
+    LR = cache.n_layers * R
     a = bkv_pass_args()
     a.selector = selector
     a.budget = int(budget)
     a.score_stride = int(score_stride)
+    a.shared_positions = int(bool(shared_positions))
     if selector == BKV_SELECT_BEACON:
         _need(queries, "queries", torch.bfloat16)
         if queries.dim() != 4 or queries.shape[0] != HC or queries.shape[3] != HEAD_DIM:
@@ -368,10 +405,11 @@ def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, wi
     stride = score_stride if score_stride > 0 else cache.max_slots
     if scores_out is not None:
         want = torch.float32 if selector == BKV_SELECT_BEACON else torch.int32
-        _need(scores_out, "scores_out", want, (HC, stride))
+        rows = LR if shared_positions and selector == BKV_SELECT_RANDOM else HC
+        _need(scores_out, "scores_out", want, (rows, stride))
         a.scores_out = scores_out.data_ptr()
     if keep_out is not None:
-        _need(keep_out, "keep_out", torch.int32, (HC, budget))
+        _need(keep_out, "keep_out", torch.int32, (LR if shared_positions else HC, budget))
         a.keep_out = keep_out.data_ptr()
     return a
 
@@ -388,15 +426,16 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
                    counts=None, window=64, bonus=1.0, assign=None, lse=None, seed=0,
                    request_ids=None, pass_idx=None, pos_ids=None, scores_out=None,
                    keep_out=None, score_stride=0, workspace=None, status=None, check=True,
-                   stream=None, timing_events=None, count_cap=0):
+                   stream=None, timing_events=None, count_cap=0, shared_positions=False):
     """One whole eviction pass (beacon: update -> score -> select -> compact;
     random: score -> select -> compact), every layer/request/head at once.
+    shared_positions: one selection per (layer, request) for all its heads.
 
     timing_events: optional list of torch.cuda.Event(enable_timing=True), 5 for
     the beacon selector and 4 for the random one, recorded around each kernel."""
     a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
                    seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride,
-                   count_cap)
+                   count_cap, shared_positions)
     ev_arr = None
     if timing_events is not None:
         handles = []

@@ -53,22 +53,33 @@ struct PassLayout {
     size_t scores_off, keep_off, total;
 };
 
+// Rows of the score buffer and of the keep buffer of a pass.  With shared
+// positions the random selector draws one row per (layer, request) and every
+// selector keeps one list per (layer, request); beacon scores stay per head.
+size_t score_rows(const CacheView& v, const bkv_pass_args* a) {
+    const bool one = a->shared_positions && a->selector == BKV_SELECT_RANDOM;
+    return (size_t)v.L * v.R * (one ? 1 : v.H);
+}
+size_t keep_rows(const CacheView& v, const bkv_pass_args* a) {
+    return (size_t)v.L * v.R * (a->shared_positions ? 1 : v.H);
+}
+
 int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     const int max_slots = v.max_blocks * kBlock;
     const int stride = a->score_stride > 0 ? a->score_stride : max_slots;
     if (stride > BKV_MAX_CANDIDATES) return BKV_ERR_INVALID;
     if (a->budget < 1) return BKV_ERR_INVALID;
-    const size_t HC = (size_t)head_caches(v);
+    if (a->shared_positions != 0 && a->shared_positions != 1) return BKV_ERR_INVALID;
     size_t off = 0;
     L->stride = stride;
     L->scores_off = L->keep_off = 0;
     if (!a->scores_out) {
         L->scores_off = off;
-        off = round_up(off + HC * (size_t)stride * 4, 256);
+        off = round_up(off + score_rows(v, a) * (size_t)stride * 4, 256);
     }
     if (!a->keep_out) {
         L->keep_off = off;
-        off = round_up(off + HC * (size_t)a->budget * 4, 256);
+        off = round_up(off + keep_rows(v, a) * (size_t)a->budget * 4, 256);
     }
     L->total = off;
     return BKV_OK;
@@ -129,18 +140,18 @@ int32_t bkv_beacon_score(const bkv_cache* cache, const float* beacons, const int
 }
 
 int32_t bkv_random_score(const bkv_cache* cache, uint64_t seed, const uint64_t* request_ids,
-                         const int32_t* pass_idx, uint32_t* scores, int32_t score_stride,
-                         int32_t* status, bkv_stream_t stream) {
+                         const int32_t* pass_idx, int32_t shared, uint32_t* scores,
+                         int32_t score_stride, int32_t* status, bkv_stream_t stream) {
     CacheView v;
     int32_t e = check_cache(cache, &v);
     if (e) return e;
     if (!request_ids || !pass_idx || !scores) return BKV_ERR_NULL;
-    if (score_stride < 1) return BKV_ERR_INVALID;
+    if (score_stride < 1 || (shared != 0 && shared != 1)) return BKV_ERR_INVALID;
     if (!aligned(request_ids, 8) || !aligned(pass_idx, 4) || !aligned(scores, 4) ||
         (status && !aligned(status, 4)))
         return BKV_ERR_INVALID;
-    return hip_status(launch_random_score(v, seed, request_ids, pass_idx, scores, score_stride,
-                                          Check{-1, score_stride, 0}, status,
+    return hip_status(launch_random_score(v, seed, request_ids, pass_idx, shared, scores,
+                                          score_stride, Check{-1, score_stride, 0}, status,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -155,24 +166,41 @@ int32_t bkv_topk_select(const bkv_cache* cache, const void* scores, int32_t scor
     if (score_stride < 1 || score_stride > BKV_MAX_CANDIDATES || budget < 1) return BKV_ERR_INVALID;
     if (!aligned(scores, 4) || !aligned(keep_idx, 4) || (status && !aligned(status, 4)))
         return BKV_ERR_INVALID;
-    return hip_status(launch_topk_select(v, scores, score_kind, score_stride, budget, keep_idx,
-                                         Check{budget, score_stride, 0}, status,
+    return hip_status(launch_topk_select(v, scores, score_kind, score_stride, 1, 0, budget,
+                                         keep_idx, Check{budget, score_stride, 0}, status,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int32_t bkv_topk_select_shared(const bkv_cache* cache, const void* scores, int32_t score_kind,
+                               int32_t score_stride, int32_t score_heads, int32_t budget,
+                               int32_t* keep_idx, int32_t* status, bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!scores || !keep_idx) return BKV_ERR_NULL;
+    if (score_kind != BKV_SCORE_F32 && score_kind != BKV_SCORE_U32) return BKV_ERR_INVALID;
+    if (score_stride < 1 || score_stride > BKV_MAX_CANDIDATES || budget < 1) return BKV_ERR_INVALID;
+    if (score_heads < 1 || score_heads > v.H) return BKV_ERR_INVALID;
+    if (!aligned(scores, 4) || !aligned(keep_idx, 4) || (status && !aligned(status, 4)))
+        return BKV_ERR_INVALID;
+    return hip_status(launch_topk_select(v, scores, score_kind, score_stride, score_heads, 1,
+                                         budget, keep_idx, Check{budget, score_stride, 0}, status,
                                          static_cast<hipStream_t>(stream)));
 }
 
 int32_t bkv_kv_compact(const bkv_cache* cache, const int32_t* keep_idx, int32_t budget,
-                       int32_t* pos_ids, int32_t pos_stride, int32_t* status,
-                       bkv_stream_t stream) {
+                       int32_t keep_shared, int32_t* pos_ids, int32_t pos_stride,
+                       int32_t* status, bkv_stream_t stream) {
     CacheView v;
     int32_t e = check_cache(cache, &v);
     if (e) return e;
     if (!keep_idx) return BKV_ERR_NULL;
-    if (budget < 1) return BKV_ERR_INVALID;
+    if (budget < 1 || (keep_shared != 0 && keep_shared != 1)) return BKV_ERR_INVALID;
     if (pos_ids && pos_stride < v.max_blocks * kBlock) return BKV_ERR_INVALID;
     if (!aligned(keep_idx, 4) || (pos_ids && !aligned(pos_ids, 4)) ||
         (status && !aligned(status, 4)))
         return BKV_ERR_INVALID;
-    return hip_status(launch_kv_compact(v, keep_idx, budget, pos_ids, pos_stride,
+    return hip_status(launch_kv_compact(v, keep_idx, budget, keep_shared, pos_ids, pos_stride,
                                         Check{budget, -1, 1}, status,
                                         static_cast<hipStream_t>(stream)));
 }
@@ -208,6 +236,7 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
     if ((a->scores_out && !aligned(a->scores_out, 4)) || (a->keep_out && !aligned(a->keep_out, 4)))
         return BKV_ERR_INVALID;
     const bool beacon = a->selector == BKV_SELECT_BEACON;
+    const int shared = a->shared_positions;
     if (beacon) {
         if (!a->queries || !a->beacons || !a->counts) return BKV_ERR_NULL;
         if (a->n_beacons < 1 || a->n_beacons > BKV_MAX_BEACONS || a->T < 1 || a->G < 1 ||
@@ -249,20 +278,21 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
             he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
                                      static_cast<float*>(sc), L.stride, a->lse, all, status, s);
         if (he == hipSuccess) he = mark();
-        if (he == hipSuccess)
-            he = launch_topk_select(v, sc, BKV_SCORE_F32, L.stride, a->budget, keep, all, status,
-                                    s);
+        if (he == hipSuccess)  // shared: the largest of the H per-head scores
+            he = launch_topk_select(v, sc, BKV_SCORE_F32, L.stride, v.H, shared, a->budget, keep,
+                                    all, status, s);
     } else {
-        he = launch_random_score(v, a->seed, a->request_ids, a->pass_idx,
+        he = launch_random_score(v, a->seed, a->request_ids, a->pass_idx, shared,
                                  static_cast<uint32_t*>(sc), L.stride, all, status, s);
         if (he == hipSuccess) he = mark();
-        if (he == hipSuccess)
-            he = launch_topk_select(v, sc, BKV_SCORE_U32, L.stride, a->budget, keep, all, status,
-                                    s);
+        if (he == hipSuccess)  // shared: one draw row per (layer, request)
+            he = launch_topk_select(v, sc, BKV_SCORE_U32, L.stride, 1, shared, a->budget, keep,
+                                    all, status, s);
     }
     if (he == hipSuccess) he = mark();
     if (he == hipSuccess)
-        he = launch_kv_compact(v, keep, a->budget, a->pos_ids, a->pos_stride, all, status, s);
+        he = launch_kv_compact(v, keep, a->budget, shared, a->pos_ids, a->pos_stride, all, status,
+                               s);
     if (he == hipSuccess) he = mark();
     return hip_status(he);
 }

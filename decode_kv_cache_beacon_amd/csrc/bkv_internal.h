@@ -123,14 +123,15 @@ hipError_t launch_beacon_update(int HC, int T, int G, int K, const uint16_t* q, 
 hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const int32_t* counts,
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, Check ck, int32_t* status, hipStream_t s);
+// `shared`: one row / keep list per (layer, request) instead of per head-cache.
 hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
-                               const int32_t* pass_idx, uint32_t* scores, int stride, Check ck,
-                               int32_t* status, hipStream_t s);
+                               const int32_t* pass_idx, int shared, uint32_t* scores, int stride,
+                               Check ck, int32_t* status, hipStream_t s);
 hipError_t launch_topk_select(const CacheView& c, const void* scores, int kind, int stride,
-                              int budget, int32_t* keep, Check ck, int32_t* status,
-                              hipStream_t s);
+                              int score_heads, int shared, int budget, int32_t* keep, Check ck,
+                              int32_t* status, hipStream_t s);
 hipError_t launch_kv_compact(const CacheView& c, const int32_t* keep, int budget,
-                             int32_t* pos_ids, int pos_stride, Check ck, int32_t* status,
-                             hipStream_t s);
+                             int keep_shared, int32_t* pos_ids, int pos_stride, Check ck,
+                             int32_t* status, hipStream_t s);
 
 }  // namespace bkv

@@ -14,6 +14,9 @@
 // Memory: a row is 256 contiguous bytes; 16 lanes move one row with 16-byte
 // accesses, so each wave instruction moves 4 whole rows (1 KiB).  The rows
 // are touched once, so loads and stores are non-temporal.
+//
+// With shared positions every head of a (layer, request) applies the one keep
+// list of that (layer, request).
 
 #include "bkv_internal.h"
 
@@ -28,7 +31,8 @@ constexpr int kRowsPerIter = kRowsPerRound * kRounds;       // 128 rows per barr
 
 __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CacheView c,
                                                               const int32_t* __restrict__ keep,
-                                                              int B, int32_t* __restrict__ pos_ids,
+                                                              int B, int keep_shared,
+                                                              int32_t* __restrict__ pos_ids,
                                                               int pos_stride, Check ck,
                                                               int32_t* status) {
     const int hc = blockIdx.x;
@@ -37,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CacheView c,
 
     const int N = c.seq_len[x.req];
     const int nk = min(N, B);
-    const int32_t* kp = keep + (size_t)hc * B;
+    const int32_t* kp = keep + (size_t)(keep_shared ? hc / c.H : hc) * B;
 
     // The keep list must be strictly ascending inside [0, N): that is what
     // keeps every access in bounds and the in-place move race-free.
@@ -108,12 +112,12 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CacheView c,
 }  // namespace
 
 hipError_t launch_kv_compact(const CacheView& c, const int32_t* keep, int budget,
-                             int32_t* pos_ids, int pos_stride, Check ck, int32_t* status,
-                             hipStream_t s) {
+                             int keep_shared, int32_t* pos_ids, int pos_stride, Check ck,
+                             int32_t* status, hipStream_t s) {
     const int HC = c.L * c.R * c.H;
     if (HC == 0) return hipSuccess;
     hipLaunchKernelGGL(kv_compact_kernel, dim3(HC), dim3(kThreads), 0, s, c, keep, budget,
-                       pos_ids, pos_stride, ck, status);
+                       keep_shared, pos_ids, pos_stride, ck, status);
     return hipGetLastError();
 }
 

@@ -4,7 +4,9 @@
 //
 // Counter-based: the draw of slot n depends only on (seed, request id, pass
 // index, layer, head, n), so the scorer needs no RNG state and a new pass
-// index draws afresh.  Philox4x64-10 as published by Salmon, Moraes, Dror and
+// index draws afresh.  With shared positions (same article, section "发现二":
+// every head on one common set of positions) one row per (layer, request) is
+// drawn, with the head field of the counter set to 0.  Philox4x64-10 as published by Salmon, Moraes, Dror and
 // Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC'11): ten rounds of
 // two 64x64->128-bit multiplies with a Weyl-sequence key schedule.  One thread
 // evaluates one counter and scores the four slots 4g .. 4g+3.
@@ -43,10 +45,10 @@ __device__ __forceinline__ U64x4 philox4x64_10(U64x4 x, uint64_t k0, uint64_t k1
 
 __global__ __launch_bounds__(kThreads) void random_score_kernel(
     CacheView c, uint64_t seed, const uint64_t* __restrict__ req_ids,
-    const int32_t* __restrict__ pass_idx, uint32_t* __restrict__ scores, int stride, Check ck,
-    int32_t* status) {
-    const int hc = blockIdx.x;
-    const HeadIdx x = split_hc(c, hc);
+    const int32_t* __restrict__ pass_idx, int shared, uint32_t* __restrict__ scores, int stride,
+    Check ck, int32_t* status) {
+    const int row = blockIdx.x;  // head-cache, or (layer, request) when shared
+    const HeadIdx x = shared ? HeadIdx{row / c.R, row % c.R, 0} : split_hc(c, row);
     if (!request_ok(c, x.layer, x.req, ck, status)) return;
     const int N = c.seq_len[x.req];
     const int P = c.prompt_len[x.req];
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void random_score_kernel(
     ctr.v[2] = ((uint64_t)(uint32_t)x.layer << 32) | (uint64_t)(uint32_t)x.head;
     ctr.v[3] = req_ids[x.req];
     const U64x4 w = philox4x64_10(ctr, seed, 0);
-    uint32_t* out = scores + (size_t)hc * stride;
+    uint32_t* out = scores + (size_t)row * stride;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int n = n0 + k;
@@ -71,15 +73,15 @@ __global__ __launch_bounds__(kThreads) void random_score_kernel(
 }  // namespace
 
 hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
-                               const int32_t* pass_idx, uint32_t* scores, int stride, Check ck,
-                               int32_t* status, hipStream_t s) {
-    const int HC = c.L * c.R * c.H;
-    if (HC == 0) return hipSuccess;
+                               const int32_t* pass_idx, int shared, uint32_t* scores, int stride,
+                               Check ck, int32_t* status, hipStream_t s) {
+    const int rows = c.L * c.R * (shared ? 1 : c.H);
+    if (rows == 0) return hipSuccess;
     const int max_slots = c.max_blocks * kBlock;
     const int groups = (max_slots + 3) / 4;
     const int gx = (groups + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(random_score_kernel, dim3(HC, gx), dim3(kThreads), 0, s, c, seed, req_ids,
-                       pass_idx, scores, stride, ck, status);
+    hipLaunchKernelGGL(random_score_kernel, dim3(rows, gx), dim3(kThreads), 0, s, c, seed,
+                       req_ids, pass_idx, shared, scores, stride, ck, status);
     return hipGetLastError();
 }
 

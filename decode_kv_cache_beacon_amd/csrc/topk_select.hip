@@ -11,6 +11,12 @@
 // prefix scans (over "== T" and over "kept") then emit the kept slots in
 // ascending order, prompt first.  The selection is exact integer work, so the
 // result is bit-reproducible.
+//
+// Shared positions (same article, section "发现二": all heads on one common
+// set of positions): one workgroup per (layer, request) selects once for all
+// its KV heads.  A candidate's key is the largest of its `score_heads`
+// per-head keys (score_heads = 1 for one shared random draw), and the keep
+// list is written once per (layer, request).
 
 #include "bkv_internal.h"
 
@@ -46,7 +52,8 @@ __device__ int block_exclusive_scan(int v, int* s_wsum) {
 
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
                                                                const uint32_t* __restrict__ scores,
-                                                               int is_f32, int stride, int B,
+                                                               int is_f32, int stride,
+                                                               int score_heads, int shared, int B,
                                                                int32_t* __restrict__ keep, Check ck,
                                                                int32_t* status) {
     extern __shared__ uint32_t s_key[];  // [stride]
@@ -55,12 +62,12 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
     __shared__ uint32_t s_prefix;
     __shared__ int s_need;
 
-    const int hc = blockIdx.x;
-    const HeadIdx x = split_hc(c, hc);
+    const int unit = blockIdx.x;  // head-cache, or (layer, request) when shared
+    const HeadIdx x = shared ? HeadIdx{unit / c.R, unit % c.R, 0} : split_hc(c, unit);
     if (!request_ok(c, x.layer, x.req, ck, status)) return;
     const int N = c.seq_len[x.req];
     const int P = c.prompt_len[x.req];
-    int32_t* out = keep + (size_t)hc * B;
+    int32_t* out = keep + (size_t)unit * B;
     const int tid = threadIdx.x;
 
     if (N <= B) {  // nothing to evict: keep every slot
@@ -72,10 +79,14 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
     for (int i = tid; i < P; i += kThreads) out[i] = i;
     if (k == 0) return;
 
-    const uint32_t* src = scores + (size_t)hc * stride;
+    const uint32_t* src = scores + (size_t)unit * score_heads * stride;
     for (int i = tid; i < m; i += kThreads) {
-        uint32_t v = src[i];
-        if (is_f32 && (v >> 31)) v = 0;  // negative fp32 scores rank as 0
+        uint32_t v = 0;
+        for (int h = 0; h < score_heads; ++h) {
+            uint32_t w = src[(size_t)h * stride + i];
+            if (is_f32 && (w >> 31)) w = 0;  // negative fp32 scores rank as 0
+            v = max(v, w);
+        }
         s_key[i] = v;
     }
 
@@ -148,19 +159,19 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
 }  // namespace
 
 hipError_t launch_topk_select(const CacheView& c, const void* scores, int kind, int stride,
-                              int budget, int32_t* keep, Check ck, int32_t* status,
-                              hipStream_t s) {
-    const int HC = c.L * c.R * c.H;
-    if (HC == 0) return hipSuccess;
+                              int score_heads, int shared, int budget, int32_t* keep, Check ck,
+                              int32_t* status, hipStream_t s) {
+    const int units = c.L * c.R * (shared ? 1 : c.H);
+    if (units == 0) return hipSuccess;
     const size_t lds = (size_t)stride * sizeof(uint32_t);
     if (lds > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(topk_select_kernel, dim3(HC), dim3(kThreads), lds, s, c,
+    hipLaunchKernelGGL(topk_select_kernel, dim3(units), dim3(kThreads), lds, s, c,
                        static_cast<const uint32_t*>(scores), kind == BKV_SCORE_F32 ? 1 : 0,
-                       stride, budget, keep, ck, status);
+                       stride, shared ? score_heads : 1, shared, budget, keep, ck, status);
     return hipGetLastError();
 }
 

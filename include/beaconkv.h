@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 2
+#define BKV_ABI_VERSION 3
 
 typedef void* bkv_stream_t; /* hipStream_t */
 
@@ -108,7 +108,7 @@ int32_t bkv_abi_version(void);
 /* Static English text of a code; never NULL. */
 const char* bkv_status_string(int32_t code);
 
-/* a1 -- Beacon maintenance (BeaconKV explainer, section 3.2: nearest beacon,
+/* Beacon maintenance (BeaconKV explainer, section 3.2: nearest beacon,
  * incremental update).  For each of HC head-caches, absorbs the T*G buffered
  * decode queries queries[hc][t][g][:] (bf16, 128 wide) in (t, then g) order:
  *   - if some row has count 0, the smallest such row j takes the query:
@@ -130,7 +130,7 @@ int32_t bkv_beacon_update(int32_t n_head_caches, int32_t T, int32_t G, int32_t h
                           int32_t K, const uint16_t* queries, float* beacons, int32_t* counts,
                           int32_t* assign, int32_t count_cap, bkv_stream_t stream);
 
-/* a2/a3 -- Beacon scoring of every cached key (the traversal of the paged KV
+/* Beacon scoring of every cached key (the traversal of the paged KV
  * state that content-dependent selectors need; Random Attention article,
  * section "发现四").  With live beacons J = {j : counts[hc][j] > 0} rounded to
  * bf16 (round to nearest even) and s_jn = (bf16(b_j) . k_n) / sqrt(128)
@@ -147,19 +147,23 @@ int32_t bkv_beacon_score(const bkv_cache* cache, const float* beacons, const int
                          int32_t score_stride, float* lse, int32_t* status,
                          bkv_stream_t stream);
 
-/* a4 -- Random-selector scores (Random Attention article, section "Random
+/* Random-selector scores (Random Attention article, section "Random
  * Attention": independent per-head random retention; no key is read).  For
  * slot n in [P, N) of head-cache (layer, r, head):
  *   scores[hc * score_stride + (n - P)] = high 32 bits of word (n mod 4) of
  *   Philox4x64-10(counter = (n div 4, pass_idx[r], (layer << 32) | head,
  *                  request_ids[r]), key = (seed, 0)).
  * request_ids uint64 [n_requests], pass_idx int32 [n_requests] are device
- * arrays; a new pass index gives fresh draws. */
+ * arrays; a new pass index gives fresh draws.
+ * shared = 1 (shared positions, same article, section "发现二": all heads on
+ * one common set of random positions): one row per (layer, request), row
+ * layer * n_requests + r, holding the draws of head 0; shared = 0: one row
+ * per head-cache.  Any other value is BKV_ERR_INVALID. */
 int32_t bkv_random_score(const bkv_cache* cache, uint64_t seed, const uint64_t* request_ids,
-                         const int32_t* pass_idx, uint32_t* scores, int32_t score_stride,
-                         int32_t* status, bkv_stream_t stream);
+                         const int32_t* pass_idx, int32_t shared, uint32_t* scores,
+                         int32_t score_stride, int32_t* status, bkv_stream_t stream);
 
-/* a5 -- Top-B selection with full prompt protection (Random Attention article,
+/* Top-B selection with full prompt protection (Random Attention article,
  * section "Random Attention": the prompt is always kept, the rest is a per-head
  * top-K).  The budget includes the prompt.  Per head-cache, keep_idx[hc][:]
  * (int32 [HC][budget]) receives the kept slots in ascending order:
@@ -175,7 +179,20 @@ int32_t bkv_topk_select(const bkv_cache* cache, const void* scores, int32_t scor
                         int32_t score_stride, int32_t budget, int32_t* keep_idx,
                         int32_t* status, bkv_stream_t stream);
 
-/* a6 -- Cache compaction (Random Attention article, section "发现四": the one
+/* Shared positions (Random Attention article, section "发现二": forcing
+ * every head onto one common set of positions leaves accuracy almost
+ * unchanged).  One selection per (layer, request), u = layer * n_requests + r,
+ * for all its KV heads.  The candidate key of slot n is the largest of the
+ * score_heads per-head keys scores[(u * score_heads + h) * score_stride +
+ * (n - P)], h < score_heads (1 <= score_heads <= n_kv_heads: n_kv_heads for
+ * per-head beacon scores, 1 for one shared random draw row); keys are ranked
+ * and the prompt protected exactly as in bkv_topk_select.  keep_idx is int32
+ * [n_layers * n_requests][budget]; use it with bkv_kv_compact(keep_shared=1). */
+int32_t bkv_topk_select_shared(const bkv_cache* cache, const void* scores, int32_t score_kind,
+                               int32_t score_stride, int32_t score_heads, int32_t budget,
+                               int32_t* keep_idx, int32_t* status, bkv_stream_t stream);
+
+/* Cache compaction (Random Attention article, section "发现四": the one
  * step every selector shares).  In place, for i < min(N, budget):
  *   K[i] <- K[keep[i]], V[i] <- V[keep[i]]   (every layer pool, per head)
  *   pos_ids[hc][i] <- pos_ids[hc][keep[i]]   (when pos_ids is not NULL)
@@ -183,17 +200,26 @@ int32_t bkv_topk_select(const bkv_cache* cache, const void* scores, int32_t scor
  * ascending inside [0, N) (device-checked: BKV_ERR_INVALID, head-cache left
  * untouched); slots past min(N, budget) keep stale data and can be released by
  * the caller (every head keeps the same count, so whole tail blocks free up).
- * seq_len is not modified. */
+ * seq_len is not modified.  keep_shared = 0: keep_idx is [HC][budget], one
+ * list per head-cache; keep_shared = 1: keep_idx is [n_layers *
+ * n_requests][budget] and head-cache hc applies row hc / n_kv_heads (shared
+ * positions, see bkv_topk_select_shared). */
 int32_t bkv_kv_compact(const bkv_cache* cache, const int32_t* keep_idx, int32_t budget,
-                       int32_t* pos_ids, int32_t pos_stride, int32_t* status,
-                       bkv_stream_t stream);
+                       int32_t keep_shared, int32_t* pos_ids, int32_t pos_stride,
+                       int32_t* status, bkv_stream_t stream);
 
-/* a7 -- One whole eviction pass at a synchronized batch point: maintenance,
+/* One whole eviction pass at a synchronized batch point: maintenance,
  * scoring, selection and compaction for every layer, request and head. */
 typedef struct bkv_pass_args {
     int32_t selector;          /* BKV_SELECT_BEACON or BKV_SELECT_RANDOM */
     int32_t budget;            /* B, prompt included */
     int32_t score_stride;      /* 0 -> max_blocks * block_size */
+    int32_t shared_positions;  /* 0: per-head selection; 1: one selection per (layer,
+                                  request) for all its heads (bkv_topk_select_shared:
+                                  beacon merges the per-head scores by their maximum,
+                                  random draws one row); keep lists then have
+                                  n_layers * n_requests rows, and so does the random
+                                  selector's score buffer */
     /* beacon selector */
     int32_t n_beacons;         /* K */
     int32_t T, G;              /* buffered decode steps, query heads per KV head */
@@ -212,8 +238,8 @@ typedef struct bkv_pass_args {
     /* optional outputs / buffers */
     int32_t* pos_ids;          /* nullable int32 [HC][pos_stride], compacted with the cache */
     int32_t pos_stride;
-    void* scores_out;          /* nullable [HC][score_stride] scores; else workspace */
-    int32_t* keep_out;         /* nullable [HC][budget] keep lists; else workspace */
+    void* scores_out;          /* nullable [rows][score_stride] scores; else workspace */
+    int32_t* keep_out;         /* nullable [rows][budget] keep lists; else workspace */
     /* optional profiling hook: caller-created hipEvent_t handles, recorded on
      * `stream` before the first kernel and after every kernel of the pass
      * (beacon: 5 events around update, score, select, compact; random: 4
@@ -228,7 +254,8 @@ typedef struct bkv_pass_args {
  * buffer aligned to 256 bytes. */
 int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, size_t* bytes);
 
-/* Runs, on `stream`: (beacon) a1 -> a2/a3 -> a5 -> a6, or (random) a4 -> a5 -> a6.
+/* Runs, on `stream`: (beacon) maintenance -> beacon scoring -> selection ->
+ * compaction, or (random) random scoring -> selection -> compaction.
  * A request that fails a device check (lengths, block ids, budget) is left
  * entirely untouched -- beacons, counts, cache and pos_ids -- and flagged in
  * *status. */

@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     lib = ctypes.CDLL(bk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 2
+    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 3
     for code in range(0, 9):
         s = bk.bkv_status_string(code)
         assert s and s != "unknown status code"
@@ -96,12 +96,27 @@ def test_select_compact_random_validation():
     assert sel(ctypes.byref(c), FAKE, 0, 160, 0, FAKE, None, None) == bk.BKV_ERR_INVALID
     assert sel(ctypes.byref(c), None, 0, 160, 64, FAKE, None, None) == bk.BKV_ERR_NULL
     cmp_ = bk._lib.bkv_kv_compact
-    assert cmp_(ctypes.byref(c), None, 64, None, 0, None, None) == bk.BKV_ERR_NULL
-    assert cmp_(ctypes.byref(c), FAKE, 0, None, 0, None, None) == bk.BKV_ERR_INVALID
-    assert cmp_(ctypes.byref(c), FAKE, 64, FAKE, 100, None, None) == bk.BKV_ERR_INVALID  # pos stride < 160
+    assert cmp_(ctypes.byref(c), None, 64, 0, None, 0, None, None) == bk.BKV_ERR_NULL
+    assert cmp_(ctypes.byref(c), FAKE, 0, 0, None, 0, None, None) == bk.BKV_ERR_INVALID
+    assert cmp_(ctypes.byref(c), FAKE, 64, 0, FAKE, 100, None, None) == bk.BKV_ERR_INVALID  # pos stride < 160
+    assert cmp_(ctypes.byref(c), FAKE, 64, 2, None, 0, None, None) == bk.BKV_ERR_INVALID   # keep_shared
     rnd = bk._lib.bkv_random_score
-    assert rnd(ctypes.byref(c), 1, None, FAKE, FAKE, 160, None, None) == bk.BKV_ERR_NULL
-    assert rnd(ctypes.byref(c), 1, FAKE, FAKE, FAKE, 0, None, None) == bk.BKV_ERR_INVALID
+    assert rnd(ctypes.byref(c), 1, None, FAKE, 0, FAKE, 160, None, None) == bk.BKV_ERR_NULL
+    assert rnd(ctypes.byref(c), 1, FAKE, FAKE, 0, FAKE, 0, None, None) == bk.BKV_ERR_INVALID
+    assert rnd(ctypes.byref(c), 1, FAKE, FAKE, -1, FAKE, 160, None, None) == bk.BKV_ERR_INVALID
+
+
+def test_shared_select_validation():
+    c = _cache()   # 8 KV heads
+    f = bk._lib.bkv_topk_select_shared
+    assert f(ctypes.byref(c), FAKE, 0, 160, 0, 64, FAKE, None, None) == bk.BKV_ERR_INVALID  # S < 1
+    assert f(ctypes.byref(c), FAKE, 0, 160, 9, 64, FAKE, None, None) == bk.BKV_ERR_INVALID  # S > H
+    assert f(ctypes.byref(c), FAKE, 3, 160, 8, 64, FAKE, None, None) == bk.BKV_ERR_INVALID  # kind
+    assert f(ctypes.byref(c), FAKE, 0, 40000, 8, 64, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert f(ctypes.byref(c), FAKE, 0, 160, 8, 0, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert f(ctypes.byref(c), None, 0, 160, 8, 64, FAKE, None, None) == bk.BKV_ERR_NULL
+    assert f(ctypes.byref(c), FAKE, 0, 160, 8, 64, FAKE + 2, None, None) == bk.BKV_ERR_INVALID
+    assert f(None, FAKE, 0, 160, 8, 64, FAKE, None, None) == bk.BKV_ERR_NULL
 
 
 def test_workspace_and_pass_validation():
@@ -112,6 +127,16 @@ def test_workspace_and_pass_validation():
     assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
     HC = 2 * 3 * 8
     assert n.value >= HC * 160 * 4 + HC * 64 * 4
+    a.shared_positions = 1        # random + shared: one score row and one keep row per (layer, request)
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
+    assert HC // 8 * (160 + 64) * 4 <= n.value < HC * 64 * 4
+    a.selector = bk.BKV_SELECT_BEACON   # beacon + shared: per-head scores, shared keep rows
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
+    assert HC * 160 * 4 + HC // 8 * 64 * 4 <= n.value < HC * 160 * 4 + HC * 64 * 4
+    a.shared_positions = 2
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == \
+        bk.BKV_ERR_INVALID
+    a.shared_positions, a.selector = 0, bk.BKV_SELECT_RANDOM
     a.scores_out, a.keep_out = FAKE, FAKE
     assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
     assert n.value == 0

@@ -112,3 +112,73 @@ def test_full_size_serving_pass():
         vo = gather_head(batch.v_pools[layer], bt[r], h, n)
         assert np.array_equal(ko[:nk], oracle.kv_compact(x["keys"], k)), hc
         assert np.array_equal(vo[:nk], oracle.kv_compact(x["vals"], k)), hc
+
+
+@pytest.mark.parametrize("selector", ["beacon", "random"])
+def test_full_size_shared_positions_pass(selector):
+    """The same workload with one selection per (layer, request) for all eight KV
+    heads, launched as the benchmark's shared-position passes.  A spread sample
+    of (layer, request) units is checked against the oracle's shared selection
+    (on the GPU's own per-head scores for the beacon selector, whose scores the
+    per-head test already checks; on the oracle's own draws for the random
+    one) and against the oracle's gather for every head of the unit."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from decode_kv_cache_beacon_amd import beaconkv as bk
+
+    wl = synth.WORKLOADS["serving_r128"]
+    dev = torch.device("cuda")
+    say("full size shared", selector, "generate")
+    batch = synth.make_batch(wl, dev)
+    cache = bk.PagedCache(batch.k_pools, batch.v_pools, batch.block_table, batch.seq_len,
+                          batch.prompt_len)
+    L, R, H = cache.n_layers, cache.n_requests, cache.n_kv_heads
+    HC, B, W = cache.n_head_caches, wl.budget, wl.window
+    N = batch.seq_len.cpu().numpy()
+    P = batch.prompt_len.cpu().numpy()
+    stride = int((N - P).max())
+    rng = np.random.default_rng(77)
+    sample = sorted({0, L * R - 1, *rng.choice(L * R, 10, replace=False).tolist()})
+    bt = batch.block_table
+    before = {}
+    for u in sample:
+        layer, r = u // R, u % R
+        before[u] = [(gather_head(batch.k_pools[layer], bt[r], h, int(N[r])),
+                      gather_head(batch.v_pools[layer], bt[r], h, int(N[r]))) for h in range(H)]
+    keep = torch.full((L * R, B), -7, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    say("full size shared", selector, "pass")
+    if selector == "beacon":
+        scores = torch.zeros((HC, stride), dtype=torch.float32, device=dev)
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=batch.queries,
+                          beacons=batch.beacons, counts=batch.counts, window=W, bonus=wl.bonus,
+                          scores_out=scores, keep_out=keep, score_stride=stride, status=status,
+                          check=False, shared_positions=True)
+    else:
+        rid = torch.arange(R, dtype=torch.int64, device=dev)
+        pss = torch.full((R,), 2001, dtype=torch.int32, device=dev)
+        scores = torch.zeros((L * R, stride), dtype=torch.int32, device=dev)
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed, request_ids=rid,
+                          pass_idx=pss, scores_out=scores, keep_out=keep, score_stride=stride,
+                          status=status, check=False, shared_positions=True)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    kn = keep.cpu().numpy()
+    for u in sample:
+        layer, r = u // R, u % R
+        n, p = int(N[r]), int(P[r])
+        say("full size shared unit", u, "layer", layer, "request", r)
+        kp = keep_rows(kn[u])
+        if selector == "beacon":
+            rows = scores[u * H:(u + 1) * H, : n - p].cpu().numpy().astype(np.float64)
+            assert np.array_equal(kp, oracle.shared_select(rows, n, p, B)), u
+        else:
+            draw = oracle.random_score(wl.seed, r, 2001, layer, 0, n, p)
+            assert np.array_equal(scores[u, : n - p].cpu().numpy().view(np.uint32), draw), u
+            assert np.array_equal(kp, oracle.shared_select(draw[None], n, p, B)), u
+        for h in range(H):
+            ko = gather_head(batch.k_pools[layer], bt[r], h, n)
+            vo = gather_head(batch.v_pools[layer], bt[r], h, n)
+            k0, v0 = before[u][h]
+            assert np.array_equal(ko[: len(kp)], oracle.kv_compact(k0, kp)), (u, h)
+            assert np.array_equal(vo[: len(kp)], oracle.kv_compact(v0, kp)), (u, h)

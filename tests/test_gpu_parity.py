@@ -314,15 +314,19 @@ def test_beacon_score_one_shot_long():
 
 
 # ------------------------------------------------------------------ whole pass
-def _pass_case(wl, N, P, B, selector, seed=17):
+def _pass_case(wl, N, P, B, selector, seed=17, shared=False):
+    """One bkv_evict_pass against the oracle.  shared=True: one selection per
+    (layer, request) for all its heads (beacon: merged per-head scores;
+    random: one draw row with the head field 0)."""
     batch = synth.make_batch(wl)
     cache = device_cache(batch, N, P)
     k_in, v_in = host_pools(cache)
     bt = batch.block_table.numpy()
+    L, R, H = cache.n_layers, cache.n_requests, cache.n_kv_heads
     HC, S = cache.n_head_caches, cache.max_slots
     pos = np.tile(np.arange(S, dtype=np.int32), (HC, 1))
     pos_dev = torch.from_numpy(pos).cuda()
-    keep = torch.full((HC, B), -7, dtype=torch.int32).cuda()
+    keep = torch.full((L * R if shared else HC, B), -7, dtype=torch.int32).cuda()
     if selector == "beacon":
         q, b, c = batch.queries.cuda(), batch.beacons.cuda(), batch.counts.cuda()
         T, G = q.shape[1], q.shape[2]
@@ -330,47 +334,82 @@ def _pass_case(wl, N, P, B, selector, seed=17):
         sc = torch.zeros((HC, S)).cuda()
         bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
                           window=64, bonus=1.0, assign=assign, pos_ids=pos_dev, scores_out=sc,
-                          keep_out=keep)
+                          keep_out=keep, shared_positions=shared)
     else:
         rid = torch.arange(100, 100 + cache.n_requests, dtype=torch.int64).cuda()
         pss = torch.full((cache.n_requests,), 4, dtype=torch.int32).cuda()
-        sc = torch.zeros((HC, S), dtype=torch.int32).cuda()
+        sc = torch.zeros((L * R if shared else HC, S), dtype=torch.int32).cuda()
         bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=seed, request_ids=rid,
-                          pass_idx=pss, pos_ids=pos_dev, scores_out=sc, keep_out=keep)
+                          pass_idx=pss, pos_ids=pos_dev, scores_out=sc, keep_out=keep,
+                          shared_positions=shared)
     torch.cuda.synchronize()
     k_out, v_out = host_pools(cache)
     kn, scn, posn = keep.cpu().numpy(), sc.cpu().numpy(), pos_dev.cpu().numpy()
     qb = synth.bits(batch.queries)
     mism = 0
+    keys, vals, kept = {}, {}, {}
+    for layer in range(L):
+        for r in range(R):
+            n, p = N[r], P[r]
+            hcs = [hc_index(R, H, layer, r, h) for h in range(H)]
+            for h, hc in enumerate(hcs):
+                keys[hc] = oracle.gather_paged(k_in[layer], bt[r], h, n)
+                vals[hc] = oracle.gather_paged(v_in[layer], bt[r], h, n)
+            if selector == "beacon":
+                os_, gs = [], []
+                for hc in hcs:
+                    ob, oc, gap = oracle.beacon_update_forced(qb[hc], batch.beacons[hc].numpy(),
+                                                              batch.counts[hc].numpy(),
+                                                              assign[hc].cpu().numpy())
+                    assert gap.max() <= ASSIGN_TOL, hc
+                    assert np.array_equal(ob.view(np.int32), b[hc].cpu().numpy().view(np.int32))
+                    assert np.array_equal(oc, c[hc].cpu().numpy()), hc
+                    o, _ = oracle.beacon_score(keys[hc], ob, oc, p, 64, 1.0)
+                    check_scores(scn[hc, :n - p], o, f"pass hc {hc}")
+                    os_.append(o)
+                    gs.append(scn[hc, :n - p].astype(np.float64))
+                if shared:
+                    u = layer * R + r
+                    kp = keep_rows(kn[u])
+                    ref = oracle.shared_select(np.stack(os_), n, p, B)
+                    merged = np.max(np.stack(os_), axis=0)
+                    mism += check_selection(kp, ref, merged, n, p, B, f"shared pass {u}")
+                    assert np.array_equal(kp, oracle.shared_select(np.stack(gs), n, p, B)), u
+                    for hc in hcs:
+                        kept[hc] = kp
+                else:
+                    for hc, o, g in zip(hcs, os_, gs):
+                        kp = keep_rows(kn[hc])
+                        ref = oracle.topk_select(o, n, p, B)
+                        mism += check_selection(kp, ref, o, n, p, B, f"pass hc {hc}")
+                        assert np.array_equal(kp, oracle.topk_select(g, n, p, B)), hc
+                        kept[hc] = kp
+            else:
+                if shared:
+                    u = layer * R + r
+                    draw = oracle.random_score(seed, 100 + r, 4, layer, 0, n, p)
+                    assert np.array_equal(scn[u, :n - p].view(np.uint32), draw), u
+                    kp = keep_rows(kn[u])
+                    assert np.array_equal(kp, oracle.shared_select(draw[None], n, p, B)), u
+                    for hc in hcs:
+                        kept[hc] = kp
+                else:
+                    for h, hc in enumerate(hcs):
+                        draw = oracle.random_score(seed, 100 + r, 4, layer, h, n, p)
+                        assert np.array_equal(scn[hc, :n - p].view(np.uint32), draw), hc
+                        kp = keep_rows(kn[hc])
+                        assert np.array_equal(kp, oracle.topk_select(draw, n, p, B)), hc
+                        kept[hc] = kp
     for hc, layer, r, h in head_iter(cache):
-        keys = oracle.gather_paged(k_in[layer], bt[r], h, N[r])
-        vals = oracle.gather_paged(v_in[layer], bt[r], h, N[r])
-        kp = keep_rows(kn[hc])
-        if selector == "beacon":
-            ob, oc, gap = oracle.beacon_update_forced(qb[hc], batch.beacons[hc].numpy(),
-                                                      batch.counts[hc].numpy(),
-                                                      assign[hc].cpu().numpy())
-            assert gap.max() <= ASSIGN_TOL, hc
-            assert np.array_equal(ob.view(np.int32), b[hc].cpu().numpy().view(np.int32)), hc
-            assert np.array_equal(oc, c[hc].cpu().numpy()), hc
-            os_, _ = oracle.beacon_score(keys, ob, oc, P[r], 64, 1.0)
-            gs = scn[hc, :N[r] - P[r]]
-            check_scores(gs, os_, f"pass hc {hc}")
-            ref = oracle.topk_select(os_, N[r], P[r], B)
-            mism += check_selection(kp, ref, os_, N[r], P[r], B, f"pass hc {hc}")
-            own = oracle.topk_select(gs.astype(np.float64), N[r], P[r], B)
-            assert np.array_equal(kp, own), hc
-        else:
-            u = oracle.random_score(seed, 100 + r, 4, layer, h, N[r], P[r])
-            assert np.array_equal(scn[hc, :N[r] - P[r]].view(np.uint32), u), hc
-            assert np.array_equal(kp, oracle.topk_select(u, N[r], P[r], B)), hc
+        kp = kept[hc]
         nk = len(kp)
         ko = oracle.gather_paged(k_out[layer], bt[r], h, N[r])
         vo = oracle.gather_paged(v_out[layer], bt[r], h, N[r])
-        assert np.array_equal(ko[:nk], oracle.kv_compact(keys, kp)), hc
-        assert np.array_equal(vo[:nk], oracle.kv_compact(vals, kp)), hc
+        assert np.array_equal(ko[:nk], oracle.kv_compact(keys[hc], kp)), hc
+        assert np.array_equal(vo[:nk], oracle.kv_compact(vals[hc], kp)), hc
         assert np.array_equal(posn[hc, :nk], kp), hc
-    say(selector, "selection differences at boundary ties:", mism)
+    say(selector, "shared" if shared else "per head", "selection differences at boundary ties:",
+        mism)
 
 
 @pytest.mark.parametrize("selector", ["beacon", "random"])
@@ -378,6 +417,63 @@ def test_evict_pass_end_to_end(selector):
     say("pass", selector)
     wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=512, prompt_len=200, seq_len=576)
     _pass_case(wl, N=[576, 541, 400], P=[200, 333, 100], B=512, selector=selector)
+
+
+@pytest.mark.parametrize("selector", ["beacon", "random"])
+def test_evict_pass_shared_positions(selector):
+    say("pass shared", selector)
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=4, budget=512, prompt_len=200, seq_len=576)
+    _pass_case(wl, N=[576, 541, 400], P=[200, 333, 100], B=512, selector=selector, shared=True)
+
+
+def test_shared_select_standalone_entry_points():
+    """bkv_random_score(shared) -> bkv_topk_select_shared -> bkv_kv_compact(keep_shared),
+    and per-head fp32 scores merged over heads, with ties and the N <= B / P == B cases."""
+    say("shared standalone")
+    wl = small(n_layers=2, n_requests=4, n_kv_heads=4, budget=512, prompt_len=200, seq_len=700)
+    batch = synth.make_batch(wl)
+    N, P, B = [700, 512, 600, 300], [200, 512, 0, 100], 512
+    cache = device_cache(batch, N, P)
+    L, R, H = cache.n_layers, cache.n_requests, cache.n_kv_heads
+    stride = 700
+    rid = torch.arange(4, dtype=torch.int64).cuda() * 3 + 1
+    pss = torch.tensor([2, 0, 9, 4], dtype=torch.int32).cuda()
+    u = torch.full((L * R, stride), -1, dtype=torch.int32).cuda()
+    bk.bkv_random_score(cache, 77, rid, pss, u, shared=True)
+    keep = torch.full((L * R, B), -7, dtype=torch.int32).cuda()
+    bk.bkv_topk_select_shared(cache, u, B, keep)
+    un, kn = u.cpu().numpy().view(np.uint32), keep.cpu().numpy()
+    for layer in range(L):
+        for r in range(R):
+            i = layer * R + r
+            draw = oracle.random_score(77, int(rid[r]), int(pss[r]), layer, 0, N[r], P[r])
+            assert np.array_equal(un[i, :N[r] - P[r]], draw), i
+            assert np.array_equal(keep_rows(kn[i]), oracle.shared_select(draw[None], N[r], P[r],
+                                                                          B)), i
+    # per-head fp32 scores with heavy ties, merged by their maximum over the heads
+    rng = np.random.default_rng(11)
+    f = (np.round(rng.random((cache.n_head_caches, stride)) * 5) / 5).astype(np.float32)
+    f[:, ::9] += 1.0
+    bk.bkv_topk_select_shared(cache, torch.from_numpy(f).cuda(), B, keep)
+    kn = keep.cpu().numpy()
+    for layer in range(L):
+        for r in range(R):
+            i = layer * R + r
+            rows = f[i * H:(i + 1) * H, :N[r] - P[r]].astype(np.float64)
+            assert np.array_equal(keep_rows(kn[i]), oracle.shared_select(rows, N[r], P[r], B)), i
+    # compaction applies the one list to every head
+    k_in, v_in = host_pools(cache)
+    bk.bkv_kv_compact(cache, keep, B, keep_shared=True)
+    k_out, v_out = host_pools(cache)
+    bt = batch.block_table.numpy()
+    for hc, layer, r, h in head_iter(cache):
+        kp = keep_rows(kn[layer * R + r])
+        a = oracle.gather_paged(k_in[layer], bt[r], h, N[r])
+        o = oracle.gather_paged(k_out[layer], bt[r], h, N[r])
+        assert np.array_equal(o[:len(kp)], oracle.kv_compact(a, kp)), hc
+        a = oracle.gather_paged(v_in[layer], bt[r], h, N[r])
+        o = oracle.gather_paged(v_out[layer], bt[r], h, N[r])
+        assert np.array_equal(o[:len(kp)], oracle.kv_compact(a, kp)), hc
 
 
 def test_evict_pass_tiny_one_shot():
