@@ -350,6 +350,94 @@ int oracle_shared_select(int H, int N, int P, int B, const double* scores, int32
     return n;
 }
 
+/* Page retention (Random Attention article, section "发现二": keeping
+ * contiguous blocks of 1 to 64 tokens instead of scattered tokens leaves
+ * accuracy almost unchanged, and so does forcing all heads onto one common
+ * set of positions).  Reading taken here: the retained unit is a whole cache
+ * page of `page` slots, chosen once per request for every layer and head, so
+ * the cache shrinks by dropping pages from the request's block table.
+ *   - page j covers slots [j*page, min((j+1)*page, N)); npages = ceil(N/page);
+ *   - pages holding a prompt slot (j*page < P) and a partial last page
+ *     (N mod page != 0) are always kept;
+ *   - a page's score is the largest score of any of its candidate slots in
+ *     any of the n_rows score rows of the request;
+ *   - Bp = B / page pages survive: the forced pages plus the best remaining
+ *     pages by (score descending, page ascending); npages <= Bp keeps all;
+ *     forced pages > Bp is refused (-1).
+ * scores is [n_rows][N - P] row-major.  keep_pages receives the kept page
+ * indices in ascending order; returns their count. */
+int oracle_page_select(int n_rows, int N, int P, int B, int page, const double* scores,
+                       int32_t* keep_pages) {
+    if (n_rows < 1 || page < 1 || P < 0 || N < P || B < 0) return -1;
+    const int m = N - P;
+    const int npages = (N + page - 1) / page;
+    const int Bp = B / page;
+    if (npages <= Bp) {
+        for (int j = 0; j < npages; ++j) keep_pages[j] = j;
+        return npages;
+    }
+    unsigned char* forced = (unsigned char*)calloc((size_t)(npages ? npages : 1), 1);
+    int n_forced = 0;
+    for (int j = 0; j < npages; ++j) {
+        const int last_partial = (j == npages - 1) && (N % page != 0);
+        if ((long)j * page < P || last_partial) {
+            forced[j] = 1;
+            ++n_forced;
+        }
+    }
+    if (n_forced > Bp) {
+        free(forced);
+        return -1;
+    }
+    cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)npages);
+    int nc = 0;
+    for (int j = 0; j < npages; ++j) {
+        if (forced[j]) continue;
+        double best = -INFINITY;
+        for (int n = j * page; n < (j + 1) * page && n < N; ++n)
+            for (int r = 0; r < n_rows; ++r) {
+                const double v = scores[(size_t)r * m + (n - P)];
+                if (v > best) best = v;
+            }
+        c[nc].score = best;
+        c[nc].slot = j;
+        ++nc;
+    }
+    qsort(c, (size_t)nc, sizeof(cand_t), cand_order);
+    unsigned char* kept = forced;  /* forced pages, then the best candidates */
+    for (int i = 0; i < Bp - n_forced; ++i) kept[c[i].slot] = 1;
+    int o = 0;
+    for (int j = 0; j < npages; ++j)
+        if (kept[j]) keep_pages[o++] = j;
+    free(c);
+    free(forced);
+    return o;
+}
+
+/* The block-table rewrite that page retention replaces compaction with: the
+ * kept pages' blocks move to the front in page order, the dropped pages'
+ * blocks are released (ascending page order), and the new length counts the
+ * valid slots of the kept pages.  Returns the new N. */
+int oracle_page_remap(int N, int page, const int32_t* block_row, int n_keep,
+                      const int32_t* keep_pages, int32_t* new_row, int32_t* freed,
+                      int32_t* n_freed) {
+    const int npages = (N + page - 1) / page;
+    unsigned char* kept = (unsigned char*)calloc((size_t)(npages ? npages : 1), 1);
+    int new_n = 0;
+    for (int i = 0; i < n_keep; ++i) {
+        const int j = keep_pages[i];
+        kept[j] = 1;
+        new_row[i] = block_row[j];
+        new_n += ((j + 1) * page <= N) ? page : N - j * page;
+    }
+    int f = 0;
+    for (int j = 0; j < npages; ++j)
+        if (!kept[j]) freed[f++] = block_row[j];
+    *n_freed = f;
+    free(kept);
+    return new_n;
+}
+
 /* ------------------------------------------------------------------ */
 /* Compaction                                                          */
 /* ------------------------------------------------------------------ */

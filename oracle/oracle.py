@@ -12,7 +12,7 @@ nearest-beacon assignment and incremental beacon update; the Random Attention
 article (aiinking.com), section "Random Attention: 不判断重要性, 只随机保留",
 for prompt protection and per-head top-K of random scores, section "发现四"
 for the shared compaction step, and section "发现二" for one common set of
-positions shared by all heads.  Rules the pages leave open follow the readings
+positions shared by all heads, and for retaining contiguous blocks (pages).  Rules the pages leave open follow the readings
 fixed for this build (listed in the design notes of the repository).
 """
 from __future__ import annotations
@@ -72,6 +72,10 @@ def lib():
         L.oracle_topk_select.restype = i32
         L.oracle_shared_select.argtypes = [i32, i32, i32, i32, P, P]
         L.oracle_shared_select.restype = i32
+        L.oracle_page_select.argtypes = [i32, i32, i32, i32, i32, P, P]
+        L.oracle_page_select.restype = i32
+        L.oracle_page_remap.argtypes = [i32, i32, P, i32, P, P, P, P]
+        L.oracle_page_remap.restype = i32
         L.oracle_kv_compact.argtypes = [i32, P, i64, P, P]
         L.oracle_kv_compact.restype = None
         L.oracle_num_threads.argtypes = []
@@ -198,6 +202,39 @@ def shared_select(scores, N, P, B):
     if n < 0:
         raise ValueError(f"selection refused: P={P} exceeds budget B={B} or bad lengths")
     return keep[:n]
+
+
+def page_select(scores, N, P, B, page=16):
+    """Pages kept for one request: scores[n_rows][N-P] are all its score rows
+    (every layer and head, or one shared draw row).  Prompt pages and a partial
+    last page are always kept; a page's score is the largest of its slots'
+    scores over all rows; B // page pages survive."""
+    s = np.asarray(scores).astype(np.float64)
+    if s.ndim == 1:
+        s = s[None, :]
+    s = _c(s, np.float64)
+    assert s.shape[1] == N - P
+    npages = (N + page - 1) // page
+    keep = np.zeros(max(npages, 1), np.int32)
+    n = lib().oracle_page_select(s.shape[0], int(N), int(P), int(B), int(page),
+                                 _ptr(s) if s.size else None, _ptr(keep))
+    if n < 0:
+        raise ValueError(f"page selection refused: forced pages exceed B // page (P={P}, B={B})")
+    return keep[:n]
+
+
+def page_remap(block_row, N, keep_pages, page=16):
+    """(new block row, released blocks, new N) after keeping keep_pages."""
+    row = _c(block_row, np.int32)
+    kp = _c(keep_pages, np.int32)
+    npages = (N + page - 1) // page
+    new_row = np.zeros(max(len(kp), 1), np.int32)
+    freed = np.zeros(max(npages, 1), np.int32)
+    nf = ctypes.c_int32(0)
+    new_n = lib().oracle_page_remap(int(N), int(page), _ptr(row), len(kp),
+                                    _ptr(kp) if len(kp) else None, _ptr(new_row), _ptr(freed),
+                                    ctypes.byref(nf))
+    return new_row[:len(kp)], freed[:nf.value], int(new_n)
 
 
 # ---------------------------------------------------------------- compaction

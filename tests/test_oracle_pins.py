@@ -5,6 +5,7 @@ rational arithmetic, exhaustive enumeration or hand-computed values, chosen so
 that a plausible slip (dropped term, wrong sign or index, transposed operand,
 off-by-one count) fails at least one of them.
 """
+import itertools
 import math
 
 import numpy as np
@@ -435,6 +436,107 @@ def test_shared_select_reduces_to_per_head_selection():
     assert list(oracle.shared_select(np.ones((3, 5)), 8, 3, 10)) == list(range(8))   # N <= B
     with pytest.raises(ValueError):
         oracle.shared_select(np.ones((3, 5)), 8, 3, 2)                             # P > B
+
+
+# --------------------------------------------------------------- page retention
+def test_page_select_hand_computed():
+    # page 4, N 18, P 5: pages [0,4) [4,8) [8,12) [12,16) [16,18).  Pages 0 and 1
+    # hold prompt slots and page 4 is a partial last page: all three are kept.
+    # B 16 -> 4 pages, so one of pages 2 and 3 survives.  Row 0 peaks in page 2
+    # at 0.7, row 1 in page 3 at 0.8: the largest slot score over both rows
+    # keeps page 3 (a page mean, or row 0 alone, would keep page 2).
+    N, P = 18, 5
+    s = np.zeros((2, N - P))
+    s[0, 8 - P:12 - P] = [0.1, 0.7, 0.1, 0.1]
+    s[0, 12 - P:16 - P] = [0.2, 0.2, 0.2, 0.2]
+    s[1, 8 - P:12 - P] = [0.3, 0.3, 0.3, 0.3]
+    s[1, 12 - P:16 - P] = [0.0, 0.0, 0.8, 0.0]
+    s[0, 16 - P] = 0.99
+    kp = oracle.page_select(s, N, P, 16, page=4)
+    assert list(kp) == [0, 1, 3, 4]
+    row, freed, n = oracle.page_remap([40, 41, 42, 43, 44], N, kp, page=4)
+    assert list(row) == [40, 41, 43, 44] and list(freed) == [42] and n == 4 + 4 + 4 + 2
+    # equal page scores: the earlier page wins
+    s[1, 12 - P:16 - P] = [0.0, 0.0, 0.7, 0.0]
+    assert list(oracle.page_select(s, N, P, 16, page=4)) == [0, 1, 2, 4]
+
+
+def test_page_select_with_unit_pages_is_the_shared_selection():
+    for trial in range(10):
+        H, N, P = int(RNG.integers(1, 4)), int(RNG.integers(50, 300)), int(RNG.integers(0, 40))
+        B = int(RNG.integers(P, N))
+        s = RNG.random((H, N - P))
+        assert np.array_equal(oracle.page_select(s, N, P, B, page=1),
+                              oracle.shared_select(s, N, P, B)), trial
+
+
+def test_page_select_matches_exhaustive_dominance():
+    for trial in range(40):
+        page = int(RNG.choice([2, 3, 4]))
+        rows = int(RNG.integers(1, 4))
+        N = int(RNG.integers(6, 30))
+        P = int(RNG.integers(0, N // 2))
+        npages = -(-N // page)
+        forced = [j for j in range(npages) if j * page < P or (j == npages - 1 and N % page)]
+        cands = [j for j in range(npages) if j not in forced]
+        if not cands:
+            continue
+        Bp = len(forced) + int(RNG.integers(0, len(cands)))
+        s = RNG.integers(0, 3, (rows, N - P)).astype(np.float64) if trial % 2 else \
+            RNG.random((rows, N - P))
+        # page score written out: max over rows and the page's candidate slots
+        ps = []
+        for j in cands:
+            ps.append(max(s[r][n - P] for r in range(rows)
+                          for n in range(j * page, min((j + 1) * page, N))))
+        k = Bp - len(forced)
+        found = []
+        for S in itertools.combinations(range(len(cands)), k):
+            inside = set(S)
+            beats = lambda a, b: ps[a] > ps[b] or (ps[a] == ps[b] and a < b)   # noqa: E731
+            if all(beats(a, b) for a in S for b in range(len(cands)) if b not in inside):
+                found.append(sorted(forced + [cands[i] for i in S]))
+        assert len(found) == 1
+        kp = oracle.page_select(s, N, P, Bp * page, page=page)
+        assert list(kp) == found[0], (trial, list(kp), found)
+
+
+def test_page_select_edge_cases_and_remap_invariants():
+    s = RNG.random((3, 100 - 20))
+    # everything fits: all pages kept, nothing released
+    kp = oracle.page_select(s, 100, 20, 112, page=16)
+    assert list(kp) == list(range(7))
+    # prompt pages plus the partial last page exceed the budget: refused
+    with pytest.raises(ValueError):
+        oracle.page_select(s, 100, 20, 32, page=16)      # 2 prompt + 1 partial > 2
+    assert list(oracle.page_select(s, 100, 20, 48, page=16)) == [0, 1, 6]
+    # steady state of the serving shape: 132 pages, 128 kept
+    N, P, B = 2112, 1024, 2048
+    s = RNG.random((288, N - P))
+    kp = oracle.page_select(s, N, P, B, page=16)
+    assert len(kp) == B // 16 and np.all(np.diff(kp) > 0)
+    assert np.array_equal(kp[:64], np.arange(64))
+    block_row = RNG.permutation(5000)[:132].astype(np.int32)
+    row, freed, n = oracle.page_remap(block_row, N, kp, page=16)
+    assert n == B and len(freed) == 4
+    assert sorted(np.concatenate([row, freed]).tolist()) == sorted(block_row.tolist())
+    assert np.array_equal(row, block_row[kp])
+
+
+def test_random_page_retention_is_uniform_over_pages():
+    # one shared draw row per request: the page score is the largest of 16
+    # independent uniform draws, so every candidate page is equally likely
+    # to survive ((Bp - forced) / candidates each)
+    N, P, B, trials = 512, 64, 256, 4000
+    hits = np.zeros(N // 16)
+    for t in range(trials):
+        u = oracle.random_score(3, t, 0, 0, 0, N, P)
+        hits[oracle.page_select(u[None], N, P, B, page=16)] += 1
+    cand = hits[P // 16:] / trials
+    expect = (B // 16 - P // 16) / (N // 16 - P // 16)
+    sd = math.sqrt(expect * (1 - expect) / trials)
+    assert np.all(hits[:P // 16] == trials)
+    assert np.all(np.abs(cand - expect) < 5 * sd), (cand, expect)
 
 
 # --------------------------------------------------------------- compaction
