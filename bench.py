@@ -43,10 +43,10 @@ def source_hash(*paths):
 
 
 def kernel_source_hash(kernel):
-    """Hash of a kernel's source file and the shared device header."""
+    """Hash of a kernel's source file and the shared device headers."""
     csrc = os.path.join(ROOT, "decode_kv_cache_beacon_amd", "csrc")
     return source_hash(os.path.join(csrc, KERNEL_SOURCES[kernel]),
-                       os.path.join(csrc, "bkv_internal.h"))
+                       os.path.join(csrc, "bkv_internal.h"), os.path.join(csrc, "select_util.h"))
 
 
 KERNEL_SOURCES = {
@@ -55,6 +55,7 @@ KERNEL_SOURCES = {
     "topk_select": "topk_select.hip",
     "kv_compact": "kv_compact.hip",
     "random_score": "random_score.hip",
+    "page_retain": "page_retain.hip",
 }
 
 
@@ -153,6 +154,7 @@ KERNEL_SYMBOLS = {
     "topk_select_kernel": "topk_select",
     "kv_compact_kernel": "kv_compact",
     "random_score_kernel": "random_score",
+    "page_retain_kernel": "page_retain",
 }
 COPY_SYMBOL = "__amd_rocclr_copyBuffer"
 PROFILE_CMDS = {
@@ -161,7 +163,7 @@ PROFILE_CMDS = {
               "--no-shared --count-cap 0"),
     "pmc": ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} -f csv -d <pmc-dir>/{c} -o {c} -- "
             "python3 <repo>/bench.py --steps 2 --warmup 0 --no-random --no-cpu-baseline "
-            "--no-shared --count-cap 0"),
+            "--no-shared --no-pages --count-cap 0"),
     "summary": "python bench.py --summarize-profiles <prof-dir> <pmc-dir>",
 }
 
@@ -188,8 +190,10 @@ def summarize_profiles(prof_dir, pmc_dir, workload):
     os.makedirs(out, exist_ok=True)
     lines = [f"# Kernel durations, workload {workload}", "",
              "rocprofv3 kernel trace of one benchmark run (5 timed + 1 warm-up beacon passes, "
-             "then the same number of random-selector passes; top-B selection and compaction "
-             "run in both).", "", "Command:", "", "    " + PROFILE_CMDS["trace"], "",
+             "then the same number of random-selector passes, then as many page-retention "
+             "passes of each selector; top-B selection and compaction run in the first two, "
+             "maintenance and scoring also in the page-retention beacon passes).", "",
+             "Command:", "", "    " + PROFILE_CMDS["trace"], "",
              "| kernel | launches | mean ms | min ms | max ms |", "|---|---|---|---|---|"]
     for k in KERNEL_SOURCES:
         if k in dur:
@@ -262,6 +266,8 @@ def main():
     ap.add_argument("--workload", default="serving_r128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-random", action="store_true", help="skip the random-selector A/B")
+    ap.add_argument("--no-pages", action="store_true",
+                    help="skip the page-retention (whole pages, no row moves) passes")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-position (one selection per layer and request) passes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -502,6 +508,68 @@ def main():
         shared["note"] = ("one keep list per (layer, request) for all KV heads: beacon scores "
                           "merged by their maximum over heads, random draws one row")
         result["shared_positions"] = shared
+
+    # page retention: whole pages per request, the block table rewritten in
+    # place instead of moving rows; between passes (untimed) the released
+    # blocks take the next 64 appended tokens, as an allocator would hand them out
+    if not args.no_pages:
+        Bp, npages = B // synth.BLOCK, (B + W) // synth.BLOCK
+        bt0 = cache.block_table.clone()
+        kp_pages = torch.zeros((R, Bp), dtype=torch.int32, device=dev)
+        freed = torch.zeros((R, cache.max_blocks), dtype=torch.int32, device=dev)
+        rid = torch.arange(R, dtype=torch.int64, device=dev)
+        pss = torch.zeros(R, dtype=torch.int32, device=dev)
+        ur = torch.zeros((R, stride), dtype=torch.int32, device=dev)
+        seq0 = cache.seq_len.clone()
+
+        def append_tail():
+            tb = cache.block_table[:, Bp:npages].long()
+            for layer, (fk, fv) in enumerate(fresh):
+                cache.k_pools[layer][tb] = fk
+                cache.v_pools[layer][tb] = fv
+
+        pages = {}
+        for sel in ("beacon", "random"):
+            n_ev = 4 if sel == "beacon" else 3
+            runs = []
+            for s in range(args.warmup + args.steps):
+                append_tail()
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+                outs = (cache.block_table, cache.seq_len, freed)
+                if sel == "beacon":
+                    bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b,
+                                      counts=c, window=W, bonus=wl.bonus, scores_out=scores,
+                                      keep_out=kp_pages, score_stride=stride, status=status,
+                                      check=False, timing_events=ev, page_retention=outs)
+                else:
+                    pss.fill_(s + 3000)
+                    bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed,
+                                      request_ids=rid, pass_idx=pss, scores_out=ur,
+                                      keep_out=kp_pages, score_stride=stride, status=status,
+                                      check=False, timing_events=ev, page_retention=outs)
+                if s >= args.warmup:
+                    runs.append(ev)
+                # the released blocks become the tail pages again; the length returns to B + W
+                cache.block_table[:, Bp:npages] = freed[:, :npages - Bp]
+                cache.seq_len.copy_(seq0)
+            torch.cuda.synchronize()
+            bk.check_status(status, f"page-retention {sel} passes")
+            kn_ = (["beacon_update", "beacon_score"] if sel == "beacon" else ["random_score"]) + \
+                ["page_retain"]
+            tpass = sum(e[0].elapsed_time(e[-1]) for e in runs) / len(runs)
+            kms_ = {n: round(sum(e[i].elapsed_time(e[i + 1]) for e in runs) / len(runs), 4)
+                    for i, n in enumerate(kn_)}
+            rows_read = HC if sel == "beacon" else R
+            pbytes = rows_read * stride * 4 + R * (2 * cache.max_blocks * 4 + Bp * 4 + 4)
+            pages[sel] = {"passes_per_s": round(1000.0 / tpass, 3), "ms": round(tpass, 4),
+                          "kernel_ms": kms_,
+                          "page_retain_algorithmic_bytes": int(pbytes),
+                          "page_retain_gbps": round(pbytes / (kms_["page_retain"] * 1e-3) / 1e9, 1)}
+        pages["note"] = ("whole 16-slot pages kept once per request for every layer and head; "
+                         "the block table is rewritten in place and no K/V row moves")
+        result["page_retention"] = pages
+        cache.block_table.copy_(bt0)
+        cache.seq_len.copy_(seq0)
 
     # beacon forgetting: the maintenance kernel with a count cap (moving
     # average once a row is full), timed alone on the same queries and state

@@ -24,11 +24,12 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
-BKV_ABI_VERSION = 3
+BKV_ABI_VERSION = 4
 BKV_OK, BKV_ERR_NULL, BKV_ERR_INVALID, BKV_ERR_BUDGET, BKV_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BKV_ERR_WORKSPACE, BKV_ERR_HIP, BKV_ERR_LENGTH, BKV_ERR_BLOCK_TABLE = 5, 6, 7, 8
 BKV_SCORE_F32, BKV_SCORE_U32 = 0, 1
 BKV_SELECT_BEACON, BKV_SELECT_RANDOM = 0, 1
+BKV_ROWS_PER_HEAD, BKV_ROWS_PER_LAYER_REQUEST, BKV_ROWS_PER_REQUEST = 0, 1, 2
 BKV_MAX_BEACONS = 256
 BKV_MAX_CANDIDATES = 32768
 HEAD_DIM = 128
@@ -50,6 +51,8 @@ class bkv_cache(ctypes.Structure):
 class bkv_pass_args(ctypes.Structure):
     _fields_ = [
         ("selector", _i32), ("budget", _i32), ("score_stride", _i32), ("shared_positions", _i32),
+        ("page_retention", _i32), ("block_table_out", _P), ("seq_len_out", _P),
+        ("freed_blocks", _P),
         ("n_beacons", _i32), ("T", _i32), ("G", _i32), ("window", _i32), ("bonus", _f32),
         ("queries", _P), ("beacons", _P), ("counts", _P), ("assign", _P), ("count_cap", _i32),
         ("lse", _P),
@@ -78,6 +81,9 @@ _lib.bkv_topk_select_shared.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i3
 _lib.bkv_topk_select_shared.restype = _i32
 _lib.bkv_kv_compact.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i32, _P, _i32, _P, _P]
 _lib.bkv_kv_compact.restype = _i32
+_lib.bkv_page_retain.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i32, _i32, _i32, _P, _P, _P,
+                                 _P, _P, _P]
+_lib.bkv_page_retain.restype = _i32
 _lib.bkv_workspace_size.argtypes = [ctypes.POINTER(bkv_cache), ctypes.POINTER(bkv_pass_args),
                                     ctypes.POINTER(_sz)]
 _lib.bkv_workspace_size.restype = _i32
@@ -87,7 +93,7 @@ _lib.bkv_evict_pass.restype = _i32
 
 EXPORTS = ("bkv_abi_version", "bkv_status_string", "bkv_beacon_update", "bkv_beacon_score",
            "bkv_random_score", "bkv_topk_select", "bkv_topk_select_shared", "bkv_kv_compact",
-           "bkv_workspace_size", "bkv_evict_pass")
+           "bkv_page_retain", "bkv_workspace_size", "bkv_evict_pass")
 
 
 class BkvError(RuntimeError):
@@ -269,12 +275,19 @@ def bkv_beacon_score(cache: PagedCache, beacons, counts, scores, window=64, bonu
     return st
 
 
-def bkv_random_score(cache: PagedCache, seed, request_ids, pass_idx, scores, shared=False,
-                     status=None, check=True, stream=None):
-    """scores uint32 draws (stored in an int32 tensor) [HC, stride], or
-    [n_layers * n_requests, stride] with shared=True (one draw row per layer and request)."""
+def _layout_rows(cache: PagedCache, rows):
+    return {BKV_ROWS_PER_HEAD: cache.n_head_caches,
+            BKV_ROWS_PER_LAYER_REQUEST: cache.n_layers * cache.n_requests,
+            BKV_ROWS_PER_REQUEST: cache.n_requests}[rows]
+
+
+def bkv_random_score(cache: PagedCache, seed, request_ids, pass_idx, scores,
+                     rows=BKV_ROWS_PER_HEAD, status=None, check=True, stream=None):
+    """scores uint32 draws (stored in an int32 tensor) [n_rows, stride]: one row per
+    head-cache, per (layer, request) (shared positions) or per request (page retention)."""
     R = cache.n_requests
-    rows = cache.n_layers * R if shared else cache.n_head_caches
+    layout = int(rows)
+    rows = _layout_rows(cache, layout)
     _need(request_ids, "request_ids", torch.int64, (R,))
     _need(pass_idx, "pass_idx", torch.int32, (R,))
     _need(scores, "scores", torch.int32)
@@ -283,7 +296,7 @@ def bkv_random_score(cache: PagedCache, seed, request_ids, pass_idx, scores, sha
     st, own = _status(status, cache.device)
     c = cache.struct()
     code = _lib.bkv_random_score(ctypes.byref(c), int(seed) & (2**64 - 1), _ptr(request_ids),
-                                 _ptr(pass_idx), int(bool(shared)), _ptr(scores),
+                                 _ptr(pass_idx), layout, _ptr(scores),
                                  scores.shape[1], _ptr(st), _stream(stream))
     _check(code, "bkv_random_score")
     if own and check:
@@ -365,9 +378,38 @@ def bkv_kv_compact(cache: PagedCache, keep, budget, pos_ids=None, status=None, c
     return st
 
 
+def bkv_page_retain(cache: PagedCache, scores, budget, keep_pages, block_table_out, seq_len_out,
+                    freed_blocks, rows=BKV_ROWS_PER_HEAD, status=None, check=True, stream=None):
+    """Whole-page retention, one selection per request for every layer and head.
+
+    scores: fp32 per-head beacon scores [HC, stride] (rows=BKV_ROWS_PER_HEAD) or int32-stored
+    uint32 draws [n_requests, stride] (rows=BKV_ROWS_PER_REQUEST).  keep_pages int32
+    [n_requests, budget // 16]; block_table_out int32 [n_requests, max_blocks] and seq_len_out
+    int32 [n_requests] (either may be the cache's own tensor: rewritten in place);
+    freed_blocks int32 [n_requests, max_blocks]."""
+    R = cache.n_requests
+    kind = _score_kind(scores)
+    _need(scores, "scores", scores.dtype)
+    if scores.dim() != 2 or scores.shape[0] != _layout_rows(cache, rows):
+        raise ValueError("scores rows do not match the row layout")
+    _need(keep_pages, "keep_pages", torch.int32, (R, budget // BLOCK_SIZE))
+    _need(block_table_out, "block_table_out", torch.int32, (R, cache.max_blocks))
+    _need(seq_len_out, "seq_len_out", torch.int32, (R,))
+    _need(freed_blocks, "freed_blocks", torch.int32, (R, cache.max_blocks))
+    st, own = _status(status, cache.device)
+    c = cache.struct()
+    code = _lib.bkv_page_retain(ctypes.byref(c), _ptr(scores), kind, scores.shape[1], int(rows),
+                                int(budget), _ptr(keep_pages), _ptr(block_table_out),
+                                _ptr(seq_len_out), _ptr(freed_blocks), _ptr(st), _stream(stream))
+    _check(code, "bkv_page_retain")
+    if own and check:
+        check_status(st, "bkv_page_retain", stream)
+    return st
+
+
 def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, window, bonus,
                assign, lse, seed, request_ids, pass_idx, pos_ids, scores_out, keep_out,
-               score_stride, count_cap=0, shared_positions=False):
+               score_stride, count_cap=0, shared_positions=False, page_retention=None):
     HC, R = cache.n_head_caches, cache.n_requests
     LR = cache.n_layers * R
     a = bkv_pass_args()
@@ -375,6 +417,13 @@ def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, wi
     a.budget = int(budget)
     a.score_stride = int(score_stride)
     a.shared_positions = int(bool(shared_positions))
+    if page_retention is not None:
+        bto, slo, fr = page_retention
+        _need(bto, "block_table_out", torch.int32, (R, cache.max_blocks))
+        _need(slo, "seq_len_out", torch.int32, (R,))
+        _need(fr, "freed_blocks", torch.int32, (R, cache.max_blocks))
+        a.page_retention = 1
+        a.block_table_out, a.seq_len_out, a.freed_blocks = bto.data_ptr(), slo.data_ptr(), fr.data_ptr()
     if selector == BKV_SELECT_BEACON:
         _need(queries, "queries", torch.bfloat16)
         if queries.dim() != 4 or queries.shape[0] != HC or queries.shape[3] != HEAD_DIM:
@@ -405,11 +454,19 @@ def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, wi
     stride = score_stride if score_stride > 0 else cache.max_slots
     if scores_out is not None:
         want = torch.float32 if selector == BKV_SELECT_BEACON else torch.int32
-        rows = LR if shared_positions and selector == BKV_SELECT_RANDOM else HC
+        rows = HC
+        if selector == BKV_SELECT_RANDOM and page_retention is not None:
+            rows = R
+        elif selector == BKV_SELECT_RANDOM and shared_positions:
+            rows = LR
         _need(scores_out, "scores_out", want, (rows, stride))
         a.scores_out = scores_out.data_ptr()
     if keep_out is not None:
-        _need(keep_out, "keep_out", torch.int32, (LR if shared_positions else HC, budget))
+        if page_retention is not None:
+            shape = (R, budget // BLOCK_SIZE)
+        else:
+            shape = (LR if shared_positions else HC, budget)
+        _need(keep_out, "keep_out", torch.int32, shape)
         a.keep_out = keep_out.data_ptr()
     return a
 
@@ -426,16 +483,19 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
                    counts=None, window=64, bonus=1.0, assign=None, lse=None, seed=0,
                    request_ids=None, pass_idx=None, pos_ids=None, scores_out=None,
                    keep_out=None, score_stride=0, workspace=None, status=None, check=True,
-                   stream=None, timing_events=None, count_cap=0, shared_positions=False):
+                   stream=None, timing_events=None, count_cap=0, shared_positions=False,
+                   page_retention=None):
     """One whole eviction pass (beacon: update -> score -> select -> compact;
     random: score -> select -> compact), every layer/request/head at once.
     shared_positions: one selection per (layer, request) for all its heads.
+    page_retention: (block_table_out, seq_len_out, freed_blocks) to keep whole
+    pages per request instead (no rows move; keep_out is then the kept pages).
 
     timing_events: optional list of torch.cuda.Event(enable_timing=True), 5 for
     the beacon selector and 4 for the random one, recorded around each kernel."""
     a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
                    seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride,
-                   count_cap, shared_positions)
+                   count_cap, shared_positions, page_retention)
     ev_arr = None
     if timing_events is not None:
         handles = []

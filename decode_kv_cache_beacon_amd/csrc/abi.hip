@@ -53,15 +53,31 @@ struct PassLayout {
     size_t scores_off, keep_off, total;
 };
 
-// Rows of the score buffer and of the keep buffer of a pass.  With shared
-// positions the random selector draws one row per (layer, request) and every
-// selector keeps one list per (layer, request); beacon scores stay per head.
+// Row layout of the random selector's draws in a pass: per head-cache, per
+// (layer, request) with shared positions, per request with page retention.
+int random_rows(const bkv_pass_args* a) {
+    return a->page_retention     ? BKV_ROWS_PER_REQUEST
+           : a->shared_positions ? BKV_ROWS_PER_LAYER_REQUEST
+                                 : BKV_ROWS_PER_HEAD;
+}
+size_t layout_rows(const CacheView& v, int rows) {
+    return rows == BKV_ROWS_PER_REQUEST        ? (size_t)v.R
+           : rows == BKV_ROWS_PER_LAYER_REQUEST ? (size_t)v.L * v.R
+                                                : (size_t)v.L * v.R * v.H;
+}
+// Rows of the score buffer and of the keep buffer of a pass (beacon scores
+// are always per head-cache).
 size_t score_rows(const CacheView& v, const bkv_pass_args* a) {
-    const bool one = a->shared_positions && a->selector == BKV_SELECT_RANDOM;
-    return (size_t)v.L * v.R * (one ? 1 : v.H);
+    return a->selector == BKV_SELECT_RANDOM ? layout_rows(v, random_rows(a))
+                                            : layout_rows(v, BKV_ROWS_PER_HEAD);
 }
 size_t keep_rows(const CacheView& v, const bkv_pass_args* a) {
-    return (size_t)v.L * v.R * (a->shared_positions ? 1 : v.H);
+    return a->page_retention     ? (size_t)v.R
+           : a->shared_positions ? (size_t)v.L * v.R
+                                 : (size_t)v.L * v.R * v.H;
+}
+size_t keep_cols(const bkv_pass_args* a) {
+    return a->page_retention ? (size_t)(a->budget / kBlock) : (size_t)a->budget;
 }
 
 int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
@@ -70,6 +86,9 @@ int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     if (stride > BKV_MAX_CANDIDATES) return BKV_ERR_INVALID;
     if (a->budget < 1) return BKV_ERR_INVALID;
     if (a->shared_positions != 0 && a->shared_positions != 1) return BKV_ERR_INVALID;
+    if (a->page_retention != 0 && a->page_retention != 1) return BKV_ERR_INVALID;
+    if (a->page_retention && (a->budget % kBlock != 0 || a->shared_positions))
+        return BKV_ERR_INVALID;
     size_t off = 0;
     L->stride = stride;
     L->scores_off = L->keep_off = 0;
@@ -79,7 +98,7 @@ int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     }
     if (!a->keep_out) {
         L->keep_off = off;
-        off = round_up(off + keep_rows(v, a) * (size_t)a->budget * 4, 256);
+        off = round_up(off + keep_rows(v, a) * keep_cols(a) * 4, 256);
     }
     L->total = off;
     return BKV_OK;
@@ -140,17 +159,18 @@ int32_t bkv_beacon_score(const bkv_cache* cache, const float* beacons, const int
 }
 
 int32_t bkv_random_score(const bkv_cache* cache, uint64_t seed, const uint64_t* request_ids,
-                         const int32_t* pass_idx, int32_t shared, uint32_t* scores,
+                         const int32_t* pass_idx, int32_t rows, uint32_t* scores,
                          int32_t score_stride, int32_t* status, bkv_stream_t stream) {
     CacheView v;
     int32_t e = check_cache(cache, &v);
     if (e) return e;
     if (!request_ids || !pass_idx || !scores) return BKV_ERR_NULL;
-    if (score_stride < 1 || (shared != 0 && shared != 1)) return BKV_ERR_INVALID;
+    if (score_stride < 1 || rows < BKV_ROWS_PER_HEAD || rows > BKV_ROWS_PER_REQUEST)
+        return BKV_ERR_INVALID;
     if (!aligned(request_ids, 8) || !aligned(pass_idx, 4) || !aligned(scores, 4) ||
         (status && !aligned(status, 4)))
         return BKV_ERR_INVALID;
-    return hip_status(launch_random_score(v, seed, request_ids, pass_idx, shared, scores,
+    return hip_status(launch_random_score(v, seed, request_ids, pass_idx, rows, scores,
                                           score_stride, Check{-1, score_stride, 0}, status,
                                           static_cast<hipStream_t>(stream)));
 }
@@ -205,6 +225,28 @@ int32_t bkv_kv_compact(const bkv_cache* cache, const int32_t* keep_idx, int32_t 
                                         static_cast<hipStream_t>(stream)));
 }
 
+int32_t bkv_page_retain(const bkv_cache* cache, const void* scores, int32_t score_kind,
+                        int32_t score_stride, int32_t score_rows, int32_t budget,
+                        int32_t* keep_pages, int32_t* block_table_out, int32_t* seq_len_out,
+                        int32_t* freed_blocks, int32_t* status, bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!scores || !keep_pages || !block_table_out || !seq_len_out || !freed_blocks)
+        return BKV_ERR_NULL;
+    if (score_kind != BKV_SCORE_F32 && score_kind != BKV_SCORE_U32) return BKV_ERR_INVALID;
+    if (score_rows != BKV_ROWS_PER_HEAD && score_rows != BKV_ROWS_PER_REQUEST)
+        return BKV_ERR_INVALID;
+    if (score_stride < 1 || budget < kBlock || budget % kBlock != 0) return BKV_ERR_INVALID;
+    if (!aligned(scores, 4) || !aligned(keep_pages, 4) || !aligned(block_table_out, 4) ||
+        !aligned(seq_len_out, 4) || !aligned(freed_blocks, 4) || (status && !aligned(status, 4)))
+        return BKV_ERR_INVALID;
+    return hip_status(launch_page_retain(v, scores, score_kind, score_stride, score_rows, budget,
+                                         keep_pages, block_table_out, seq_len_out, freed_blocks,
+                                         Check{budget, score_stride, 1, 1}, status,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, size_t* bytes) {
     CacheView v;
     int32_t e = check_cache(cache, &v);
@@ -237,6 +279,13 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
         return BKV_ERR_INVALID;
     const bool beacon = a->selector == BKV_SELECT_BEACON;
     const int shared = a->shared_positions;
+    const bool pages = a->page_retention;
+    if (pages) {
+        if (!a->block_table_out || !a->seq_len_out || !a->freed_blocks) return BKV_ERR_NULL;
+        if (a->pos_ids || !aligned(a->block_table_out, 4) || !aligned(a->seq_len_out, 4) ||
+            !aligned(a->freed_blocks, 4))
+            return BKV_ERR_INVALID;
+    }
     if (beacon) {
         if (!a->queries || !a->beacons || !a->counts) return BKV_ERR_NULL;
         if (a->n_beacons < 1 || a->n_beacons > BKV_MAX_BEACONS || a->T < 1 || a->G < 1 ||
@@ -256,9 +305,9 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
     int32_t* keep = a->keep_out ? a->keep_out : reinterpret_cast<int32_t*>(ws + L.keep_off);
     hipStream_t s = static_cast<hipStream_t>(stream);
     // every kernel applies every check, so a failing request is skipped by all steps
-    const Check all{a->budget, L.stride, 1};
+    const Check all{a->budget, L.stride, 1, pages ? 1 : 0};
     const int HC = (int)head_caches(v);
-    const int n_marks = beacon ? 5 : 4;
+    const int n_marks = (beacon ? 5 : 4) - (pages ? 1 : 0);
     const bool timed = a->timing_events && a->n_timing_events >= n_marks;
     if (timed)
         for (int i = 0; i < n_marks; ++i)
@@ -278,22 +327,31 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
             he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
                                      static_cast<float*>(sc), L.stride, a->lse, all, status, s);
         if (he == hipSuccess) he = mark();
-        if (he == hipSuccess)  // shared: the largest of the H per-head scores
+        if (he == hipSuccess && pages)
+            he = launch_page_retain(v, sc, BKV_SCORE_F32, L.stride, BKV_ROWS_PER_HEAD, a->budget,
+                                    keep, a->block_table_out, a->seq_len_out, a->freed_blocks,
+                                    all, status, s);
+        else if (he == hipSuccess)  // shared: the largest of the H per-head scores
             he = launch_topk_select(v, sc, BKV_SCORE_F32, L.stride, v.H, shared, a->budget, keep,
                                     all, status, s);
     } else {
-        he = launch_random_score(v, a->seed, a->request_ids, a->pass_idx, shared,
+        he = launch_random_score(v, a->seed, a->request_ids, a->pass_idx, random_rows(a),
                                  static_cast<uint32_t*>(sc), L.stride, all, status, s);
         if (he == hipSuccess) he = mark();
-        if (he == hipSuccess)  // shared: one draw row per (layer, request)
+        if (he == hipSuccess && pages)
+            he = launch_page_retain(v, sc, BKV_SCORE_U32, L.stride, BKV_ROWS_PER_REQUEST,
+                                    a->budget, keep, a->block_table_out, a->seq_len_out,
+                                    a->freed_blocks, all, status, s);
+        else if (he == hipSuccess)  // shared: one draw row per (layer, request)
             he = launch_topk_select(v, sc, BKV_SCORE_U32, L.stride, 1, shared, a->budget, keep,
                                     all, status, s);
     }
     if (he == hipSuccess) he = mark();
-    if (he == hipSuccess)
+    if (he == hipSuccess && !pages) {
         he = launch_kv_compact(v, keep, a->budget, shared, a->pos_ids, a->pos_stride, all, status,
                                s);
-    if (he == hipSuccess) he = mark();
+        if (he == hipSuccess) he = mark();
+    }
     return hip_status(he);
 }
 

@@ -48,6 +48,9 @@ struct Check {
     int budget;     // < 0: no budget check
     int cand_cap;   // < 0: no candidate-capacity check (N - P <= cand_cap)
     int blocks;     // non-zero: validate pool alignment and every block id in use
+    int pages;      // non-zero: page retention -- the budget counts whole pages (the prompt
+                    // pages and a partial last page must fit in budget / 16 pages) and, as
+                    // one selection spans every layer, every layer's pools must be aligned
 };
 
 // Validates request r.  Every thread of the block must call it (it
@@ -62,7 +65,20 @@ __device__ inline bool request_ok(const CacheView& c, int layer, int r, const Ch
     if (ck.budget >= 0 && P > ck.budget) err |= 1 << BKV_ERR_BUDGET;
     if (ck.cand_cap >= 0 && !(err & (1 << BKV_ERR_LENGTH)) && N - P > ck.cand_cap)
         err |= 1 << BKV_ERR_LENGTH;
+    if (ck.pages && ck.budget >= 0 && !(err & (1 << BKV_ERR_LENGTH))) {
+        const int npages = (N + kBlock - 1) / kBlock;
+        const int prompt_pages = (P + kBlock - 1) / kBlock;
+        const int forced = prompt_pages + ((N % kBlock) != 0 && npages - 1 >= prompt_pages);
+        if (npages > ck.budget / kBlock && forced > ck.budget / kBlock)
+            err |= 1 << BKV_ERR_BUDGET;
+    }
     bool bad = false;
+    if (ck.pages) {
+        bool mis = false;
+        for (int l = threadIdx.x; l < c.L; l += blockDim.x)
+            mis |= ((c.k_pools[l] | c.v_pools[l]) & 15u) != 0;
+        if (__syncthreads_or(mis)) err |= 1 << BKV_ERR_INVALID;
+    }
     if (ck.blocks) {
         if (((c.k_pools[layer] | c.v_pools[layer]) & 15u) != 0) err |= 1 << BKV_ERR_INVALID;
         const int nb = (err & (1 << BKV_ERR_LENGTH)) ? 0 : (N + kBlock - 1) / kBlock;
@@ -124,9 +140,14 @@ hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const i
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, Check ck, int32_t* status, hipStream_t s);
 // `shared`: one row / keep list per (layer, request) instead of per head-cache.
+// `rows` of the random scorer: BKV_ROWS_PER_HEAD, _PER_LAYER_REQUEST or _PER_REQUEST.
 hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
-                               const int32_t* pass_idx, int shared, uint32_t* scores, int stride,
+                               const int32_t* pass_idx, int rows, uint32_t* scores, int stride,
                                Check ck, int32_t* status, hipStream_t s);
+hipError_t launch_page_retain(const CacheView& c, const void* scores, int kind, int stride,
+                              int rows, int budget, int32_t* keep_pages, int32_t* block_table_out,
+                              int32_t* seq_len_out, int32_t* freed, Check ck, int32_t* status,
+                              hipStream_t s);
 hipError_t launch_topk_select(const CacheView& c, const void* scores, int kind, int stride,
                               int score_heads, int shared, int budget, int32_t* keep, Check ck,
                               int32_t* status, hipStream_t s);

@@ -1,0 +1,155 @@
+// page_retain.hip -- page retention: the cache shrinks by whole 16-slot pages,
+// chosen once per request for every layer and head, so the compaction becomes
+// a rewrite of the request's block table and no K/V row moves.
+//
+// Random Attention article, section "发现二": keeping contiguous blocks of 1 to
+// 64 tokens instead of scattered tokens leaves accuracy almost unchanged, and
+// so does forcing every head onto one common set of positions.  With the
+// block equal to the cache page and one selection per request, both hold at
+// once and the selection maps straight onto the paged layout.
+//
+// One workgroup of 1024 threads per request:
+//   1. stage the request's block-table row in LDS (before anything is written,
+//      so the output row may alias the input);
+//   2. page key = the largest candidate-slot score of the page over all the
+//      request's score rows (every layer and head of per-head beacon scores,
+//      or one shared random row), folded into LDS with an integer max;
+//   3. prompt pages and a partial last page are kept; the budget / 16 - forced
+//      best remaining pages are found with the shared radix select (ties to
+//      the earlier page);
+//   4. one block-wide scan places each kept page's block at the front of the
+//      new row (page order) and each dropped page's block in the released list.
+
+#include "select_util.h"
+
+namespace bkv {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kMaxPagesPerThread = (kMaxBlocksPerReq + kThreads - 1) / kThreads;
+
+__global__ __launch_bounds__(kThreads) void page_retain_kernel(
+    CacheView c, const uint32_t* __restrict__ scores, int is_f32, int stride, int per_request_row,
+    int B, int32_t* __restrict__ keep_pages, int32_t* block_table_out, int32_t* seq_len_out,
+    int32_t* __restrict__ freed, Check ck, int32_t* status) {
+    __shared__ int s_bt[kMaxBlocksPerReq];
+    __shared__ uint32_t s_pkey[kMaxBlocksPerReq];
+    __shared__ RadixScratch s_rs;
+    __shared__ int s_wsum[kWaves];
+
+    const int r = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (!request_ok(c, 0, r, ck, status)) return;
+    const int N = c.seq_len[r];
+    const int P = c.prompt_len[r];
+    const int npages = (N + kBlock - 1) / kBlock;
+    const int Bp = B / kBlock;
+    const int32_t* bt = c.block_table + (size_t)r * c.max_blocks;
+    for (int j = tid; j < npages; j += kThreads) {
+        s_bt[j] = bt[j];
+        s_pkey[j] = 0;
+    }
+    __syncthreads();  // every read of the block-table row and of seq_len is done
+
+    const int pf = (P + kBlock - 1) / kBlock;  // pages [0, pf) hold prompt slots
+    const bool last_partial = (N % kBlock) != 0 && npages - 1 >= pf;
+    const int pe = npages - (last_partial ? 1 : 0);  // candidate pages [pf, pe)
+    const bool evict = npages > Bp;
+    const int k = evict ? Bp - pf - (last_partial ? 1 : 0) : 0;  // >= 0 (budget check)
+
+    uint32_t T = 0;
+    int need = 0;
+    if (k > 0) {
+        // candidate slots n in [pf*16, pe*16), at score column n - P
+        const int i0 = pf * kBlock - P, i1 = pe * kBlock - P;
+        const int layers = per_request_row ? 1 : c.L;
+        const int heads = per_request_row ? 1 : c.H;
+        const size_t layer_step = per_request_row ? 0 : (size_t)c.R * c.H * stride;
+        const uint32_t* first_row =
+            scores + (per_request_row ? (size_t)r : (size_t)r * c.H) * stride;
+        for (int i = i0 + tid; i < i1; i += kThreads) {
+            uint32_t v = 0;
+            for (int l = 0; l < layers; ++l) {
+                const uint32_t* src = first_row + l * layer_step + i;
+                for (int h = 0; h < heads; ++h) {
+                    uint32_t w = src[(size_t)h * stride];
+                    if (is_f32 && (w >> 31)) w = 0;  // negative fp32 scores rank as 0
+                    v = max(v, w);
+                }
+            }
+            atomicMax(&s_pkey[(P + i) / kBlock], v);
+        }
+        __syncthreads();
+        T = radix_select<kThreads>(s_pkey + pf, pe - pf, k, &s_rs, &need);
+    }
+
+    // Each thread owns a contiguous run of pages (page order).
+    const int seg = (npages + kThreads - 1) / kThreads;
+    const int lo = min(tid * seg, npages), hi = min(lo + seg, npages);
+    int eq = 0;
+    if (k > 0)
+        for (int j = max(lo, pf); j < min(hi, pe); ++j) eq += (s_pkey[j] == T);
+    const int eq_before = block_exclusive_scan<kThreads>(eq, s_wsum);
+    bool take[kMaxPagesPerThread];
+    int kept = 0, e = eq_before;
+#pragma unroll
+    for (int u = 0; u < kMaxPagesPerThread; ++u) {
+        const int j = lo + u;
+        bool t = false;
+        if (j < hi) {
+            if (!evict || j < pf || j >= pe) {
+                t = true;  // nothing to evict, a prompt page or the partial last page
+            } else if (k > 0) {
+                const uint32_t v = s_pkey[j];
+                t = v > T || (v == T && e < need);
+                e += (v == T);
+            }
+        }
+        take[u] = t;
+        kept += t;
+    }
+    const int kept_before = block_exclusive_scan<kThreads>(kept, s_wsum);
+    const int n_kept = evict ? Bp : npages;
+
+    int32_t* kp = keep_pages + (size_t)r * Bp;
+    int32_t* row_out = block_table_out + (size_t)r * c.max_blocks;
+    int32_t* fr = freed + (size_t)r * c.max_blocks;
+    int kb = kept_before;
+#pragma unroll
+    for (int u = 0; u < kMaxPagesPerThread; ++u) {
+        const int j = lo + u;
+        if (j >= hi) break;
+        if (take[u]) {
+            if (kb < Bp) kp[kb] = j;  // kb < Bp whenever j is kept under eviction
+            row_out[kb] = s_bt[j];
+            ++kb;
+        } else {
+            fr[j - kb] = s_bt[j];
+        }
+    }
+    for (int i = n_kept + tid; i < Bp; i += kThreads) kp[i] = -1;
+    for (int i = n_kept + tid; i < npages; i += kThreads) row_out[i] = -1;
+    for (int i = npages - n_kept + tid; i < c.max_blocks; i += kThreads) fr[i] = -1;
+    if (tid == 0) {
+        // every kept page is full except a partial last page, which is always kept
+        const int tail = N % kBlock;
+        seq_len_out[r] = evict ? n_kept * kBlock - (tail ? kBlock - tail : 0) : N;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_page_retain(const CacheView& c, const void* scores, int kind, int stride,
+                              int rows, int budget, int32_t* keep_pages, int32_t* block_table_out,
+                              int32_t* seq_len_out, int32_t* freed, Check ck, int32_t* status,
+                              hipStream_t s) {
+    if (c.R == 0) return hipSuccess;
+    hipLaunchKernelGGL(page_retain_kernel, dim3(c.R), dim3(kThreads), 0, s, c,
+                       static_cast<const uint32_t*>(scores), kind == BKV_SCORE_F32 ? 1 : 0,
+                       stride, rows == BKV_ROWS_PER_REQUEST ? 1 : 0, budget, keep_pages,
+                       block_table_out, seq_len_out, freed, ck, status);
+    return hipGetLastError();
+}
+
+}  // namespace bkv

@@ -6,7 +6,8 @@
 // index, layer, head, n), so the scorer needs no RNG state and a new pass
 // index draws afresh.  With shared positions (same article, section "发现二":
 // every head on one common set of positions) one row per (layer, request) is
-// drawn, with the head field of the counter set to 0.  Philox4x64-10 as published by Salmon, Moraes, Dror and
+// drawn, with the head field of the counter set to 0; for page retention one
+// row per request, with the layer and head fields set to 0.  Philox4x64-10 as published by Salmon, Moraes, Dror and
 // Shaw ("Parallel random numbers: as easy as 1, 2, 3", SC'11): ten rounds of
 // two 64x64->128-bit multiplies with a Weyl-sequence key schedule.  One thread
 // evaluates one counter and scores the four slots 4g .. 4g+3.
@@ -45,10 +46,12 @@ __device__ __forceinline__ U64x4 philox4x64_10(U64x4 x, uint64_t k0, uint64_t k1
 
 __global__ __launch_bounds__(kThreads) void random_score_kernel(
     CacheView c, uint64_t seed, const uint64_t* __restrict__ req_ids,
-    const int32_t* __restrict__ pass_idx, int shared, uint32_t* __restrict__ scores, int stride,
+    const int32_t* __restrict__ pass_idx, int rows, uint32_t* __restrict__ scores, int stride,
     Check ck, int32_t* status) {
-    const int row = blockIdx.x;  // head-cache, or (layer, request) when shared
-    const HeadIdx x = shared ? HeadIdx{row / c.R, row % c.R, 0} : split_hc(c, row);
+    const int row = blockIdx.x;  // head-cache, (layer, request) or request
+    const HeadIdx x = rows == BKV_ROWS_PER_REQUEST        ? HeadIdx{0, row, 0}
+                      : rows == BKV_ROWS_PER_LAYER_REQUEST ? HeadIdx{row / c.R, row % c.R, 0}
+                                                           : split_hc(c, row);
     if (!request_ok(c, x.layer, x.req, ck, status)) return;
     const int N = c.seq_len[x.req];
     const int P = c.prompt_len[x.req];
@@ -73,15 +76,17 @@ __global__ __launch_bounds__(kThreads) void random_score_kernel(
 }  // namespace
 
 hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
-                               const int32_t* pass_idx, int shared, uint32_t* scores, int stride,
+                               const int32_t* pass_idx, int rows, uint32_t* scores, int stride,
                                Check ck, int32_t* status, hipStream_t s) {
-    const int rows = c.L * c.R * (shared ? 1 : c.H);
-    if (rows == 0) return hipSuccess;
+    const int n_rows = rows == BKV_ROWS_PER_REQUEST        ? c.R
+                       : rows == BKV_ROWS_PER_LAYER_REQUEST ? c.L * c.R
+                                                            : c.L * c.R * c.H;
+    if (n_rows == 0) return hipSuccess;
     const int max_slots = c.max_blocks * kBlock;
     const int groups = (max_slots + 3) / 4;
     const int gx = (groups + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(random_score_kernel, dim3(rows, gx), dim3(kThreads), 0, s, c, seed,
-                       req_ids, pass_idx, shared, scores, stride, ck, status);
+    hipLaunchKernelGGL(random_score_kernel, dim3(n_rows, gx), dim3(kThreads), 0, s, c, seed,
+                       req_ids, pass_idx, rows, scores, stride, ck, status);
     return hipGetLastError();
 }
 

@@ -18,37 +18,13 @@
 // per-head keys (score_heads = 1 for one shared random draw), and the keep
 // list is written once per (layer, request).
 
-#include "bkv_internal.h"
+#include "select_util.h"
 
 namespace bkv {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
-// Exclusive prefix sum of one int per thread over the whole block, in thread
-// order.  Synchronises; s_wsum needs kWaves entries.
-__device__ int block_exclusive_scan(int v, int* s_wsum) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
-    const int incl = wave_inclusive_scan(v);
-    if (lane == kWave - 1) s_wsum[w] = incl;
-    __syncthreads();
-    int off = 0;
-    for (int j = 0; j < w; ++j) off += s_wsum[j];
-    __syncthreads();  // s_wsum may be reused by the next scan
-    return off + incl - v;
-}
 
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
                                                                const uint32_t* __restrict__ scores,
@@ -57,10 +33,8 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
                                                                int32_t* __restrict__ keep, Check ck,
                                                                int32_t* status) {
     extern __shared__ uint32_t s_key[];  // [stride]
-    __shared__ int s_hist[256];
+    __shared__ RadixScratch s_rs;
     __shared__ int s_wsum[kWaves];
-    __shared__ uint32_t s_prefix;
-    __shared__ int s_need;
 
     const int unit = blockIdx.x;  // head-cache, or (layer, request) when shared
     const HeadIdx x = shared ? HeadIdx{unit / c.R, unit % c.R, 0} : split_hc(c, unit);
@@ -90,55 +64,16 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
         s_key[i] = v;
     }
 
-    // MSB-first radix select of the k-th largest key.
-    uint32_t prefix = 0, mask = 0;
-    int need = k;  // rank still to locate inside the keys matching `prefix`
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += kThreads) s_hist[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < m; i += kThreads) {
-            const uint32_t v = s_key[i];
-            if ((v & mask) == prefix) atomicAdd(&s_hist[(v >> shift) & 255u], 1);
-        }
-        __syncthreads();
-        if (tid < kWave) {
-            // lane l owns digits 255-4l .. 252-4l (descending)
-            int cnt[4], local = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                cnt[j] = s_hist[255 - 4 * tid - j];
-                local += cnt[j];
-            }
-            const int incl = wave_inclusive_scan(local);
-            const int excl = incl - local;  // keys with a larger digit
-            if (excl < need && need <= incl) {
-                int rem = need - excl, above = excl, digit = 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (rem <= cnt[j]) {
-                        digit = 255 - 4 * tid - j;
-                        break;
-                    }
-                    rem -= cnt[j];
-                    above += cnt[j];
-                }
-                s_prefix = prefix | ((uint32_t)digit << shift);
-                s_need = need - above;
-            }
-        }
-        __syncthreads();
-        prefix = s_prefix;
-        need = s_need;
-        mask |= 0xFFu << shift;
-    }
-    const uint32_t T = prefix;  // the k-th largest key; `need` copies of T are kept
+    // MSB-first radix select of the k-th largest key; `need` copies of it are kept.
+    int need;
+    const uint32_t T = radix_select<kThreads>(s_key, m, k, &s_rs, &need);
 
     // Each thread owns one contiguous run of candidates (slot order).
     const int seg = (m + kThreads - 1) / kThreads;
     const int lo = min(tid * seg, m), hi = min(lo + seg, m);
     int eq = 0;
     for (int i = lo; i < hi; ++i) eq += (s_key[i] == T);
-    const int eq_before = block_exclusive_scan(eq, s_wsum);
+    const int eq_before = block_exclusive_scan<kThreads>(eq, s_wsum);
     int kept = 0, e = eq_before;
     for (int i = lo; i < hi; ++i) {
         const uint32_t v = s_key[i];
@@ -146,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
         e += (v == T);
         kept += take;
     }
-    int o = P + block_exclusive_scan(kept, s_wsum);
+    int o = P + block_exclusive_scan<kThreads>(kept, s_wsum);
     e = eq_before;
     for (int i = lo; i < hi; ++i) {
         const uint32_t v = s_key[i];

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 3
+#define BKV_ABI_VERSION 4
 
 typedef void* bkv_stream_t; /* hipStream_t */
 
@@ -75,6 +75,9 @@ enum {
 
 enum { BKV_SCORE_F32 = 0, BKV_SCORE_U32 = 1 };           /* score buffer element type */
 enum { BKV_SELECT_BEACON = 0, BKV_SELECT_RANDOM = 1 };   /* selector of bkv_evict_pass */
+/* Row layout of a score buffer: one row per head-cache (hc), per (layer,
+ * request) (row layer * n_requests + r), or per request (row r). */
+enum { BKV_ROWS_PER_HEAD = 0, BKV_ROWS_PER_LAYER_REQUEST = 1, BKV_ROWS_PER_REQUEST = 2 };
 
 #define BKV_MAX_BEACONS 256
 #define BKV_MAX_CANDIDATES 32768 /* largest score_stride bkv_topk_select accepts */
@@ -155,12 +158,14 @@ int32_t bkv_beacon_score(const bkv_cache* cache, const float* beacons, const int
  *                  request_ids[r]), key = (seed, 0)).
  * request_ids uint64 [n_requests], pass_idx int32 [n_requests] are device
  * arrays; a new pass index gives fresh draws.
- * shared = 1 (shared positions, same article, section "发现二": all heads on
- * one common set of random positions): one row per (layer, request), row
- * layer * n_requests + r, holding the draws of head 0; shared = 0: one row
- * per head-cache.  Any other value is BKV_ERR_INVALID. */
+ * rows selects the row layout (same article, section "发现二": all heads on
+ * one common set of random positions): BKV_ROWS_PER_HEAD draws one row per
+ * head-cache; BKV_ROWS_PER_LAYER_REQUEST one row per (layer, request), row
+ * layer * n_requests + r, with the head field 0 (shared positions);
+ * BKV_ROWS_PER_REQUEST one row per request, row r, with the layer and head
+ * fields 0 (page retention).  Any other value is BKV_ERR_INVALID. */
 int32_t bkv_random_score(const bkv_cache* cache, uint64_t seed, const uint64_t* request_ids,
-                         const int32_t* pass_idx, int32_t shared, uint32_t* scores,
+                         const int32_t* pass_idx, int32_t rows, uint32_t* scores,
                          int32_t score_stride, int32_t* status, bkv_stream_t stream);
 
 /* Top-B selection with full prompt protection (Random Attention article,
@@ -208,6 +213,38 @@ int32_t bkv_kv_compact(const bkv_cache* cache, const int32_t* keep_idx, int32_t 
                        int32_t keep_shared, int32_t* pos_ids, int32_t pos_stride,
                        int32_t* status, bkv_stream_t stream);
 
+/* Page retention (Random Attention article, section "发现二": keeping
+ * contiguous blocks of up to 64 tokens instead of scattered tokens, and one
+ * common set of positions for all heads, both leave accuracy almost
+ * unchanged).  One selection of whole 16-slot pages per request, for every
+ * layer and head, so no K/V row moves: the request's block table is rewritten.
+ * For request r with N slots, P prompt slots and npages = ceil(N / 16):
+ *   - pages holding a prompt slot and a partial last page are always kept;
+ *   - a page's key is the largest score of its slots over the request's score
+ *     rows: score_rows = BKV_ROWS_PER_HEAD reads every head-cache row of the
+ *     request ((layer * n_requests + r) * n_kv_heads + h), BKV_ROWS_PER_REQUEST
+ *     reads row r (one shared random draw row); column n - P as usual;
+ *   - budget / 16 pages survive (budget must be a multiple of 16): the forced
+ *     pages plus the best remaining pages by (key descending, page ascending);
+ *     npages <= budget / 16 keeps every page; more forced pages than that is
+ *     the device error BKV_ERR_BUDGET (request untouched).
+ * Outputs, for every request that passes its checks:
+ *   keep_pages int32 [n_requests][budget / 16]: kept page indices ascending,
+ *     -1 padded;
+ *   block_table_out int32 [n_requests][max_blocks]: entry i < kept = the block
+ *     of the i-th kept page, entries [kept, npages) = -1, the rest untouched;
+ *     it may be the cache's own block_table (rewritten in place);
+ *   seq_len_out int32 [n_requests]: the new slot count (may be the cache's
+ *     own seq_len); prompt_len is unchanged, since prompt pages stay in front;
+ *   freed_blocks int32 [n_requests][max_blocks]: the blocks of the dropped
+ *     pages in page order, then -1; the caller returns them to its allocator.
+ * scores is read exactly as written by bkv_beacon_score (BKV_SCORE_F32) or
+ * bkv_random_score (BKV_SCORE_U32, rows BKV_ROWS_PER_REQUEST). */
+int32_t bkv_page_retain(const bkv_cache* cache, const void* scores, int32_t score_kind,
+                        int32_t score_stride, int32_t score_rows, int32_t budget,
+                        int32_t* keep_pages, int32_t* block_table_out, int32_t* seq_len_out,
+                        int32_t* freed_blocks, int32_t* status, bkv_stream_t stream);
+
 /* One whole eviction pass at a synchronized batch point: maintenance,
  * scoring, selection and compaction for every layer, request and head. */
 typedef struct bkv_pass_args {
@@ -220,6 +257,15 @@ typedef struct bkv_pass_args {
                                   random draws one row); keep lists then have
                                   n_layers * n_requests rows, and so does the random
                                   selector's score buffer */
+    int32_t page_retention;    /* 1: bkv_page_retain replaces selection and compaction
+                                  (budget a multiple of 16, shared_positions 0,
+                                  pos_ids NULL); keep lists are the kept pages
+                                  [n_requests][budget / 16], the random selector
+                                  draws one row per request, and the three outputs
+                                  below are required */
+    int32_t* block_table_out;  /* page retention: [n_requests][max_blocks], may alias */
+    int32_t* seq_len_out;      /* page retention: [n_requests], may alias */
+    int32_t* freed_blocks;     /* page retention: [n_requests][max_blocks] */
     /* beacon selector */
     int32_t n_beacons;         /* K */
     int32_t T, G;              /* buffered decode steps, query heads per KV head */
@@ -239,12 +285,15 @@ typedef struct bkv_pass_args {
     int32_t* pos_ids;          /* nullable int32 [HC][pos_stride], compacted with the cache */
     int32_t pos_stride;
     void* scores_out;          /* nullable [rows][score_stride] scores; else workspace */
-    int32_t* keep_out;         /* nullable [rows][budget] keep lists; else workspace */
+    int32_t* keep_out;         /* nullable [rows][budget] keep lists (kept pages
+                                  [n_requests][budget / 16] with page retention);
+                                  else workspace */
     /* optional profiling hook: caller-created hipEvent_t handles, recorded on
      * `stream` before the first kernel and after every kernel of the pass
      * (beacon: 5 events around update, score, select, compact; random: 4
-     * events around score, select, compact).  Ignored when NULL or when
-     * n_timing_events is smaller than that. */
+     * events around score, select, compact; one fewer with page retention,
+     * whose one kernel replaces select and compact).  Ignored when NULL or
+     * when n_timing_events is smaller than that. */
     void* const* timing_events;
     int32_t n_timing_events;
 } bkv_pass_args;
@@ -255,7 +304,8 @@ typedef struct bkv_pass_args {
 int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, size_t* bytes);
 
 /* Runs, on `stream`: (beacon) maintenance -> beacon scoring -> selection ->
- * compaction, or (random) random scoring -> selection -> compaction.
+ * compaction, or (random) random scoring -> selection -> compaction; with
+ * page_retention, bkv_page_retain takes the place of the last two.
  * A request that fails a device check (lengths, block ids, budget) is left
  * entirely untouched -- beacons, counts, cache and pos_ids -- and flagged in
  * *status. */

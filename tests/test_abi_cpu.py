@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(bk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 3
+    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 4
     for code in range(0, 9):
         s = bk.bkv_status_string(code)
         assert s and s != "unknown status code"
@@ -104,6 +104,28 @@ def test_select_compact_random_validation():
     assert rnd(ctypes.byref(c), 1, None, FAKE, 0, FAKE, 160, None, None) == bk.BKV_ERR_NULL
     assert rnd(ctypes.byref(c), 1, FAKE, FAKE, 0, FAKE, 0, None, None) == bk.BKV_ERR_INVALID
     assert rnd(ctypes.byref(c), 1, FAKE, FAKE, -1, FAKE, 160, None, None) == bk.BKV_ERR_INVALID
+    assert rnd(ctypes.byref(c), 1, FAKE, FAKE, 3, FAKE, 160, None, None) == bk.BKV_ERR_INVALID
+
+
+def test_page_retain_validation():
+    c = _cache()
+    f = bk._lib.bkv_page_retain
+    ok = dict(scores=FAKE, kind=0, stride=160, rows=bk.BKV_ROWS_PER_HEAD, budget=64, keep=FAKE,
+              bt=FAKE, sl=FAKE, fr=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(ctypes.byref(c), a["scores"], a["kind"], a["stride"], a["rows"], a["budget"],
+                 a["keep"], a["bt"], a["sl"], a["fr"], None, None)
+
+    assert call(budget=40) == bk.BKV_ERR_INVALID          # not a whole number of pages
+    assert call(budget=0) == bk.BKV_ERR_INVALID
+    assert call(rows=bk.BKV_ROWS_PER_LAYER_REQUEST) == bk.BKV_ERR_INVALID
+    assert call(kind=2) == bk.BKV_ERR_INVALID
+    assert call(stride=0) == bk.BKV_ERR_INVALID
+    assert call(bt=None) == bk.BKV_ERR_NULL
+    assert call(fr=None) == bk.BKV_ERR_NULL
+    assert call(sl=FAKE + 2) == bk.BKV_ERR_INVALID
 
 
 def test_shared_select_validation():
@@ -137,6 +159,16 @@ def test_workspace_and_pass_validation():
     assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == \
         bk.BKV_ERR_INVALID
     a.shared_positions, a.selector = 0, bk.BKV_SELECT_RANDOM
+    a.page_retention = 1           # random + pages: one draw row and one page list per request
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
+    assert 3 * 160 * 4 + 3 * 4 * 4 <= n.value <= 3 * 160 * 4 + 3 * 4 * 4 + 512
+    a.shared_positions = 1         # pages exclude shared positions
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == \
+        bk.BKV_ERR_INVALID
+    a.shared_positions, a.budget = 0, 72   # pages need a whole number of pages
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == \
+        bk.BKV_ERR_INVALID
+    a.page_retention, a.budget = 0, 64
     a.scores_out, a.keep_out = FAKE, FAKE
     assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
     assert n.value == 0

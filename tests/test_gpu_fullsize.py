@@ -182,3 +182,78 @@ def test_full_size_shared_positions_pass(selector):
             k0, v0 = before[u][h]
             assert np.array_equal(ko[: len(kp)], oracle.kv_compact(k0, kp)), (u, h)
             assert np.array_equal(vo[: len(kp)], oracle.kv_compact(v0, kp)), (u, h)
+
+
+@pytest.mark.parametrize("selector", ["beacon", "random"])
+def test_full_size_page_retention_pass(selector):
+    """The same workload with page retention, launched as the benchmark's
+    page-retention passes (block table and lengths rewritten in place).  A
+    spread sample of requests is checked against the oracle's page selection
+    (on the GPU's per-head scores of all 288 head-caches of the request for the
+    beacon selector; on the oracle's own draws for the random one) and block
+    rewrite; every request's new length and released count are checked, and
+    the sampled requests' K/V rows must not have moved."""
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from decode_kv_cache_beacon_amd import beaconkv as bk
+
+    wl = synth.WORKLOADS["serving_r128"]
+    dev = torch.device("cuda")
+    say("full size pages", selector, "generate")
+    batch = synth.make_batch(wl, dev)
+    cache = bk.PagedCache(batch.k_pools, batch.v_pools, batch.block_table, batch.seq_len,
+                          batch.prompt_len)
+    L, R, H = cache.n_layers, cache.n_requests, cache.n_kv_heads
+    HC, B, W, M = cache.n_head_caches, wl.budget, wl.window, cache.max_blocks
+    N = batch.seq_len.cpu().numpy()
+    P = batch.prompt_len.cpu().numpy()
+    stride = int((N - P).max())
+    bt_in = batch.block_table.cpu().numpy().copy()
+    rng = np.random.default_rng(5)
+    sample = sorted({0, R - 1, *rng.choice(R, 6, replace=False).tolist()})
+    before = {r: [gather_head(batch.k_pools[layer], batch.block_table[r], h, int(N[r]))
+                  for layer in (0, L - 1) for h in (0, H - 1)] for r in sample}
+    kp = torch.full((R, B // 16), -7, dtype=torch.int32, device=dev)
+    freed = torch.full((R, M), -7, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    bt_dev_in = batch.block_table.clone()
+    outs = (cache.block_table, cache.seq_len, freed)
+    say("full size pages", selector, "pass")
+    if selector == "beacon":
+        scores = torch.zeros((HC, stride), dtype=torch.float32, device=dev)
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=batch.queries,
+                          beacons=batch.beacons, counts=batch.counts, window=W, bonus=wl.bonus,
+                          scores_out=scores, keep_out=kp, score_stride=stride, status=status,
+                          check=False, page_retention=outs)
+    else:
+        rid = torch.arange(R, dtype=torch.int64, device=dev)
+        pss = torch.full((R,), 3001, dtype=torch.int32, device=dev)
+        scores = torch.zeros((R, stride), dtype=torch.int32, device=dev)
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed, request_ids=rid,
+                          pass_idx=pss, scores_out=scores, keep_out=kp, score_stride=stride,
+                          status=status, check=False, page_retention=outs)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    sln, frn, kpn = cache.seq_len.cpu().numpy(), freed.cpu().numpy(), kp.cpu().numpy()
+    btn = cache.block_table.cpu().numpy()
+    npages = -(-N // 16)
+    assert np.all(sln == B)                               # 132 full pages -> 128 kept
+    assert np.all((frn >= 0).sum(1) == npages - B // 16)
+    for r in sample:
+        n, p = int(N[r]), int(P[r])
+        say("full size pages request", r)
+        if selector == "beacon":
+            rows = scores.view(L, R, H, stride)[:, r, :, : n - p].reshape(L * H, n - p)
+            ref = oracle.page_select(rows.cpu().numpy().astype(np.float64), n, p, B)
+        else:
+            draw = oracle.random_score(wl.seed, r, 3001, 0, 0, n, p)
+            assert np.array_equal(scores[r, : n - p].cpu().numpy().view(np.uint32), draw), r
+            ref = oracle.page_select(draw[None], n, p, B)
+        assert np.array_equal(kpn[r][kpn[r] >= 0], ref), r
+        row, fr, new_n = oracle.page_remap(bt_in[r], n, ref)
+        assert np.array_equal(btn[r, : len(row)], row) and np.all(btn[r, len(row): npages[r]] == -1)
+        assert np.array_equal(frn[r, : len(fr)], fr) and new_n == sln[r], r
+        after = [gather_head(batch.k_pools[layer], bt_dev_in[r], h, n)
+                 for layer in (0, L - 1) for h in (0, H - 1)]
+        for x, y in zip(before[r], after):
+            assert np.array_equal(x, y), r                # no row moved

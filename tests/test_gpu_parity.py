@@ -439,7 +439,7 @@ def test_shared_select_standalone_entry_points():
     rid = torch.arange(4, dtype=torch.int64).cuda() * 3 + 1
     pss = torch.tensor([2, 0, 9, 4], dtype=torch.int32).cuda()
     u = torch.full((L * R, stride), -1, dtype=torch.int32).cuda()
-    bk.bkv_random_score(cache, 77, rid, pss, u, shared=True)
+    bk.bkv_random_score(cache, 77, rid, pss, u, rows=bk.BKV_ROWS_PER_LAYER_REQUEST)
     keep = torch.full((L * R, B), -7, dtype=torch.int32).cuda()
     bk.bkv_topk_select_shared(cache, u, B, keep)
     un, kn = u.cpu().numpy().view(np.uint32), keep.cpu().numpy()
@@ -474,6 +474,155 @@ def test_shared_select_standalone_entry_points():
         a = oracle.gather_paged(v_in[layer], bt[r], h, N[r])
         o = oracle.gather_paged(v_out[layer], bt[r], h, N[r])
         assert np.array_equal(o[:len(kp)], oracle.kv_compact(a, kp)), hc
+
+
+def _page_outputs(cache, B):
+    R, M = cache.n_requests, cache.max_blocks
+    dev = torch.device("cuda")
+    return (torch.full((R, B // 16), -7, dtype=torch.int32, device=dev),
+            torch.full((R, M), -7, dtype=torch.int32, device=dev),
+            torch.full((R,), -7, dtype=torch.int32, device=dev),
+            torch.full((R, M), -7, dtype=torch.int32, device=dev))
+
+
+def _check_pages(where, r, kp_row, bt_row_in, bt_row_out, n_out, fr_row, ref_pages, N, M):
+    """GPU page outputs of request r against the oracle's pages and block-table rewrite."""
+    kp = keep_rows(kp_row)
+    assert np.array_equal(kp, ref_pages), (where, r, kp, ref_pages)
+    row, freed, new_n = oracle.page_remap(bt_row_in, N, ref_pages)
+    npages = -(-N // 16)
+    assert np.array_equal(bt_row_out[:len(row)], row), (where, r)
+    assert np.all(bt_row_out[len(row):npages] == -1), (where, r)
+    assert np.array_equal(bt_row_out[npages:], bt_row_in[npages:]), (where, r)  # untouched
+    assert n_out == new_n, (where, r, n_out, new_n)
+    assert np.array_equal(fr_row[:len(freed)], freed), (where, r)
+    assert np.all(fr_row[len(freed):] == -1), (where, r)
+
+
+def test_page_retain_standalone():
+    """bkv_random_score(rows per request) -> bkv_page_retain in place, and per-head fp32
+    scores merged over every layer and head out of place; partial pages, unaligned
+    prompts, nothing to evict and a refused request."""
+    say("page retain standalone")
+    wl = small(n_layers=3, n_requests=5, n_kv_heads=2, budget=512, prompt_len=200, seq_len=700)
+    batch = synth.make_batch(wl)
+    # (N, P): partial last page + unaligned prompt; aligned; N <= B; prompt fills the
+    # budget exactly; too many forced pages (refused)
+    N, P, B = [700, 640, 500, 688, 700], [201, 64, 100, 512, 510], 512
+    cache = device_cache(batch, N, P)
+    R, M, L, H = cache.n_requests, cache.max_blocks, cache.n_layers, cache.n_kv_heads
+    stride = 700
+    k_in, v_in = host_pools(cache)
+    bt_in = batch.block_table.numpy().copy()
+    rid = torch.arange(R, dtype=torch.int64).cuda() + 40
+    pss = torch.tensor([1, 2, 3, 4, 5], dtype=torch.int32).cuda()
+    u = torch.full((R, stride), -1, dtype=torch.int32).cuda()
+    bk.bkv_random_score(cache, 5, rid, pss, u, rows=bk.BKV_ROWS_PER_REQUEST)
+    kp, _, _, fr = _page_outputs(cache, B)
+    st = bk.bkv_page_retain(cache, u, B, kp, cache.block_table, cache.seq_len, fr,
+                            rows=bk.BKV_ROWS_PER_REQUEST, check=False)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 1 << bk.BKV_ERR_BUDGET       # request 4: 32 prompt pages + 1 partial
+    un = u.cpu().numpy().view(np.uint32)
+    kpn, btn, sln, frn = (kp.cpu().numpy(), cache.block_table.cpu().numpy(),
+                          cache.seq_len.cpu().numpy(), fr.cpu().numpy())
+    for r in range(R):
+        draw = oracle.random_score(5, int(rid[r]), int(pss[r]), 0, 0, N[r], P[r])
+        assert np.array_equal(un[r, :N[r] - P[r]], draw), r
+        if r == 4:
+            assert np.all(kpn[r] == -7) and np.array_equal(btn[r], bt_in[r]) and sln[r] == N[r]
+            assert np.all(frn[r] == -7)
+            continue
+        ref = oracle.page_select(draw[None], N[r], P[r], B)
+        _check_pages("random", r, kpn[r], bt_in[r], btn[r], sln[r], frn[r], ref, N[r], M)
+    k_out, v_out = host_pools(cache)
+    for layer in range(L):                       # no K/V row moved
+        assert np.array_equal(k_in[layer], k_out[layer]) and np.array_equal(v_in[layer], v_out[layer])
+
+    # per-head fp32 scores (heavy ties), out of place, on a fresh copy of the cache
+    cache = device_cache(batch, N, P)
+    rng = np.random.default_rng(21)
+    f = (np.round(rng.random((cache.n_head_caches, stride)) * 7) / 7).astype(np.float32)
+    kp, bto, slo, fr = _page_outputs(cache, B)
+    st = bk.bkv_page_retain(cache, torch.from_numpy(f).cuda(), B, kp, bto, slo, fr, check=False)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 1 << bk.BKV_ERR_BUDGET
+    kpn, bton, slon, frn = kp.cpu().numpy(), bto.cpu().numpy(), slo.cpu().numpy(), fr.cpu().numpy()
+    for r in range(R):
+        if r == 4:
+            assert np.all(bton[r] == -7) and slon[r] == -7
+            continue
+        rows = np.stack([f[hc_index(R, H, layer, r, h), :N[r] - P[r]]
+                         for layer in range(L) for h in range(H)]).astype(np.float64)
+        ref = oracle.page_select(rows, N[r], P[r], B)
+        row_out = bton[r].copy()
+        row_out[row_out == -7] = bt_in[r][row_out == -7]   # entries the kernel leaves alone
+        _check_pages("f32", r, kpn[r], bt_in[r], row_out, slon[r], frn[r], ref, N[r], M)
+        assert np.all(bton[r][-(-N[r] // 16):] == -7), r   # beyond the old pages: untouched
+    assert np.array_equal(cache.block_table.cpu().numpy(), bt_in)   # input table unchanged
+
+
+def _page_pass_case(wl, N, P, B, selector, seed=23):
+    """bkv_evict_pass with page retention, in place on the cache's block table."""
+    batch = synth.make_batch(wl)
+    cache = device_cache(batch, N, P)
+    k_in, v_in = host_pools(cache)
+    bt_in = batch.block_table.numpy().copy()
+    L, R, H = cache.n_layers, cache.n_requests, cache.n_kv_heads
+    HC, S, M = cache.n_head_caches, cache.max_slots, cache.max_blocks
+    kp, _, _, fr = _page_outputs(cache, B)
+    outs = (cache.block_table, cache.seq_len, fr)
+    if selector == "beacon":
+        q, b, c = batch.queries.cuda(), batch.beacons.cuda(), batch.counts.cuda()
+        T, G = q.shape[1], q.shape[2]
+        assign = torch.zeros((HC, T * G), dtype=torch.int32).cuda()
+        sc = torch.zeros((HC, S)).cuda()
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                          window=64, bonus=1.0, assign=assign, scores_out=sc, keep_out=kp,
+                          page_retention=outs)
+    else:
+        rid = torch.arange(100, 100 + R, dtype=torch.int64).cuda()
+        pss = torch.full((R,), 4, dtype=torch.int32).cuda()
+        sc = torch.zeros((R, S), dtype=torch.int32).cuda()
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=seed, request_ids=rid,
+                          pass_idx=pss, scores_out=sc, keep_out=kp, page_retention=outs)
+    torch.cuda.synchronize()
+    k_out, v_out = host_pools(cache)
+    for layer in range(L):                       # no K/V row moved
+        assert np.array_equal(k_in[layer], k_out[layer]) and np.array_equal(v_in[layer], v_out[layer])
+    scn = sc.cpu().numpy()
+    kpn, btn, sln, frn = (kp.cpu().numpy(), cache.block_table.cpu().numpy(),
+                          cache.seq_len.cpu().numpy(), fr.cpu().numpy())
+    qb = synth.bits(batch.queries)
+    for r in range(R):
+        n, p = N[r], P[r]
+        if selector == "beacon":
+            rows = []
+            for layer in range(L):
+                for h in range(H):
+                    hc = hc_index(R, H, layer, r, h)
+                    ob, oc, gap = oracle.beacon_update_forced(qb[hc], batch.beacons[hc].numpy(),
+                                                              batch.counts[hc].numpy(),
+                                                              assign[hc].cpu().numpy())
+                    assert gap.max() <= ASSIGN_TOL, hc
+                    assert np.array_equal(ob.view(np.int32), b[hc].cpu().numpy().view(np.int32))
+                    keys = oracle.gather_paged(k_in[layer], bt_in[r], h, n)
+                    o, _ = oracle.beacon_score(keys, ob, oc, p, 64, 1.0)
+                    check_scores(scn[hc, :n - p], o, f"page pass hc {hc}")
+                    rows.append(scn[hc, :n - p].astype(np.float64))
+            ref = oracle.page_select(np.stack(rows), n, p, B)
+        else:
+            draw = oracle.random_score(seed, 100 + r, 4, 0, 0, n, p)
+            assert np.array_equal(scn[r, :n - p].view(np.uint32), draw), r
+            ref = oracle.page_select(draw[None], n, p, B)
+        _check_pages(selector, r, kpn[r], bt_in[r], btn[r], sln[r], frn[r], ref, n, M)
+
+
+@pytest.mark.parametrize("selector", ["beacon", "random"])
+def test_evict_pass_page_retention(selector):
+    say("pass pages", selector)
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=512, prompt_len=200, seq_len=584)
+    _page_pass_case(wl, N=[584, 541, 400], P=[200, 333, 100], B=512, selector=selector)
 
 
 def test_evict_pass_tiny_one_shot():
