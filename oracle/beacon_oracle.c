@@ -451,6 +451,45 @@ void oracle_kv_compact(int n_keep, const int32_t* keep, int64_t row_bytes,
 }
 
 /* ------------------------------------------------------------------ */
+/* Decode attention over a compacted head-cache                        */
+/* ------------------------------------------------------------------ */
+
+/* The step after the pass (Random Attention article, section "发现四": every
+ * selector shares the same attention kernels over the compacted paged
+ * cache).  For each of the G query heads of one KV head, single-query softmax
+ * attention over the N cached rows:
+ *   s_n = scale * (q . k_n),  p_n = exp(s_n - max s) / sum exp(s - max s),
+ *   out = sum_n p_n v_n.
+ * Slot order and positions play no part (the keys were stored with their
+ * positions already applied), so a compacted cache is attended as is.
+ * q[G][d], keys/vals[N][d] bf16 bits; out[G][d] in double.  N = 0 gives 0. */
+void oracle_decode_attention(int N, int d, int G, const uint16_t* q, const uint16_t* keys,
+                             const uint16_t* vals, double scale, double* out) {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    for (int g = 0; g < G; ++g) {
+        double* o = out + (size_t)g * d;
+        for (int j = 0; j < d; ++j) o[j] = 0.0;
+        if (N == 0) continue;
+        double mx = -INFINITY;
+        for (int n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int j = 0; j < d; ++j)
+                acc += bf16_value(q[(size_t)g * d + j]) * bf16_value(keys[(size_t)n * d + j]);
+            s[n] = scale * acc;
+            if (s[n] > mx) mx = s[n];
+        }
+        double z = 0.0;
+        for (int n = 0; n < N; ++n) {
+            s[n] = exp(s[n] - mx);
+            z += s[n];
+        }
+        for (int n = 0; n < N; ++n)
+            for (int j = 0; j < d; ++j) o[j] += (s[n] / z) * bf16_value(vals[(size_t)n * d + j]);
+    }
+    free(s);
+}
+
+/* ------------------------------------------------------------------ */
 /* Whole pass over many independent head-caches (CPU baseline)         */
 /* ------------------------------------------------------------------ */
 

@@ -76,6 +76,8 @@ def lib():
         L.oracle_page_select.restype = i32
         L.oracle_page_remap.argtypes = [i32, i32, P, i32, P, P, P, P]
         L.oracle_page_remap.restype = i32
+        L.oracle_decode_attention.argtypes = [i32, i32, i32, P, P, P, f64, P]
+        L.oracle_decode_attention.restype = None
         L.oracle_kv_compact.argtypes = [i32, P, i64, P, P]
         L.oracle_kv_compact.restype = None
         L.oracle_num_threads.argtypes = []
@@ -247,6 +249,23 @@ def kv_compact(rows, keep):
     if kp.shape[0]:
         assert kp.min() >= 0 and kp.max() < r.shape[0]
         lib().oracle_kv_compact(int(kp.shape[0]), _ptr(kp), int(row_bytes), _ptr(r), _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- attention
+def decode_attention(q_bits, keys_bits, vals_bits, scale=None):
+    """Single-query softmax attention of q[G][d] over keys/vals[N][d] (bf16 bits) in
+    double; scale defaults to 1/sqrt(d).  Returns out[G][d] (float64)."""
+    q = _c(q_bits, np.uint16)
+    k = _c(keys_bits, np.uint16)
+    v = _c(vals_bits, np.uint16)
+    G, d = q.shape
+    N = k.shape[0]
+    assert k.shape == (N, d) and v.shape == (N, d)
+    out = np.zeros((G, d), np.float64)
+    sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    lib().oracle_decode_attention(N, d, G, _ptr(q), _ptr(k) if N else None,
+                                  _ptr(v) if N else None, sc, _ptr(out))
     return out
 
 

@@ -539,6 +539,43 @@ def test_random_page_retention_is_uniform_over_pages():
     assert np.all(np.abs(cand - expect) < 5 * sd), (cand, expect)
 
 
+# --------------------------------------------------------------- decode attention
+def _bf16_rows(shape, scale=1.0):
+    return bf16_bits(RNG.standard_normal(shape).astype(np.float32) * scale)
+
+
+def test_decode_attention_matches_torch_sdpa():
+    for G, N in [(4, 37), (1, 1), (8, 300)]:
+        q, k, v = _bf16_rows((G, 128)), _bf16_rows((N, 128), 2.0), _bf16_rows((N, 128))
+        qf, kf, vf = (torch.from_numpy(bf16_values(x).astype(np.float64)) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(qf[None], kf[None], vf[None])[0]
+        out = oracle.decode_attention(q, k, v)
+        assert np.allclose(out, ref.numpy(), rtol=1e-12, atol=1e-12), (G, N)
+
+
+def test_decode_attention_closed_forms():
+    q, k, v = _bf16_rows((4, 128)), _bf16_rows((1, 128)), _bf16_rows((1, 128))
+    assert np.array_equal(oracle.decode_attention(q, k, v), np.tile(bf16_values(v), (4, 1)))
+    k = np.tile(_bf16_rows((1, 128)), (50, 1))                 # identical keys -> mean of values
+    v = _bf16_rows((50, 128))
+    mean = bf16_values(v).astype(np.float64).mean(0)
+    assert np.allclose(oracle.decode_attention(q, k, v), np.tile(mean, (4, 1)), rtol=1e-13,
+                       atol=1e-13)
+    k, v = _bf16_rows((20, 128)), _bf16_rows((20, 128))          # huge scale -> the best key
+    best = (bf16_values(q).astype(np.float64) @ bf16_values(k).astype(np.float64).T).argmax(1)
+    hard = oracle.decode_attention(q, k, v, scale=1e6)
+    assert np.allclose(hard, bf16_values(v)[best], atol=1e-9)
+    assert np.all(oracle.decode_attention(q, k[:0], v[:0]) == 0)  # empty cache
+
+
+def test_decode_attention_ignores_slot_order():
+    q, k, v = _bf16_rows((4, 128)), _bf16_rows((200, 128), 1.5), _bf16_rows((200, 128))
+    perm = RNG.permutation(200)
+    a = oracle.decode_attention(q, k, v)
+    b = oracle.decode_attention(q, k[perm], v[perm])
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
 # --------------------------------------------------------------- compaction
 def test_compaction_is_numpy_gather():
     rows = RNG.integers(0, 2**16, (300, 128), dtype=np.uint16)
