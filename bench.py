@@ -56,6 +56,7 @@ KERNEL_SOURCES = {
     "kv_compact": "kv_compact.hip",
     "random_score": "random_score.hip",
     "page_retain": "page_retain.hip",
+    "decode_attention": "decode_attention.hip",
 }
 
 
@@ -155,6 +156,7 @@ KERNEL_SYMBOLS = {
     "kv_compact_kernel": "kv_compact",
     "random_score_kernel": "random_score",
     "page_retain_kernel": "page_retain",
+    "decode_attention_kernel": "decode_attention",
 }
 COPY_SYMBOL = "__amd_rocclr_copyBuffer"
 PROFILE_CMDS = {
@@ -437,6 +439,30 @@ def main():
         "wall_ms_per_step_incl_append": round(wall * 1e3 / args.steps, 3),
         "roofline": roof,
     }
+
+    # the consumer of the pass: one decode step of attention over the compacted
+    # cache (every layer, request and KV head; the length set to the kept count)
+    cache.seq_len.clamp_(max=B)
+    q_last = q[:, -1].contiguous()                      # [HC, G, 128] bf16
+    att_out = torch.empty((HC, wl.group, wl.head_dim), dtype=torch.float32, device=dev)
+    bk.bkv_decode_attention(cache, q_last, att_out, status=status, check=False)
+    att_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    for e0, e1 in att_ev:
+        e0.record()
+        bk.bkv_decode_attention(cache, q_last, att_out, status=status, check=False)
+        e1.record()
+    torch.cuda.synchronize()
+    bk.check_status(status, "decode attention")
+    att_ms = sum(a.elapsed_time(b_) for a, b_ in att_ev) / len(att_ev)
+    att_bytes = HC * (min(N[0], B) * 2 * wl.head_dim * 2 + wl.group * wl.head_dim * (2 + 4))
+    result["decode_attention"] = {
+        "ms": round(att_ms, 4), "algorithmic_bytes": int(att_bytes),
+        "gbps": round(att_bytes / (att_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(att_bytes / (att_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "note": f"one decode step, {wl.group} query heads per KV head over the {min(N[0], B)} "
+                "kept slots of every head-cache, fp32 output"}
+    cache.seq_len.copy_(torch.tensor(N, dtype=torch.int32, device=dev))
 
     if not args.no_random:
         rid = torch.arange(R, dtype=torch.int64, device=dev)

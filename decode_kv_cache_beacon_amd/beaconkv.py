@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
-BKV_ABI_VERSION = 4
+BKV_ABI_VERSION = 5
 BKV_OK, BKV_ERR_NULL, BKV_ERR_INVALID, BKV_ERR_BUDGET, BKV_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BKV_ERR_WORKSPACE, BKV_ERR_HIP, BKV_ERR_LENGTH, BKV_ERR_BLOCK_TABLE = 5, 6, 7, 8
 BKV_SCORE_F32, BKV_SCORE_U32 = 0, 1
@@ -32,6 +32,7 @@ BKV_SELECT_BEACON, BKV_SELECT_RANDOM = 0, 1
 BKV_ROWS_PER_HEAD, BKV_ROWS_PER_LAYER_REQUEST, BKV_ROWS_PER_REQUEST = 0, 1, 2
 BKV_MAX_BEACONS = 256
 BKV_MAX_CANDIDATES = 32768
+BKV_MAX_QUERY_HEADS = 8
 HEAD_DIM = 128
 BLOCK_SIZE = 16
 
@@ -84,6 +85,8 @@ _lib.bkv_kv_compact.restype = _i32
 _lib.bkv_page_retain.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i32, _i32, _i32, _P, _P, _P,
                                  _P, _P, _P]
 _lib.bkv_page_retain.restype = _i32
+_lib.bkv_decode_attention.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _f32, _P, _P, _P]
+_lib.bkv_decode_attention.restype = _i32
 _lib.bkv_workspace_size.argtypes = [ctypes.POINTER(bkv_cache), ctypes.POINTER(bkv_pass_args),
                                     ctypes.POINTER(_sz)]
 _lib.bkv_workspace_size.restype = _i32
@@ -93,7 +96,7 @@ _lib.bkv_evict_pass.restype = _i32
 
 EXPORTS = ("bkv_abi_version", "bkv_status_string", "bkv_beacon_update", "bkv_beacon_score",
            "bkv_random_score", "bkv_topk_select", "bkv_topk_select_shared", "bkv_kv_compact",
-           "bkv_page_retain", "bkv_workspace_size", "bkv_evict_pass")
+           "bkv_page_retain", "bkv_decode_attention", "bkv_workspace_size", "bkv_evict_pass")
 
 
 class BkvError(RuntimeError):
@@ -404,6 +407,27 @@ def bkv_page_retain(cache: PagedCache, scores, budget, keep_pages, block_table_o
     _check(code, "bkv_page_retain")
     if own and check:
         check_status(st, "bkv_page_retain", stream)
+    return st
+
+
+def bkv_decode_attention(cache: PagedCache, queries, out, scale=None, status=None, check=True,
+                         stream=None):
+    """queries bf16 [HC, G, 128] -> out fp32 [HC, G, 128]: softmax attention of every query
+    head over the slots [0, seq_len) of its head-cache; scale defaults to 1/sqrt(128)."""
+    HC = cache.n_head_caches
+    _need(queries, "queries", torch.bfloat16)
+    if queries.dim() != 3 or queries.shape[0] != HC or queries.shape[2] != HEAD_DIM:
+        raise ValueError("queries must be [HC, G, 128]")
+    G = queries.shape[1]
+    _need(out, "out", torch.float32, (HC, G, HEAD_DIM))
+    sc = HEAD_DIM ** -0.5 if scale is None else float(scale)
+    st, own = _status(status, cache.device)
+    c = cache.struct()
+    code = _lib.bkv_decode_attention(ctypes.byref(c), _ptr(queries), G, sc, _ptr(out), _ptr(st),
+                                     _stream(stream))
+    _check(code, "bkv_decode_attention")
+    if own and check:
+        check_status(st, "bkv_decode_attention", stream)
     return st
 
 

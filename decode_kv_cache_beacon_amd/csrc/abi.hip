@@ -247,6 +247,19 @@ int32_t bkv_page_retain(const bkv_cache* cache, const void* scores, int32_t scor
                                          static_cast<hipStream_t>(stream)));
 }
 
+int32_t bkv_decode_attention(const bkv_cache* cache, const uint16_t* queries, int32_t G,
+                             float scale, float* out, int32_t* status, bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!queries || !out) return BKV_ERR_NULL;
+    if (G < 1 || G > BKV_MAX_QUERY_HEADS) return BKV_ERR_INVALID;
+    if (!aligned(queries, 16) || !aligned(out, 16) || (status && !aligned(status, 4)))
+        return BKV_ERR_INVALID;
+    return hip_status(launch_decode_attention(v, queries, G, scale, out, status,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, size_t* bytes) {
     CacheView v;
     int32_t e = check_cache(cache, &v);

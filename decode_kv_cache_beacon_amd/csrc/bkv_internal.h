@@ -144,6 +144,8 @@ hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const i
 hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
                                const int32_t* pass_idx, int rows, uint32_t* scores, int stride,
                                Check ck, int32_t* status, hipStream_t s);
+hipError_t launch_decode_attention(const CacheView& c, const uint16_t* q, int G, float scale,
+                                   float* out, int32_t* status, hipStream_t s);
 hipError_t launch_page_retain(const CacheView& c, const void* scores, int kind, int stride,
                               int rows, int budget, int32_t* keep_pages, int32_t* block_table_out,
                               int32_t* seq_len_out, int32_t* freed, Check ck, int32_t* status,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 4
+#define BKV_ABI_VERSION 5
 
 typedef void* bkv_stream_t; /* hipStream_t */
 
@@ -81,6 +81,7 @@ enum { BKV_ROWS_PER_HEAD = 0, BKV_ROWS_PER_LAYER_REQUEST = 1, BKV_ROWS_PER_REQUE
 
 #define BKV_MAX_BEACONS 256
 #define BKV_MAX_CANDIDATES 32768 /* largest score_stride bkv_topk_select accepts */
+#define BKV_MAX_QUERY_HEADS 8     /* largest G bkv_decode_attention accepts */
 
 /* A paged bf16 KV cache (vLLM-style pools, one K and one V pool per layer).
  * Layer pool l holds bf16 [num_blocks][n_kv_heads][block_size][head_dim];
@@ -244,6 +245,19 @@ int32_t bkv_page_retain(const bkv_cache* cache, const void* scores, int32_t scor
                         int32_t score_stride, int32_t score_rows, int32_t budget,
                         int32_t* keep_pages, int32_t* block_table_out, int32_t* seq_len_out,
                         int32_t* freed_blocks, int32_t* status, bkv_stream_t stream);
+
+/* Decode attention over the (compacted) cache: the step every selector hands
+ * its cache to (Random Attention article, section "发现四": the selectors share
+ * the attention kernels and the paging).  For every head-cache hc and query
+ * head g < G (1 <= G <= BKV_MAX_QUERY_HEADS), over the slots n < N of its
+ * request:
+ *   s_n = scale * (q . k_n),  out[hc][g][:] = sum_n softmax(s)_n v_n
+ * with fp32 products and sums (bf16 inputs); N = 0 gives zeros.  queries bf16
+ * [HC][G][128], out fp32 [HC][G][128], both 16-byte aligned.  Slot order does
+ * not matter: keys are stored with their positions already applied, so after
+ * compaction set seq_len to the kept count and attend. */
+int32_t bkv_decode_attention(const bkv_cache* cache, const uint16_t* queries, int32_t G,
+                             float scale, float* out, int32_t* status, bkv_stream_t stream);
 
 /* One whole eviction pass at a synchronized batch point: maintenance,
  * scoring, selection and compaction for every layer, request and head. */

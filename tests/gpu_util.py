@@ -27,6 +27,13 @@ SCORE_ATOL = 1e-30
 # total ~475 u = 2.8e-5 per cosine; the chosen row is then within 2 x 2.8e-5
 # of the best cosine.
 ASSIGN_TOL = 6e-5
+# Decode attention, |gpu - oracle| <= ATT_TOL * max |v| of the head-cache: the
+# fp32 logit (128 exact bf16 products, fp32 sums) is off by at most ~128 u |q||k|
+# scale, at most ~3e-4 in log units for these inputs; a weight p = exp(s - m)
+# then carries that relative error, plus ~1e-6 from exp2 and the rescalings,
+# and sum_n p_n v_n / sum_n p_n inherits it times max |v|.  1e-3 leaves a
+# margin of three over that worst case.
+ATT_TOL = 1e-3
 
 
 def hc_index(R, H, layer, req, head):
@@ -78,6 +85,11 @@ def check_selection(gpu_keep, ref_keep, ref_scores, N, P, B, where=""):
         assert abs(s - boundary) <= SCORE_RTOL * abs(boundary) + SCORE_ATOL, (
             f"{where}: slot {n} differs with oracle score {s} vs boundary {boundary}")
     return len(diff)
+
+
+def bf16_values(bits):
+    """float32 values of bf16 bit patterns."""
+    return (np.asarray(bits, np.uint32) << 16).view(np.float32)
 
 
 def keep_rows(keep_row):

@@ -19,7 +19,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     lib = ctypes.CDLL(bk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 4
+    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 5
     for code in range(0, 9):
         s = bk.bkv_status_string(code)
         assert s and s != "unknown status code"
@@ -105,6 +105,19 @@ def test_select_compact_random_validation():
     assert rnd(ctypes.byref(c), 1, FAKE, FAKE, 0, FAKE, 0, None, None) == bk.BKV_ERR_INVALID
     assert rnd(ctypes.byref(c), 1, FAKE, FAKE, -1, FAKE, 160, None, None) == bk.BKV_ERR_INVALID
     assert rnd(ctypes.byref(c), 1, FAKE, FAKE, 3, FAKE, 160, None, None) == bk.BKV_ERR_INVALID
+
+
+def test_decode_attention_validation():
+    c = _cache()
+    f = bk._lib.bkv_decode_attention
+    assert f(ctypes.byref(c), FAKE, 0, 0.1, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert f(ctypes.byref(c), FAKE, 9, 0.1, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert f(ctypes.byref(c), None, 4, 0.1, FAKE, None, None) == bk.BKV_ERR_NULL
+    assert f(ctypes.byref(c), FAKE, 4, 0.1, None, None, None) == bk.BKV_ERR_NULL
+    assert f(ctypes.byref(c), FAKE + 8, 4, 0.1, FAKE, None, None) == bk.BKV_ERR_INVALID
+    assert f(ctypes.byref(c), FAKE, 4, 0.1, FAKE + 4, None, None) == bk.BKV_ERR_INVALID
+    assert f(ctypes.byref(_cache(head_dim=64)), FAKE, 4, 0.1, FAKE, None, None) == \
+        bk.BKV_ERR_UNSUPPORTED
 
 
 def test_page_retain_validation():

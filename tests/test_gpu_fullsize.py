@@ -3,7 +3,8 @@ serving workload (36864 head-caches, 2112 cached keys each, budget 2048,
 128 beacons, 256 buffered queries per head-cache), launched exactly as the
 benchmark launches it (one bkv_evict_pass over all head-caches, scores in a
 [HC, 1088] buffer; the assignment output is also requested here so the
-maintenance step can be replayed).
+maintenance step can be replayed), then decode attention over the compacted
+cache as the benchmark times it.
 
 The oracle cannot replay 36864 head-caches in seconds, so it checks a spread
 sample of them one by one (first and last head-caches, and a seeded draw over
@@ -16,7 +17,8 @@ import torch
 
 import oracle
 from decode_kv_cache_beacon_amd import synth
-from tests.gpu_util import ASSIGN_TOL, check_scores, check_selection, keep_rows
+from tests.gpu_util import (ASSIGN_TOL, ATT_TOL, bf16_values, check_scores, check_selection,
+                            keep_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,6 +114,26 @@ def test_full_size_serving_pass():
         vo = gather_head(batch.v_pools[layer], bt[r], h, n)
         assert np.array_equal(ko[:nk], oracle.kv_compact(x["keys"], k)), hc
         assert np.array_equal(vo[:nk], oracle.kv_compact(x["vals"], k)), hc
+
+    # the consumer: decode attention over the compacted cache (length = kept count)
+    say("full size attention")
+    batch.seq_len.clamp_(max=B)
+    ql = batch.queries[:, -1].contiguous()
+    out = torch.full((HC, ql.shape[1], 128), float("nan"), device=dev)
+    st2 = torch.zeros(1, dtype=torch.int32, device=dev)
+    bk.bkv_decode_attention(cache, ql, out, status=st2, check=False)
+    torch.cuda.synchronize()
+    assert int(st2.item()) == 0
+    on, qn = out.cpu().numpy(), synth.bits(ql)
+    assert np.isfinite(on).all()
+    for hc in sample:
+        layer, r, h = hc // (R * H), (hc // H) % R, hc % H
+        nk = min(int(N[r]), B)
+        keys = gather_head(batch.k_pools[layer], bt[r], h, nk)
+        vals = gather_head(batch.v_pools[layer], bt[r], h, nk)
+        ref = oracle.decode_attention(qn[hc], keys, vals)
+        vmax = float(np.abs(bf16_values(vals)).max())
+        assert np.abs(on[hc] - ref).max() <= ATT_TOL * vmax, hc
 
 
 @pytest.mark.parametrize("selector", ["beacon", "random"])

@@ -8,8 +8,8 @@ import torch
 
 import oracle
 from decode_kv_cache_beacon_amd import synth
-from tests.gpu_util import (ASSIGN_TOL, check_scores, check_selection, device_cache, hc_index,
-                            host_pools, keep_rows)
+from tests.gpu_util import (ASSIGN_TOL, ATT_TOL, bf16_values, check_scores, check_selection,
+                            device_cache, hc_index, host_pools, keep_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -623,6 +623,60 @@ def test_evict_pass_page_retention(selector):
     say("pass pages", selector)
     wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=512, prompt_len=200, seq_len=584)
     _page_pass_case(wl, N=[584, 541, 400], P=[200, 333, 100], B=512, selector=selector)
+
+
+# ------------------------------------------------------------------ decode attention
+def _check_attention(out, q, keys, vals, where):
+    ref = oracle.decode_attention(q, keys, vals)
+    vmax = float(np.abs(bf16_values(vals)).max()) if len(vals) else 1.0
+    err = np.abs(np.asarray(out, np.float64) - ref).max()
+    assert err <= ATT_TOL * vmax, (where, err, vmax)
+
+
+@pytest.mark.parametrize("G", [1, 3, 4, 8])
+def test_decode_attention_parity(G):
+    say("attention G", G)
+    wl = small(n_layers=2, n_requests=6, n_kv_heads=2, budget=512, prompt_len=100, seq_len=576,
+               group=G)
+    batch = synth.make_batch(wl)
+    N = [576, 0, 1, 5, 17, 331]
+    cache = device_cache(batch, N, [0] * 6)
+    k_in, v_in = host_pools(cache)
+    bt = batch.block_table.numpy()
+    q = batch.queries[:, -1].contiguous().cuda()         # the last buffered decode step
+    out = torch.full((cache.n_head_caches, G, 128), float("nan")).cuda()
+    bk.bkv_decode_attention(cache, q, out)
+    on, qn = out.cpu().numpy(), synth.bits(q)
+    for hc, layer, r, h in head_iter(cache):
+        keys = oracle.gather_paged(k_in[layer], bt[r], h, N[r])
+        vals = oracle.gather_paged(v_in[layer], bt[r], h, N[r])
+        _check_attention(on[hc], qn[hc], keys, vals, f"G {G} hc {hc} N {N[r]}")
+
+
+def test_decode_attention_after_compaction():
+    """The consumer of the pass: attention over the compacted cache (length set to the
+    kept count) equals attention over the kept rows in their original slots."""
+    say("attention after compaction")
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=512, prompt_len=200, seq_len=576)
+    batch = synth.make_batch(wl)
+    N, P, B = [576, 541, 400], [200, 333, 100], 512
+    cache = device_cache(batch, N, P)
+    k_in, v_in = host_pools(cache)
+    bt = batch.block_table.numpy()
+    q, b, c = batch.queries.cuda(), batch.beacons.cuda(), batch.counts.cuda()
+    keep = torch.full((cache.n_head_caches, B), -7, dtype=torch.int32).cuda()
+    bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                      keep_out=keep)
+    cache.seq_len.copy_(torch.tensor([min(n, B) for n in N], dtype=torch.int32))
+    ql = batch.queries[:, -1].contiguous().cuda()
+    out = torch.zeros((cache.n_head_caches, ql.shape[1], 128)).cuda()
+    bk.bkv_decode_attention(cache, ql, out)
+    on, qn, kn = out.cpu().numpy(), synth.bits(ql), keep.cpu().numpy()
+    for hc, layer, r, h in head_iter(cache):
+        kp = keep_rows(kn[hc])
+        keys = oracle.gather_paged(k_in[layer], bt[r], h, N[r])[kp]
+        vals = oracle.gather_paged(v_in[layer], bt[r], h, N[r])[kp]
+        _check_attention(on[hc], qn[hc], keys, vals, f"compacted hc {hc}")
 
 
 def test_evict_pass_tiny_one_shot():
