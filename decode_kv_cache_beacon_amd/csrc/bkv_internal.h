@@ -53,11 +53,23 @@ struct Check {
                     // one selection spans every layer, every layer's pools must be aligned
 };
 
-// Validates request r.  Every thread of the block must call it (it
-// synchronises); the result is uniform.  Errors are OR-ed into *status by
-// thread 0.
+// OR of a predicate over the threads that check a request: the whole
+// workgroup, or only the calling wave (kernels whose waves serve different
+// head-caches, or one-wave workgroups that need no LDS for it).
+template <bool kWave_>
+__device__ __forceinline__ bool any_thread(bool p) {
+    if constexpr (kWave_) return __ballot(p) != 0ull;
+    else return __syncthreads_or(p) != 0;
+}
+
+// Validates request r.  Every thread of the block (kWaveOnly: of the wave)
+// must call it; the result is uniform.  Errors are OR-ed into *status by
+// thread (lane) 0.
+template <bool kWaveOnly = false>
 __device__ inline bool request_ok(const CacheView& c, int layer, int r, const Check& ck,
                                   int32_t* status) {
+    const int tid = kWaveOnly ? (int)(threadIdx.x % kWave) : (int)threadIdx.x;
+    const int nthreads = kWaveOnly ? kWave : (int)blockDim.x;
     const int N = c.seq_len[r];
     const int P = c.prompt_len[r];
     int err = 0;
@@ -75,22 +87,22 @@ __device__ inline bool request_ok(const CacheView& c, int layer, int r, const Ch
     bool bad = false;
     if (ck.pages) {
         bool mis = false;
-        for (int l = threadIdx.x; l < c.L; l += blockDim.x)
+        for (int l = tid; l < c.L; l += nthreads)
             mis |= ((c.k_pools[l] | c.v_pools[l]) & 15u) != 0;
-        if (__syncthreads_or(mis)) err |= 1 << BKV_ERR_INVALID;
+        if (any_thread<kWaveOnly>(mis)) err |= 1 << BKV_ERR_INVALID;
     }
     if (ck.blocks) {
         if (((c.k_pools[layer] | c.v_pools[layer]) & 15u) != 0) err |= 1 << BKV_ERR_INVALID;
         const int nb = (err & (1 << BKV_ERR_LENGTH)) ? 0 : (N + kBlock - 1) / kBlock;
         const int32_t* row = c.block_table + (size_t)r * c.max_blocks;
-        for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+        for (int i = tid; i < nb; i += nthreads) {
             const int b = row[i];
             bad |= (b < 0) || ((int64_t)b >= c.num_blocks);
         }
     }
-    bad = __syncthreads_or(bad);
+    bad = any_thread<kWaveOnly>(bad);
     if (bad) err |= 1 << BKV_ERR_BLOCK_TABLE;
-    if (err && threadIdx.x == 0) raise_status(status, err);
+    if (err && tid == 0) raise_status(status, err);
     return err == 0;
 }
 

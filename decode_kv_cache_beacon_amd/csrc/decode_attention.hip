@@ -62,26 +62,6 @@ __device__ __forceinline__ float dot8(const u32x4& q, const u32x4& k, float acc)
     return acc;
 }
 
-// Per-wave request checks (the workgroup's four waves may serve different
-// requests, so no block-wide barrier is used).  The result is uniform.
-__device__ bool wave_request_ok(const CacheView& c, int layer, int r, int lane, int32_t* status) {
-    const int N = c.seq_len[r];
-    const int P = c.prompt_len[r];
-    int err = 0;
-    if (P < 0 || N < P || N > c.max_blocks * kBlock) err |= 1 << BKV_ERR_LENGTH;
-    if (((c.k_pools[layer] | c.v_pools[layer]) & 15u) != 0) err |= 1 << BKV_ERR_INVALID;
-    const int nb = (err & (1 << BKV_ERR_LENGTH)) ? 0 : (N + kBlock - 1) / kBlock;
-    const int32_t* row = c.block_table + (size_t)r * c.max_blocks;
-    bool bad = false;
-    for (int i = lane; i < nb; i += kWave) {
-        const int b = row[i];
-        bad |= (b < 0) || ((int64_t)b >= c.num_blocks);
-    }
-    if (__ballot(bad)) err |= 1 << BKV_ERR_BLOCK_TABLE;
-    if (err && lane == 0) raise_status(status, err);
-    return err == 0;
-}
-
 template <int GP>  // query heads per KV head, rounded up (1, 2, 4 or 8)
 __global__ __launch_bounds__(kThreads) void decode_attention_kernel(
     CacheView c, const uint16_t* __restrict__ q, int G, float scale, float* __restrict__ out,
@@ -93,7 +73,8 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(
     const int hc = blockIdx.x * kWavesPerBlock + w;
     if (hc >= HC) return;  // the whole wave leaves; nothing below waits on other waves
     const HeadIdx x = split_hc(c, hc);
-    if (!wave_request_ok(c, x.layer, x.req, lane, status)) return;
+    // the workgroup's four waves may serve different requests: checks per wave
+    if (!request_ok<true>(c, x.layer, x.req, Check{-1, -1, 1, 0}, status)) return;
     const int N = c.seq_len[x.req];
     const int rr = lane >> 4;          // slot within an instruction
     const int cc = lane & 15;          // 16-byte chunk of the row
