@@ -34,14 +34,14 @@ def gather_head(pool, bt_row, h, N):
     return synth.bits(rows)
 
 
-def test_full_size_serving_pass():
-    if not torch.cuda.is_available():
-        pytest.skip("needs a GPU")
+def _full_size_beacon_pass(wl, n_sample, sample_seed, attention):
+    """One beacon bkv_evict_pass over every head-cache of workload wl, launched
+    as the benchmark launches it; properties on all head-caches, the oracle on
+    a spread sample of n_sample + 2 of them."""
     from decode_kv_cache_beacon_amd import beaconkv as bk
 
-    wl = synth.WORKLOADS["serving_r128"]
     dev = torch.device("cuda")
-    say("full size", wl.name, "generate")
+    say("full size", wl.name, "B", wl.budget, "generate")
     batch = synth.make_batch(wl, dev)
     cache = bk.PagedCache(batch.k_pools, batch.v_pools, batch.block_table, batch.seq_len,
                           batch.prompt_len)
@@ -52,8 +52,8 @@ def test_full_size_serving_pass():
     stride = int((N - P).max())
     T, G = wl.steps, wl.group
 
-    rng = np.random.default_rng(2024)
-    sample = sorted({0, HC - 1, *rng.choice(HC, 22, replace=False).tolist()})
+    rng = np.random.default_rng(sample_seed)
+    sample = sorted({0, HC - 1, *rng.choice(HC, n_sample, replace=False).tolist()})
     before = {}
     bt = batch.block_table
     for hc in sample:
@@ -115,6 +115,8 @@ def test_full_size_serving_pass():
         assert np.array_equal(ko[:nk], oracle.kv_compact(x["keys"], k)), hc
         assert np.array_equal(vo[:nk], oracle.kv_compact(x["vals"], k)), hc
 
+    if not attention:
+        return
     # the consumer: decode attention over the compacted cache (length = kept count)
     say("full size attention")
     batch.seq_len.clamp_(max=B)
@@ -134,6 +136,83 @@ def test_full_size_serving_pass():
         ref = oracle.decode_attention(qn[hc], keys, vals)
         vmax = float(np.abs(bf16_values(vals)).max())
         assert np.abs(on[hc] - ref).max() <= ATT_TOL * vmax, hc
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+
+
+def test_full_size_serving_pass():
+    _need_gpu()
+    _full_size_beacon_pass(synth.WORKLOADS["serving_r128"], 22, 2024, attention=True)
+
+
+@pytest.mark.parametrize("name,budget", [("qwen3_4b_r16", 2048), ("qwen3_32b_r32", 1024),
+                                         ("qwen3_32b_r32", 2048), ("qwen3_32b_r32", 4096),
+                                         ("long_prompt_r128", 3072)])
+def test_full_size_other_workloads(name, budget):
+    """The other workload shapes at their full sizes (the 64-layer, K = 256 batch
+    over its budget sweep, steady state N = B + 64), each on 8 + 2 sampled
+    head-caches."""
+    _need_gpu()
+    wl = synth.WORKLOADS[name]
+    if budget != wl.budget:
+        wl = wl.with_(budget=budget, seq_len=budget + wl.window)
+    _full_size_beacon_pass(wl, 8, budget, attention=False)
+    torch.cuda.empty_cache()
+
+
+def test_full_size_random_pass():
+    """The benchmark's random-selector pass at full size: draws, keep lists and
+    moved rows of a spread sample of head-caches, bit-exact."""
+    _need_gpu()
+    from decode_kv_cache_beacon_amd import beaconkv as bk
+
+    wl = synth.WORKLOADS["serving_r128"]
+    dev = torch.device("cuda")
+    say("full size random", "generate")
+    batch = synth.make_batch(wl, dev)
+    cache = bk.PagedCache(batch.k_pools, batch.v_pools, batch.block_table, batch.seq_len,
+                          batch.prompt_len)
+    L, R, H = cache.n_layers, cache.n_requests, cache.n_kv_heads
+    HC, B = cache.n_head_caches, wl.budget
+    N = batch.seq_len.cpu().numpy()
+    P = batch.prompt_len.cpu().numpy()
+    stride = int((N - P).max())
+    rng = np.random.default_rng(99)
+    sample = sorted({0, HC - 1, *rng.choice(HC, 16, replace=False).tolist()})
+    bt = batch.block_table
+    before = {}
+    for hc in sample:
+        layer, r, h = hc // (R * H), (hc // H) % R, hc % H
+        before[hc] = (gather_head(batch.k_pools[layer], bt[r], h, int(N[r])),
+                      gather_head(batch.v_pools[layer], bt[r], h, int(N[r])))
+    rid = torch.arange(R, dtype=torch.int64, device=dev) * 7 + 3
+    pss = torch.full((R,), 1003, dtype=torch.int32, device=dev)
+    u = torch.zeros((HC, stride), dtype=torch.int32, device=dev)
+    keep = torch.full((HC, B), -7, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    say("full size random pass")
+    bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed, request_ids=rid,
+                      pass_idx=pss, scores_out=u, keep_out=keep, score_stride=stride,
+                      status=status, check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    kn = keep.cpu().numpy()
+    assert (kn >= 0).all() and (np.diff(kn, axis=1) > 0).all()
+    for hc in sample:
+        layer, r, h = hc // (R * H), (hc // H) % R, hc % H
+        n, p = int(N[r]), int(P[r])
+        say("full size random head-cache", hc)
+        draw = oracle.random_score(wl.seed, int(rid[r]), 1003, layer, h, n, p)
+        assert np.array_equal(u[hc, : n - p].cpu().numpy().view(np.uint32), draw), hc
+        k = oracle.topk_select(draw, n, p, B)
+        assert np.array_equal(kn[hc], k), hc
+        ko = gather_head(batch.k_pools[layer], bt[r], h, n)
+        vo = gather_head(batch.v_pools[layer], bt[r], h, n)
+        assert np.array_equal(ko[:B], oracle.kv_compact(before[hc][0], k)), hc
+        assert np.array_equal(vo[:B], oracle.kv_compact(before[hc][1], k)), hc
 
 
 @pytest.mark.parametrize("selector", ["beacon", "random"])
