@@ -79,6 +79,17 @@ def algorithmic_bytes(wl, N, P, moved_rows, hc_per_req):
     return {"beacon_update": upd, "beacon_score": sc, "topk_select": sel, "kv_compact": cmp_}
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, budget_s):
     """The oracle, as it stands, on one layer of the same workload (CPU-drawn
     synthetic data of the same shapes), scaled to a full pass."""
@@ -126,6 +137,7 @@ def cpu_baseline(wl, budget_s):
         "value": 1.0 / pass_s,
         "unit": "passes/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{done} head-cache eviction passes: the {min(done, hc_total)} head-caches "
                    f"of layers 0-{L - 1} (CPU-drawn data of the same shapes) swept {sweeps} "
@@ -162,10 +174,14 @@ COPY_SYMBOL = "__amd_rocclr_copyBuffer"
 PROFILE_CMDS = {
     "trace": ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -f csv -d <prof-dir> "
               "-o bench -- python3 <repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline "
-              "--no-shared --count-cap 0"),
+              "--no-shared --no-side --count-cap 0"),
     "pmc": ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} -f csv -d <pmc-dir>/{c} -o {c} -- "
             "python3 <repo>/bench.py --steps 2 --warmup 0 --no-random --no-cpu-baseline "
-            "--no-shared --no-pages --count-cap 0"),
+            "--no-shared --no-pages --no-side --count-cap 0"),
+    "pmc_mfma": ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+                 "-f csv -d <pmc-dir>/MFMA -o MFMA -- python3 <repo>/bench.py --steps 2 "
+                 "--warmup 0 --no-random --no-cpu-baseline --no-shared --no-pages --no-side "
+                 "--count-cap 0"),
     "summary": "python bench.py --summarize-profiles <prof-dir> <pmc-dir>",
 }
 
@@ -256,8 +272,80 @@ def summarize_profiles(prof_dir, pmc_dir, workload):
         f.write("\n".join(lines) + "\n")
     with open(os.path.join(out, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
+
+    # MFMA utilisation (optional third counter run)
+    mfma = glob.glob(os.path.join(pmc_dir, "MFMA", "*counter_collection.csv"))
+    if mfma:
+        per = {}
+        for r in csv.DictReader(open(mfma[0])):
+            k = kid(r["Kernel_Name"])
+            if not k:
+                continue
+            d = per.setdefault(k, {}).setdefault(r["Counter_Name"], {})
+            key = r.get("Dispatch_Id") or r.get("Correlation_Id") or len(d)
+            d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+        lines = [f"# MFMA utilisation per launch, workload {workload}", "",
+                 "rocprofv3's derived MfmaUtil (MFMA-busy cycles summed over SIMDs, over "
+                 "GPU-active cycles times the SIMD count, in percent) and the bf16 MFMA "
+                 "operations (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = flop), mean over the "
+                 "dispatches of the beacon passes; TFLOP/s uses the kernel-trace mean duration. "
+                 f"Dense bf16 peak {MFMA_BF16_PEAK_TFLOPS:.0f} TFLOP/s.", "", "Command:", "",
+                 "    " + PROFILE_CMDS["pmc_mfma"], "",
+                 "| kernel | MfmaUtil % | bf16 MFMA flop per launch | TFLOP/s | % of peak |",
+                 "|---|---|---|---|---|"]
+        for k in KERNEL_SOURCES:
+            if k not in per:
+                continue
+            util = per[k].get("MfmaUtil", {})
+            mops = per[k].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", {})
+            u = statistics.mean(util.values()) if util else float("nan")
+            flop = statistics.mean(mops.values()) * 512 if mops else float("nan")
+            tf = flop / (statistics.mean(dur[k]) * 1e-3) / 1e12 if k in dur and mops else float("nan")
+            lines.append(f"| {k} | {u:.1f} | {flop:.3e} | {tf:.1f} | "
+                         f"{100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f} |")
+        with open(os.path.join(out, f"{workload}_mfma_counters.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
     print(f"wrote profiles/{workload}_kernel_trace.md, profiles/{workload}_hbm_counters.md, "
           "profiles/traffic.json")
+
+
+def side_pass(bk, synth, wl, steps, warmup, dev):
+    """Mean per-kernel milliseconds of `steps` whole beacon passes over a
+    freshly generated workload (no refill between passes: the lengths stay,
+    so every pass does the same work)."""
+    batch = synth.make_batch(wl, dev)
+    cache = bk.PagedCache(batch.k_pools, batch.v_pools, batch.block_table, batch.seq_len,
+                          batch.prompt_len)
+    HC, B = cache.n_head_caches, wl.budget
+    N = batch.seq_len.cpu().tolist()
+    P = batch.prompt_len.cpu().tolist()
+    stride = max(n - p for n, p in zip(N, P))
+    scores = torch_mod().zeros((HC, stride), dtype=torch_mod().float32, device=dev)
+    keep = torch_mod().zeros((HC, B), dtype=torch_mod().int32, device=dev)
+    status = torch_mod().zeros(1, dtype=torch_mod().int32, device=dev)
+    runs = []
+    for s in range(warmup + steps):
+        ev = [torch_mod().cuda.Event(enable_timing=True) for _ in range(5)]
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=batch.queries,
+                          beacons=batch.beacons, counts=batch.counts, window=wl.window,
+                          bonus=wl.bonus, scores_out=scores, keep_out=keep, score_stride=stride,
+                          status=status, check=False, timing_events=ev)
+        if s >= warmup:
+            runs.append(ev)
+    torch_mod().cuda.synchronize()
+    bk.check_status(status, f"{wl.name} side passes")
+    names = ["beacon_update", "beacon_score", "topk_select", "kv_compact"]
+    kms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in runs) / len(runs)
+           for i, n in enumerate(names)}
+    ms = sum(e[0].elapsed_time(e[4]) for e in runs) / len(runs)
+    del batch, cache, scores, keep
+    torch_mod().cuda.empty_cache()
+    return ms, kms, N, P
+
+
+def torch_mod():
+    import torch
+    return torch
 
 
 def main():
@@ -268,6 +356,8 @@ def main():
     ap.add_argument("--workload", default="serving_r128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-random", action="store_true", help="skip the random-selector A/B")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the one-shot side workloads (single head, 32k slots)")
     ap.add_argument("--no-pages", action="store_true",
                     help="skip the page-retention (whole pages, no row moves) passes")
     ap.add_argument("--no-shared", action="store_true",
@@ -384,7 +474,8 @@ def main():
     total_bytes = sum(abytes.values())
     ssc_bytes = total_bytes - abytes["beacon_update"]
     ssc_ms = kms["beacon_score"] + kms["topk_select"] + kms["kv_compact"]
-    score_flops = 2.0 * 2 * wl.n_beacons * 128 * sum(N) * hc_per_req   # two logit passes
+    # logits of every key (phase 1) and of every candidate (phase 2)
+    score_flops = 2.0 * wl.n_beacons * 128 * hc_per_req * sum(n + (n - p) for n, p in zip(N, P))
     update_flops = 2.0 * wl.steps * wl.group * wl.n_beacons * 128 * HC
 
     kernels = {}
@@ -392,7 +483,13 @@ def main():
         gbps = abytes[n] / (kms[n] * 1e-3) / 1e9
         kernels[n] = {"ms": round(kms[n], 4), "algorithmic_bytes": int(abytes[n]),
                       "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    for n in names:
+        tb = stored_traffic(n)
+        if tb:
+            kernels[n]["traffic_gbps"] = round(tb / (kms[n] * 1e-3) / 1e9, 1)
     kernels["beacon_score"]["mfma_tflops"] = round(score_flops / (kms["beacon_score"] * 1e-3) / 1e12, 1)
+    kernels["beacon_score"]["mfma_frac"] = round(
+        score_flops / (kms["beacon_score"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
     kernels["beacon_update"]["valu_tflops"] = round(update_flops / (kms["beacon_update"] * 1e-3) / 1e12, 2)
 
     dom = max(names, key=lambda n: kms[n])
@@ -415,6 +512,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "layer_passes_per_s": round(1000.0 / ms * wl.n_layers, 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -633,7 +731,32 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 5 * 2 * src.numel() * 2 / (e0.elapsed_time(e1) * 1e-3) / 1e9
     result["copy_reference_gbps"] = round(copy_gbps, 1)
+    result["copy_ceiling_frac"] = round(result["hbm_gbps"] / copy_gbps, 4)
+    for n in names:
+        result["kernels"][n]["copy_frac"] = round(result["kernels"][n]["gbps"] / copy_gbps, 4)
     del src, dst
+
+    # the other configurations' one-shot shapes, reported beside the line
+    if not args.no_side:
+        twl = synth.WORKLOADS["tiny"]
+        tms, tk, _, _ = side_pass(bk, synth, twl, 20, 3, dev)
+        result["tiny_one_shot"] = {
+            "us_per_pass": round(tms * 1e3, 1),
+            "kernel_us": {k: round(v * 1e3, 1) for k, v in tk.items()},
+            "note": "one head-cache, N = 4096 (512 prompt), K = 64, B = 1024, 256 queries: "
+                    "latency-bound, one workgroup per kernel"}
+        owl = synth.WORKLOADS["qwen3_32b_r32"].with_(n_layers=1, seq_len=32768)
+        oms, ok, oN, oP = side_pass(bk, synth, owl, 5, 1, dev)
+        ohc = owl.n_head_caches
+        oflops = 2.0 * owl.n_beacons * owl.head_dim * ohc * (oN[0] + (oN[0] - oP[0]))
+        otf = oflops / (ok["beacon_score"] * 1e-3) / 1e12
+        result["one_shot_32k"] = {
+            "ms_per_pass": round(oms, 4), "kernel_ms": {k: round(v, 4) for k, v in ok.items()},
+            "score_mfma_tflops": round(otf, 1),
+            "score_mfma_frac": round(otf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "note": f"one layer of the 64-layer shape: {ohc} head-caches, N = 32768 "
+                    f"({oP[0]} prompt), K = {owl.n_beacons}, B = {owl.budget}, "
+                    f"G = {owl.group}; scoring flops count both logit passes"}
 
     if args.copy_calibration:
         src = torch.empty(1 << 31, dtype=torch.int16, device=dev)

@@ -163,6 +163,16 @@ def test_full_size_other_workloads(name, budget):
     torch.cuda.empty_cache()
 
 
+def test_full_size_one_shot_32k():
+    """One layer of the 64-layer, K = 256 shape as a one-shot pass over 32768
+    slots (256 head-caches, 32256 candidates each), as the benchmark's side
+    measurement runs it; 2 + 2 sampled head-caches."""
+    _need_gpu()
+    wl = synth.WORKLOADS["qwen3_32b_r32"].with_(n_layers=1, seq_len=32768)
+    _full_size_beacon_pass(wl, 2, 32768, attention=False)
+    torch.cuda.empty_cache()
+
+
 def test_full_size_random_pass():
     """The benchmark's random-selector pass at full size: draws, keep lists and
     moved rows of a spread sample of head-caches, bit-exact."""
