@@ -309,7 +309,7 @@ def summarize_profiles(prof_dir, pmc_dir, workload):
           "profiles/traffic.json")
 
 
-def side_pass(bk, synth, wl, steps, warmup, dev):
+def side_pass(torch, bk, synth, wl, steps, warmup, dev):
     """Mean per-kernel milliseconds of `steps` whole beacon passes over a
     freshly generated workload (no refill between passes: the lengths stay,
     so every pass does the same work)."""
@@ -320,32 +320,27 @@ def side_pass(bk, synth, wl, steps, warmup, dev):
     N = batch.seq_len.cpu().tolist()
     P = batch.prompt_len.cpu().tolist()
     stride = max(n - p for n, p in zip(N, P))
-    scores = torch_mod().zeros((HC, stride), dtype=torch_mod().float32, device=dev)
-    keep = torch_mod().zeros((HC, B), dtype=torch_mod().int32, device=dev)
-    status = torch_mod().zeros(1, dtype=torch_mod().int32, device=dev)
+    scores = torch.zeros((HC, stride), dtype=torch.float32, device=dev)
+    keep = torch.zeros((HC, B), dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
     runs = []
     for s in range(warmup + steps):
-        ev = [torch_mod().cuda.Event(enable_timing=True) for _ in range(5)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=batch.queries,
                           beacons=batch.beacons, counts=batch.counts, window=wl.window,
                           bonus=wl.bonus, scores_out=scores, keep_out=keep, score_stride=stride,
                           status=status, check=False, timing_events=ev)
         if s >= warmup:
             runs.append(ev)
-    torch_mod().cuda.synchronize()
+    torch.cuda.synchronize()
     bk.check_status(status, f"{wl.name} side passes")
     names = ["beacon_update", "beacon_score", "topk_select", "kv_compact"]
     kms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in runs) / len(runs)
            for i, n in enumerate(names)}
     ms = sum(e[0].elapsed_time(e[4]) for e in runs) / len(runs)
     del batch, cache, scores, keep
-    torch_mod().cuda.empty_cache()
+    torch.cuda.empty_cache()
     return ms, kms, N, P
-
-
-def torch_mod():
-    import torch
-    return torch
 
 
 def main():
@@ -739,14 +734,14 @@ def main():
     # the other configurations' one-shot shapes, reported beside the line
     if not args.no_side:
         twl = synth.WORKLOADS["tiny"]
-        tms, tk, _, _ = side_pass(bk, synth, twl, 20, 3, dev)
+        tms, tk, _, _ = side_pass(torch, bk, synth, twl, 20, 3, dev)
         result["tiny_one_shot"] = {
             "us_per_pass": round(tms * 1e3, 1),
             "kernel_us": {k: round(v * 1e3, 1) for k, v in tk.items()},
             "note": "one head-cache, N = 4096 (512 prompt), K = 64, B = 1024, 256 queries: "
                     "latency-bound, one workgroup per kernel"}
         owl = synth.WORKLOADS["qwen3_32b_r32"].with_(n_layers=1, seq_len=32768)
-        oms, ok, oN, oP = side_pass(bk, synth, owl, 5, 1, dev)
+        oms, ok, oN, oP = side_pass(torch, bk, synth, owl, 5, 1, dev)
         ohc = owl.n_head_caches
         oflops = 2.0 * owl.n_beacons * owl.head_dim * ohc * (oN[0] + (oN[0] - oP[0]))
         otf = oflops / (ok["beacon_score"] * 1e-3) / 1e12

@@ -2,7 +2,9 @@
  * beaconkv.h -- C ABI of libbeaconkv.so: the decode-time KV-cache eviction
  * pass (beacon maintenance, beacon scoring, random scoring, top-B selection,
  * order-preserving compaction) as hand-written HIP kernels for MI355X
- * (gfx950, CDNA4).
+ * (gfx950, CDNA4), with its variants (a count cap on the beacon update, one
+ * selection shared by the heads of a layer, whole-page retention through the
+ * block table) and the decode attention that consumes the compacted cache.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -37,7 +39,10 @@
  *    the prompt's KV is always kept, the generated KV is sampled independently
  *    per head and the top-K kept, at the cost of one random draw and one
  *    top-K; section "发现四": every selector ends in the same cache compaction,
- *    run for a batch of requests at a synchronized point every 64 tokens.
+ *    run for a batch of requests at a synchronized point every 64 tokens, and
+ *    shares the attention kernels; section "发现二": contiguous blocks instead
+ *    of scattered tokens, and one common set of positions for all heads, both
+ *    leave accuracy almost unchanged.
  *  Rules the pages leave open are fixed as follows (see each function):
  *  cosine nearest beacon with ties to the lowest row, MacQueen fill of empty
  *  rows, fp32 running-mean update; score(n) = max over live beacons of the
