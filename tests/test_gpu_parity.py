@@ -562,6 +562,56 @@ def test_page_retain_standalone():
     assert np.array_equal(cache.block_table.cpu().numpy(), bt_in)   # input table unchanged
 
 
+def test_page_retain_edge_lengths():
+    """Lengths at page boundaries: an empty request, a single slot, one partial page,
+    no prompt with a partial last page, the prompt ending exactly on a page boundary,
+    and a cache of whole pages with exactly one page over the budget."""
+    say("page retain edges")
+    wl = small(n_layers=1, n_requests=7, n_kv_heads=2, budget=64, prompt_len=0, seq_len=96)
+    batch = synth.make_batch(wl)
+    N = [0, 1, 15, 83, 96, 80, 96]
+    P = [0, 0, 3, 0, 32, 16, 64]
+    B = 64
+    cache = device_cache(batch, N, P)
+    R, M = cache.n_requests, cache.max_blocks
+    bt_in = batch.block_table.numpy().copy()
+    stride = 96
+    rng = np.random.default_rng(8)
+    f = rng.random((cache.n_head_caches, stride)).astype(np.float32)
+    kp, _, _, fr = _page_outputs(cache, B)
+    bk.bkv_page_retain(cache, torch.from_numpy(f).cuda(), B, kp, cache.block_table,
+                       cache.seq_len, fr)
+    torch.cuda.synchronize()
+    kpn, btn, sln, frn = (kp.cpu().numpy(), cache.block_table.cpu().numpy(),
+                          cache.seq_len.cpu().numpy(), fr.cpu().numpy())
+    H = cache.n_kv_heads
+    for r in range(R):
+        rows = np.stack([f[hc_index(R, H, 0, r, h), :N[r] - P[r]] for h in range(H)])
+        ref = oracle.page_select(rows.astype(np.float64), N[r], P[r], B)
+        _check_pages("edges", r, kpn[r], bt_in[r], btn[r], sln[r], frn[r], ref, N[r], M)
+
+
+def test_decode_attention_tiny_lengths():
+    """N = 1, 2, 3, 4, 5 and 16, 17 slots with 8 query heads: the masking of the rows
+    of the first and the last page."""
+    say("attention tiny lengths")
+    wl = small("qwen3_32b_r32", n_layers=1, n_requests=7, n_kv_heads=1, budget=64, seq_len=32,
+               prompt_len=0)
+    batch = synth.make_batch(wl)
+    N = [1, 2, 3, 4, 5, 16, 17]
+    cache = device_cache(batch, N, [0] * 7)
+    k_in, v_in = host_pools(cache)
+    bt = batch.block_table.numpy()
+    q = batch.queries[:, 0].contiguous().cuda()
+    out = torch.full((cache.n_head_caches, q.shape[1], 128), float("nan")).cuda()
+    bk.bkv_decode_attention(cache, q, out)
+    on, qn = out.cpu().numpy(), synth.bits(q)
+    for hc, layer, r, h in head_iter(cache):
+        keys = oracle.gather_paged(k_in[layer], bt[r], h, N[r])
+        vals = oracle.gather_paged(v_in[layer], bt[r], h, N[r])
+        _check_attention(on[hc], qn[hc], keys, vals, f"tiny N {N[r]}")
+
+
 def _page_pass_case(wl, N, P, B, selector, seed=23):
     """bkv_evict_pass with page retention, in place on the cache's block table."""
     batch = synth.make_batch(wl)
