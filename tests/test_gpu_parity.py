@@ -771,3 +771,61 @@ def test_evict_pass_skips_invalid_request_entirely():
             assert np.array_equal(k_in[layer][blk], k_out[layer][blk])
             assert np.array_equal(v_in[layer][blk], v_out[layer][blk])
     assert any(not np.array_equal(k_in[0][blk], k_out[0][blk]) for blk in btn[0])
+
+
+def test_evict_pass_replays_from_a_hip_graph():
+    """The pass allocates nothing and sets no memory, so it can be captured: a
+    captured beacon pass, replayed several times from restored inputs (eager
+    copies and synchronisations between replays), matches the eager pass
+    byte for byte every time."""
+    say("graph replay")
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=512, prompt_len=200, seq_len=576)
+    batch = synth.make_batch(wl)
+    N, P, B = [576, 541, 400], [200, 333, 100], 512
+    cache = device_cache(batch, N, P)
+    HC, S = cache.n_head_caches, cache.max_slots
+    q = batch.queries.cuda()
+    b0, c0 = batch.beacons.cuda(), batch.counts.cuda()
+    k0 = [k.clone() for k in cache.k_pools]
+    v0 = [v.clone() for v in cache.v_pools]
+    b, c = b0.clone(), c0.clone()
+    sc = torch.zeros((HC, S)).cuda()
+    keep = torch.zeros((HC, B), dtype=torch.int32).cuda()
+    st = torch.zeros(1, dtype=torch.int32).cuda()
+    ws = torch.empty(1 << 20, dtype=torch.uint8).cuda()
+
+    def restore():
+        b.copy_(b0)
+        c.copy_(c0)
+        for dst, src in zip(cache.k_pools + cache.v_pools, k0 + v0):
+            dst.copy_(src)
+
+    def run():
+        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                          scores_out=sc, keep_out=keep, status=st, check=False, workspace=ws)
+
+    run()                                   # eager reference
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (b, c, sc, keep, *cache.k_pools, *cache.v_pools)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm-up on the capture stream
+        restore()
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    restore()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        restore()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        got = (b, c, sc, keep, *cache.k_pools, *cache.v_pools)
+        for i, (x, y) in enumerate(zip(got, ref)):
+            assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.uint8) if y.dtype == torch.bfloat16 else y), (rep, i)
