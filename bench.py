@@ -61,7 +61,7 @@ KERNEL_SOURCES = {
 
 
 def algorithmic_bytes(wl, N, P, moved_rows, hc_per_req):
-    """Bytes each kernel must move at least once per pass (see the design notes).
+    """Bytes each kernel must move at least once per pass.
 
     update : queries T*G*256 + beacons read+write 2*K*512 + counts 2*K*4
     score  : keys N*256 + beacons K*512 + counts K*4 + block table ceil(N/16)*4

@@ -74,7 +74,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The pages' workload shapes (synthetic stand-ins; see the design notes).
+# Synthetic stand-ins for the pages' workload shapes.
 WORKLOADS = {
     # one head, one layer; one-shot pass over a 4096-slot cache
     "tiny": Workload("tiny", 1, 1, 1, 1, 64, 1024, 512, 4096, 256, 8,

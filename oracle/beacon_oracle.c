@@ -20,9 +20,9 @@
  *    one random draw plus one top-K per eviction.  Section "发现四" for the
  *    shared cache-compaction step; section "发现二" for the variant in which
  *    every head uses one common set of positions.
- *  - Where the pages leave a rule open, the readings fixed for this build are
- *    applied (softmax-max beacon score with a recent-window bonus, online
- *    k-means running-mean update, cosine nearest beacon, Philox4x64-10).
+ *  - Where the pages leave a rule open, one plain reading is fixed and stated
+ *    at each function (softmax-max beacon score with a recent-window bonus,
+ *    online k-means running-mean update, cosine nearest beacon, Philox4x64-10).
  *  - Philox4x64-10 follows Salmon, Moraes, Dror, Shaw, "Parallel random
  *    numbers: as easy as 1, 2, 3", SC'11 (multiplier and Weyl constants as
  *    published there).

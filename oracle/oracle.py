@@ -12,8 +12,8 @@ nearest-beacon assignment and incremental beacon update; the Random Attention
 article (aiinking.com), section "Random Attention: 不判断重要性, 只随机保留",
 for prompt protection and per-head top-K of random scores, section "发现四"
 for the shared compaction step, and section "发现二" for one common set of
-positions shared by all heads, and for retaining contiguous blocks (pages).  Rules the pages leave open follow the readings
-fixed for this build (listed in the design notes of the repository).
+positions shared by all heads, and for retaining contiguous blocks (pages).
+Where the pages leave a rule open, each function states the rule it applies.
 """
 from __future__ import annotations
 
