@@ -368,3 +368,41 @@ def test_full_size_page_retention_pass(selector):
                  for layer in (0, L - 1) for h in (0, H - 1)]
         for x, y in zip(before[r], after):
             assert np.array_equal(x, y), r                # no row moved
+
+
+def test_full_size_capped_maintenance():
+    """The maintenance kernel alone with a count cap of 16, as the benchmark times
+    it (every head-cache of the serving workload): sampled head-caches replayed by
+    the oracle with the GPU's assignments, bit-exact state, every pick a cosine
+    argmax to within the fp32 budget, counts never above the cap once touched."""
+    _need_gpu()
+    from decode_kv_cache_beacon_amd import beaconkv as bk
+
+    wl = synth.WORKLOADS["serving_r128"]
+    dev = torch.device("cuda")
+    say("full size capped maintenance", "generate")
+    batch = synth.make_batch(wl, dev)
+    HC, T, G = wl.n_head_caches, wl.steps, wl.group
+    cap = 16
+    rng = np.random.default_rng(16)
+    sample = sorted({0, HC - 1, *rng.choice(HC, 12, replace=False).tolist()})
+    before = {hc: (synth.bits(batch.queries[hc]), batch.beacons[hc].cpu().numpy().copy(),
+                   batch.counts[hc].cpu().numpy().copy()) for hc in sample}
+    c_before = batch.counts.clone()
+    assign = torch.zeros((HC, T * G), dtype=torch.int32, device=dev)
+    say("full size capped maintenance pass")
+    bk.bkv_beacon_update(batch.queries, batch.beacons, batch.counts, assign=assign, count_cap=cap)
+    torch.cuda.synchronize()
+    touched = torch.zeros_like(batch.counts, dtype=torch.bool)
+    touched.scatter_(1, assign.long(), True)
+    # every hit leaves min(old + 1, cap) and a fill leaves 1: a touched row ends <= cap
+    assert bool((batch.counts[touched] <= cap).all())
+    assert bool((batch.counts[touched] >= 1).all())
+    assert torch.equal(batch.counts[~touched], c_before[~touched])
+    for hc in sample:
+        say("full size capped head-cache", hc)
+        q, b0, c0 = before[hc]
+        ob, oc, gap = oracle.beacon_update_forced(q, b0, c0, assign[hc].cpu().numpy(), cap=cap)
+        assert gap.max() <= ASSIGN_TOL, hc
+        assert np.array_equal(ob.view(np.int32), batch.beacons[hc].cpu().numpy().view(np.int32))
+        assert np.array_equal(oc, batch.counts[hc].cpu().numpy()), hc
