@@ -186,7 +186,7 @@ PROFILE_CMDS = {
 }
 
 
-def summarize_profiles(prof_dir, pmc_dir, workload):
+def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
     """Write the committed summaries from rocprofv3 output: per-kernel
     durations (kernel trace), HBM bytes per launch from FETCH_SIZE and
     WRITE_SIZE, each scaled by what the counter reads for the 4 GiB device
@@ -204,7 +204,7 @@ def summarize_profiles(prof_dir, pmc_dir, workload):
         k = kid(r["Kernel_Name"])
         if k:
             dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
-    out = os.path.join(ROOT, "profiles")
+    out = out or os.path.join(ROOT, "profiles")
     os.makedirs(out, exist_ok=True)
     lines = [f"# Kernel durations, workload {workload}", "",
              "rocprofv3 kernel trace of one benchmark run (5 timed + 1 warm-up beacon passes, "
@@ -305,8 +305,8 @@ def summarize_profiles(prof_dir, pmc_dir, workload):
                          f"{100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f} |")
         with open(os.path.join(out, f"{workload}_mfma_counters.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
-    print(f"wrote profiles/{workload}_kernel_trace.md, profiles/{workload}_hbm_counters.md, "
-          "profiles/traffic.json")
+    print(f"wrote {workload}_kernel_trace.md, {workload}_hbm_counters.md and traffic.json "
+          f"in {out}")
 
 
 def side_pass(torch, bk, synth, wl, steps, warmup, dev):
