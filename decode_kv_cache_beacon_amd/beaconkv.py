@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
-BKV_ABI_VERSION = 5
+BKV_ABI_VERSION = 6
 BKV_OK, BKV_ERR_NULL, BKV_ERR_INVALID, BKV_ERR_BUDGET, BKV_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BKV_ERR_WORKSPACE, BKV_ERR_HIP, BKV_ERR_LENGTH, BKV_ERR_BLOCK_TABLE = 5, 6, 7, 8
 BKV_SCORE_F32, BKV_SCORE_U32 = 0, 1
@@ -59,7 +59,7 @@ class bkv_pass_args(ctypes.Structure):
         ("lse", _P),
         ("seed", _u64), ("request_ids", _P), ("pass_idx", _P),
         ("pos_ids", _P), ("pos_stride", _i32), ("scores_out", _P), ("keep_out", _P),
-        ("timing_events", _P), ("n_timing_events", _i32),
+        ("timing_events", _P), ("n_timing_events", _i32), ("separate_steps", _i32),
     ]
 
 
@@ -433,7 +433,8 @@ def bkv_decode_attention(cache: PagedCache, queries, out, scale=None, status=Non
 
 def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, window, bonus,
                assign, lse, seed, request_ids, pass_idx, pos_ids, scores_out, keep_out,
-               score_stride, count_cap=0, shared_positions=False, page_retention=None):
+               score_stride, count_cap=0, shared_positions=False, page_retention=None,
+               separate_steps=False):
     HC, R = cache.n_head_caches, cache.n_requests
     LR = cache.n_layers * R
     a = bkv_pass_args()
@@ -441,6 +442,7 @@ def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, wi
     a.budget = int(budget)
     a.score_stride = int(score_stride)
     a.shared_positions = int(bool(shared_positions))
+    a.separate_steps = int(bool(separate_steps))
     if page_retention is not None:
         bto, slo, fr = page_retention
         _need(bto, "block_table_out", torch.int32, (R, cache.max_blocks))
@@ -508,18 +510,23 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
                    request_ids=None, pass_idx=None, pos_ids=None, scores_out=None,
                    keep_out=None, score_stride=0, workspace=None, status=None, check=True,
                    stream=None, timing_events=None, count_cap=0, shared_positions=False,
-                   page_retention=None):
+                   page_retention=None, separate_steps=False):
     """One whole eviction pass (beacon: update -> score -> select -> compact;
     random: score -> select -> compact), every layer/request/head at once.
     shared_positions: one selection per (layer, request) for all its heads.
     page_retention: (block_table_out, seq_len_out, freed_blocks) to keep whole
     pages per request instead (no rows move; keep_out is then the kept pages).
 
+    separate_steps: run score, select and compact as three kernels even where
+    the fused kernel applies (per-head beacon selection with row compaction).
+
     timing_events: optional list of torch.cuda.Event(enable_timing=True), 5 for
-    the beacon selector and 4 for the random one, recorded around each kernel."""
+    the beacon selector and 4 for the random one, recorded around each step
+    (with the fused kernel the score interval covers score, select and
+    compact, and the other two are empty)."""
     a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
                    seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride,
-                   count_cap, shared_positions, page_retention)
+                   count_cap, shared_positions, page_retention, separate_steps)
     ev_arr = None
     if timing_events is not None:
         handles = []

@@ -39,8 +39,18 @@
 //     one iteration later, and one exp2 per key gives sigma(n).
 // Scaling by 1/sqrt(d) happens in fp32 after accumulation; the bf16 beacons
 // are never pre-scaled.
+//
+// Fused eviction (the kFuse instances): the same workgroup then selects the
+// head-cache's top-B slots from the scores it has just written and compacts
+// the head-cache in place.  Selection and compaction are per head-cache, so
+// nothing waits on other workgroups; the compaction's key reads follow the
+// phase-2 stream of the same keys closely enough to be served mostly by the
+// memory-side cache, and one workgroup's compaction overlaps the other's
+// scoring on the CU.  The LDS ring, idle once phase 2 is done, holds the
+// candidate keys, the keep list and the radix-select scratch.
 
-#include "bkv_internal.h"
+#include "compact_util.h"
+#include "select_util.h"
 
 namespace bkv {
 namespace {
@@ -167,15 +177,73 @@ __device__ __forceinline__ float wave_max(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(h), kHalfLead));
 }
 
+// Layout of the idle ring for the fused selection: radix scratch, one scan
+// slot per wave and the first dropped candidate, then the candidate keys
+// followed by the keep list (kFusedMaxEntries entries between them).
+constexpr int kFuseWsumOff = (sizeof(RadixScratch) + 15) & ~15;
+constexpr int kFuseKeyOff = 2048;
+static_assert(kFuseWsumOff + 4 * (16 + 1) <= kFuseKeyOff, "fused scratch overlaps the keys");
+
+// Top-B selection of one head-cache from the scores its workgroup has just
+// written (row_scores: the N - P candidates), then the in-place compaction.
+// Same results as topk_select_kernel followed by kv_compact_kernel: the prompt
+// is kept, the B - P best candidates survive with ties to the earlier slot,
+// and the survivors move to the front in slot order.
+template <int kThreads>
+__device__ void select_compact(const CacheView& c, const HeadIdx& x, int N, int P, int B,
+                               const float* row_scores, const int* s_bt, uint8_t* scratch,
+                               int32_t* keep_row, int32_t* pos) {
+    const int tid = threadIdx.x;
+    if (N <= B) {  // nothing to evict: every slot stays where it is
+        if (keep_row)
+            for (int i = tid; i < B; i += kThreads) keep_row[i] = (i < N) ? i : -1;
+        return;
+    }
+    if (keep_row)
+        for (int i = tid; i < P; i += kThreads) keep_row[i] = i;
+    const int m = N - P, k = B - P;
+    if (k == 0) return;  // only the prompt survives, and it does not move
+    RadixScratch* rs = reinterpret_cast<RadixScratch*>(scratch);
+    int* s_wsum = reinterpret_cast<int*>(scratch + kFuseWsumOff);
+    int* s_drop = s_wsum + kThreads / kWave;
+    uint32_t* s_key = reinterpret_cast<uint32_t*>(scratch + kFuseKeyOff);
+    int* s_keep = reinterpret_cast<int*>(s_key + m);  // kept candidate r -> its slot
+    __syncthreads();  // the scores written by group 0 are visible to every thread
+    for (int i = tid; i < m; i += kThreads) {
+        const uint32_t w = __float_as_uint(row_scores[i]);
+        s_key[i] = (w >> 31) ? 0u : w;  // non-negative fp32 orders like its bits
+    }
+    if (tid == 0) *s_drop = m;
+    int need;
+    const uint32_t T = radix_select<kThreads>(s_key, m, k, rs, &need);
+    emit_selected<kThreads>(
+        s_key, m, T, need, s_wsum,
+        [&](int r, int i) {
+            s_keep[r] = P + i;
+            if (keep_row) keep_row[P + r] = P + i;
+        },
+        [&](int i) { atomicMin(s_drop, i); });
+    __syncthreads();
+    // Survivors before the first dropped candidate keep their slots.
+    const int i0 = P + *s_drop;
+    move_rows<kThreads>(c.k_pools[x.layer], c.v_pools[x.layer], s_bt, c.H, x.head, s_keep, P,
+                        i0, B, pos);
+}
+
 // NG row groups of NQ waves (NQ tile phases), MBW 32-row blocks per wave, and
-// a register budget for WPE waves per SIMD.
-template <int NG, int NQ, int MBW, int WPE>
+// a register budget for WPE waves per SIMD; kFuse adds selection and
+// compaction (budget B, nullable keep_out and pos_ids rows).
+template <int NG, int NQ, int MBW, int WPE, bool kFuse>
 __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
     CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
     int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
+    int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
     Check ck, int32_t* status) {
     constexpr int kGroups = NG, kQ = NQ, kWaves = NG * NQ;
     constexpr int kRingTiles = kQ * kRingIters;
+    static_assert(!kFuse || kRingTiles * kTileBytes >= kFuseKeyOff + 4 * kFusedMaxEntries,
+                  "the ring cannot hold the fused selection");
+    static_assert(kWaves <= 16, "fused scan slots");
     __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kRingTiles * kTileBytes];
     __shared__ int s_bt[kMaxBlocksPerReq];
     __shared__ float s_part[kWaves][32 * MBW];  // per wave, its own rows
@@ -213,10 +281,14 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
     if (tid == 0) s_rescue = 0;
     __syncthreads();
 
+    int32_t* keep_row = (kFuse && keep_out) ? keep_out + (size_t)hc * B : nullptr;
     if (N == 0) {  // empty cache: nothing to score, every live lse is log(0)
         for (int j = tid; j < K; j += blockDim.x)
             if (lse_out)
                 lse_out[(size_t)hc * K + j] = s_live[j] ? -INFINITY : __int_as_float(0x7fc00000);
+        if constexpr (kFuse)
+            for (int i = tid; i < B; i += blockDim.x)
+                if (keep_row) keep_row[i] = -1;
         return;
     }
 
@@ -551,39 +623,62 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
     }
     ring_barrier();
     if (group == 0 && iters2 > 0) finalize(iters2 - 1, mx_prev);
+    // Every ring load has landed (the loaders waited for all of them before
+    // the last hand-over) and every ring read is done: the ring is free.
+    if constexpr (kFuse)
+        select_compact<kWaves * kWave>(c, x, N, P, B, out, s_bt, s_ring, keep_row,
+                                       pos_ids ? pos_ids + (size_t)hc * pos_stride : nullptr);
+}
+
+template <int NG, int NQ, int MBW, int WPE, bool kFuse>
+void launch_cfg(const CacheView& c, const float* beacons, const int32_t* counts, int K,
+                int window, float bonus, float* scores, int stride, float* lse, int B,
+                int32_t* keep_out, int32_t* pos_ids, int pos_stride, Check ck, int32_t* status,
+                hipStream_t s) {
+    hipLaunchKernelGGL((beacon_score_kernel<NG, NQ, MBW, WPE, kFuse>), dim3(c.L * c.R * c.H),
+                       dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, window, bonus, scores,
+                       stride, lse, B, keep_out, pos_ids, pos_stride, ck, status);
+}
+
+// Layouts measured at 2112 keys per head-cache (two workgroups per CU in
+// each case):
+//   K <= 64 : 2 groups x 2 phases, 32 rows per wave (4 waves per workgroup)
+//   K <= 128: 2 groups x 2 phases, 64 rows per wave; every tile is read
+//             from LDS by two waves (four 32-row waves took 5% longer)
+//   K <= 256: 4 groups x 2 phases, 64 rows per wave
+template <bool kFuse>
+hipError_t launch_any(const CacheView& c, const float* beacons, const int32_t* counts, int K,
+                      int window, float bonus, float* scores, int stride, float* lse, int B,
+                      int32_t* keep_out, int32_t* pos_ids, int pos_stride, Check ck,
+                      int32_t* status, hipStream_t s) {
+    if (c.L * c.R * c.H == 0) return hipSuccess;
+    if (K <= 64)
+        launch_cfg<2, 2, 1, 2, kFuse>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
+                                      keep_out, pos_ids, pos_stride, ck, status, s);
+    else if (K <= 128)
+        launch_cfg<2, 2, 2, 2, kFuse>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
+                                      keep_out, pos_ids, pos_stride, ck, status, s);
+    else
+        launch_cfg<4, 2, 2, 2, kFuse>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
+                                      keep_out, pos_ids, pos_stride, ck, status, s);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-template <int NG, int NQ, int MBW, int WPE>
-void launch_cfg(const CacheView& c, const float* beacons, const int32_t* counts, int K,
-                int window, float bonus, float* scores, int stride, float* lse, Check ck,
-                int32_t* status, hipStream_t s) {
-    hipLaunchKernelGGL((beacon_score_kernel<NG, NQ, MBW, WPE>), dim3(c.L * c.R * c.H),
-                       dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, window, bonus, scores,
-                       stride, lse, ck, status);
-}
-
 hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const int32_t* counts,
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, Check ck, int32_t* status, hipStream_t s) {
-    if (c.L * c.R * c.H == 0) return hipSuccess;
-    // Layouts measured at 2112 keys per head-cache (two workgroups per CU in
-    // each case):
-    //   K <= 64 : 2 groups x 2 phases, 32 rows per wave (4 waves per workgroup)
-    //   K <= 128: 2 groups x 2 phases, 64 rows per wave; every tile is read
-    //             from LDS by two waves (four 32-row waves took 5% longer)
-    //   K <= 256: 4 groups x 2 phases, 64 rows per wave
-    if (K <= 64)
-        launch_cfg<2, 2, 1, 2>(c, beacons, counts, K, window, bonus, scores, stride, lse, ck,
-                               status, s);
-    else if (K <= 128)
-        launch_cfg<2, 2, 2, 2>(c, beacons, counts, K, window, bonus, scores, stride, lse, ck,
-                               status, s);
-    else
-        launch_cfg<4, 2, 2, 2>(c, beacons, counts, K, window, bonus, scores, stride, lse, ck,
-                               status, s);
-    return hipGetLastError();
+    return launch_any<false>(c, beacons, counts, K, window, bonus, scores, stride, lse, 0,
+                             nullptr, nullptr, 0, ck, status, s);
+}
+
+hipError_t launch_beacon_evict(const CacheView& c, const float* beacons, const int32_t* counts,
+                               int K, int window, float bonus, float* scores, int stride,
+                               float* lse, int budget, int32_t* keep_out, int32_t* pos_ids,
+                               int pos_stride, Check ck, int32_t* status, hipStream_t s) {
+    return launch_any<true>(c, beacons, counts, K, window, bonus, scores, stride, lse, budget,
+                            keep_out, pos_ids, pos_stride, ck, status, s);
 }
 
 }  // namespace bkv

@@ -151,6 +151,15 @@ hipError_t launch_beacon_update(int HC, int T, int G, int K, const uint16_t* q, 
 hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const int32_t* counts,
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, Check ck, int32_t* status, hipStream_t s);
+// Scoring, top-B selection and compaction of every head-cache in one kernel
+// (per-head selection).  `scores` is still written (the selection reads it
+// back); keep_out and pos_ids are nullable.  Requires stride + budget <=
+// kFusedMaxEntries, the candidate keys and keep list the kernel holds in LDS.
+constexpr int kFusedMaxEntries = 15872;
+hipError_t launch_beacon_evict(const CacheView& c, const float* beacons, const int32_t* counts,
+                               int K, int window, float bonus, float* scores, int stride,
+                               float* lse, int budget, int32_t* keep_out, int32_t* pos_ids,
+                               int pos_stride, Check ck, int32_t* status, hipStream_t s);
 // `shared`: one row / keep list per (layer, request) instead of per head-cache.
 // `rows` of the random scorer: BKV_ROWS_PER_HEAD, _PER_LAYER_REQUEST or _PER_REQUEST.
 hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,

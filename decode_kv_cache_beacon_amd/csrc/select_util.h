@@ -91,4 +91,36 @@ __device__ uint32_t radix_select(const uint32_t* key, int m, int k, RadixScratch
     return prefix;
 }
 
+// After radix_select: walks the m candidates in slot order and calls
+// take(r, i) for the r-th kept candidate i (keys above T, and the first
+// `need` keys equal to T) and drop(i) for every other one.  Each thread owns
+// one contiguous run of candidates; two block-wide scans give each run its
+// number of earlier keys equal to T and of earlier kept keys.
+template <int kThreads, typename Take, typename Drop>
+__device__ void emit_selected(const uint32_t* key, int m, uint32_t T, int need, int* s_wsum,
+                              Take take, Drop drop) {
+    const int seg = (m + kThreads - 1) / kThreads;
+    const int lo = min((int)threadIdx.x * seg, m), hi = min(lo + seg, m);
+    int eq = 0;
+    for (int i = lo; i < hi; ++i) eq += (key[i] == T);
+    const int eq_before = block_exclusive_scan<kThreads>(eq, s_wsum);
+    int kept = 0, e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+        const uint32_t v = key[i];
+        kept += v > T || (v == T && e < need);
+        e += (v == T);
+    }
+    int r = block_exclusive_scan<kThreads>(kept, s_wsum);
+    e = eq_before;
+    for (int i = lo; i < hi; ++i) {
+        const uint32_t v = key[i];
+        const bool t = v > T || (v == T && e < need);
+        e += (v == T);
+        if (t)
+            take(r++, i);
+        else
+            drop(i);
+    }
+}
+
 }  // namespace bkv

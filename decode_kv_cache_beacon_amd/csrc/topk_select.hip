@@ -68,27 +68,14 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
     int need;
     const uint32_t T = radix_select<kThreads>(s_key, m, k, &s_rs, &need);
 
-    // Each thread owns one contiguous run of candidates (slot order).
-    const int seg = (m + kThreads - 1) / kThreads;
-    const int lo = min(tid * seg, m), hi = min(lo + seg, m);
-    int eq = 0;
-    for (int i = lo; i < hi; ++i) eq += (s_key[i] == T);
-    const int eq_before = block_exclusive_scan<kThreads>(eq, s_wsum);
-    int kept = 0, e = eq_before;
-    for (int i = lo; i < hi; ++i) {
-        const uint32_t v = s_key[i];
-        const bool take = v > T || (v == T && e < need);
-        e += (v == T);
-        kept += take;
-    }
-    int o = P + block_exclusive_scan<kThreads>(kept, s_wsum);
-    e = eq_before;
-    for (int i = lo; i < hi; ++i) {
-        const uint32_t v = s_key[i];
-        const bool take = v > T || (v == T && e < need);
-        e += (v == T);
-        if (take && o < B) out[o++] = P + i;  // o < B always holds; the bound is defensive
-    }
+    // kept candidates in slot order after the prompt (r < k always holds; the
+    // bound is defensive)
+    emit_selected<kThreads>(
+        s_key, m, T, need, s_wsum,
+        [&](int r, int i) {
+            if (r < k) out[P + r] = P + i;
+        },
+        [](int) {});
 }
 
 }  // namespace

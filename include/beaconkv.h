@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 5
+#define BKV_ABI_VERSION 6
 
 typedef void* bkv_stream_t; /* hipStream_t */
 
@@ -308,13 +308,22 @@ typedef struct bkv_pass_args {
                                   [n_requests][budget / 16] with page retention);
                                   else workspace */
     /* optional profiling hook: caller-created hipEvent_t handles, recorded on
-     * `stream` before the first kernel and after every kernel of the pass
+     * `stream` before the first kernel and after every step of the pass
      * (beacon: 5 events around update, score, select, compact; random: 4
      * events around score, select, compact; one fewer with page retention,
-     * whose one kernel replaces select and compact).  Ignored when NULL or
-     * when n_timing_events is smaller than that. */
+     * whose one kernel replaces select and compact).  When the fused kernel
+     * runs (below), the events after score, select and compact are all
+     * recorded after it, so the score interval covers the three steps and
+     * the other two are empty.  Ignored when NULL or when n_timing_events is
+     * smaller than that. */
     void* const* timing_events;
     int32_t n_timing_events;
+    /* Beacon selector with per-head selection and row compaction: scoring,
+     * selection and compaction run as one kernel, each workgroup taking its
+     * head-cache through all three (same results as the separate kernels),
+     * whenever score_stride + budget <= 15872.  1 runs them as three kernels
+     * instead (for per-step timing). */
+    int32_t separate_steps;
 } bkv_pass_args;
 
 /* Bytes of workspace bkv_evict_pass needs for these arguments (the score and

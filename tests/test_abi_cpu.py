@@ -1,8 +1,9 @@
 """The C ABI without a GPU: exports match the header, and host-side
 validation rejects bad arguments before anything is launched (CPU only)."""
 import ctypes
-import re
 import os
+import re
+import subprocess
 
 import pytest
 
@@ -27,11 +28,40 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 5
+    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 6
     for code in range(0, 9):
         s = bk.bkv_status_string(code)
         assert s and s != "unknown status code"
     assert bk.bkv_status_string(99) == "unknown status code"
+
+
+@pytest.mark.parametrize("struct", [bk.bkv_cache, bk.bkv_pass_args])
+def test_binding_structs_match_the_header(struct, tmp_path):
+    """Every field of the ctypes mirror sits at the offset the C compiler
+    gives it in include/beaconkv.h, and the sizes agree."""
+    name = struct.__name__
+    fields = [f[0] for f in struct._fields_]
+    src = tmp_path / "layout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "beaconkv.h"',
+             "int main(void) {", f'  printf("size %zu\\n", sizeof({name}));']
+    lines += [f'  printf("{f} %zu\\n", offsetof({name}, {f}));' for f in fields]
+    lines += ["  return 0;", "}"]
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    out = dict(l.split() for l in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                 text=True).stdout.splitlines())
+    assert int(out["size"]) == ctypes.sizeof(struct)
+    for f in fields:
+        assert int(out[f]) == getattr(struct, f).offset, f
+    # the header declares no field the mirror lacks
+    body = open(os.path.join(ROOT, "include", "beaconkv.h")).read()
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    decl = re.search(r"typedef struct\s+" + name + r"\s*\{(.*?)\}\s*" + name + ";", body,
+                     re.S).group(1)
+    declared = re.findall(r"(\w+)\s*(?:,|;)", decl)
+    assert sorted(declared) == sorted(fields)
 
 
 FAKE = 0x100000  # never dereferenced: validation fails before any launch
