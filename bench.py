@@ -3,7 +3,9 @@
 
 One step = one whole beacon eviction pass over every layer, request and KV
 head of the workload (maintenance -> scoring -> top-B selection -> in-place
-compaction), at the synchronized batch point where every request holds
+compaction; the last three run as one fused kernel, each workgroup taking its
+head-cache through all three), at the synchronized batch point where every
+request holds
 N = B + 64 slots.  Between steps, outside the timed region, 64 fresh K/V rows
 per head are written into slots [B, B+64) (what the next 64 decode tokens
 would append), so every timed pass sees a full cache.  Inputs are seeded
@@ -46,11 +48,13 @@ def kernel_source_hash(kernel):
     """Hash of a kernel's source file and the shared device headers."""
     csrc = os.path.join(ROOT, "decode_kv_cache_beacon_amd", "csrc")
     return source_hash(os.path.join(csrc, KERNEL_SOURCES[kernel]),
-                       os.path.join(csrc, "bkv_internal.h"), os.path.join(csrc, "select_util.h"))
+                       *(os.path.join(csrc, h) for h in SHARED_HEADERS))
 
 
+SHARED_HEADERS = ("bkv_internal.h", "select_util.h", "compact_util.h")
 KERNEL_SOURCES = {
     "beacon_update": "beacon_update.hip",
+    "beacon_evict": "beacon_score.hip",
     "beacon_score": "beacon_score.hip",
     "topk_select": "topk_select.hip",
     "kv_compact": "kv_compact.hip",
@@ -68,6 +72,9 @@ def algorithmic_bytes(wl, N, P, moved_rows, hc_per_req):
              + scores written (N-P)*4
     select : scores read (N-P)*4 + keep list written B*4
     compact: moved rows 4*M*256 (K and V read and written) + keep list B*4
+    evict  : the fused score+select+compact kernel: the score bytes, the keep
+             list written B*4 and the moved rows 4*M*256 (the scores it reads
+             back and the keep list it keeps in LDS are not counted again)
     """
     T, G, K, B = wl.steps, wl.group, wl.n_beacons, wl.budget
     upd = sc = sel = 0
@@ -75,8 +82,10 @@ def algorithmic_bytes(wl, N, P, moved_rows, hc_per_req):
         upd += hc_per_req * (T * G * 256 + 2 * K * 512 + 2 * K * 4)
         sc += hc_per_req * (n * 256 + K * 512 + K * 4 + -(-n // 16) * 4 + (n - p) * 4)
         sel += hc_per_req * ((n - p) * 4 + B * 4)
-    cmp_ = 4 * moved_rows * 256 + len(N) * hc_per_req * B * 4
-    return {"beacon_update": upd, "beacon_score": sc, "topk_select": sel, "kv_compact": cmp_}
+    keep_lists = len(N) * hc_per_req * B * 4
+    cmp_ = 4 * moved_rows * 256 + keep_lists
+    return {"beacon_update": upd, "beacon_score": sc, "topk_select": sel, "kv_compact": cmp_,
+            "beacon_evict": sc + keep_lists + 4 * moved_rows * 256}
 
 
 def cpu_model():
@@ -163,6 +172,7 @@ def stored_traffic(kernel):
 # kernel symbol fragment -> kernel id
 KERNEL_SYMBOLS = {
     "beacon_update_kernel": "beacon_update",
+    "beacon_evict_kernel": "beacon_evict",
     "beacon_score_kernel": "beacon_score",
     "topk_select_kernel": "topk_select",
     "kv_compact_kernel": "kv_compact",
@@ -207,10 +217,11 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
     out = out or os.path.join(ROOT, "profiles")
     os.makedirs(out, exist_ok=True)
     lines = [f"# Kernel durations, workload {workload}", "",
-             "rocprofv3 kernel trace of one benchmark run (5 timed + 1 warm-up beacon passes, "
-             "then the same number of random-selector passes, then as many page-retention "
-             "passes of each selector; top-B selection and compaction run in the first two, "
-             "maintenance and scoring also in the page-retention beacon passes).", "",
+             "rocprofv3 kernel trace of one benchmark run: 5 timed + 1 warm-up beacon passes "
+             "(maintenance, then the fused score-select-compact kernel), as many with scoring, "
+             "selection and compaction as separate kernels, as many random-selector passes, "
+             "then as many page-retention passes of each selector (maintenance and scoring "
+             "also run in the page-retention beacon passes).", "",
              "Command:", "", "    " + PROFILE_CMDS["trace"], "",
              "| kernel | launches | mean ms | min ms | max ms |", "|---|---|---|---|---|"]
     for k in KERNEL_SOURCES:
@@ -334,10 +345,15 @@ def side_pass(torch, bk, synth, wl, steps, warmup, dev):
             runs.append(ev)
     torch.cuda.synchronize()
     bk.check_status(status, f"{wl.name} side passes")
-    names = ["beacon_update", "beacon_score", "topk_select", "kv_compact"]
-    kms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in runs) / len(runs)
-           for i, n in enumerate(names)}
-    ms = sum(e[0].elapsed_time(e[4]) for e in runs) / len(runs)
+    def span(i, j):
+        return sum(e[i].elapsed_time(e[j]) for e in runs) / len(runs)
+
+    if stride + B <= bk.FUSED_MAX_ENTRIES:  # the pass ran the fused kernel
+        kms = {"beacon_update": span(0, 1), "beacon_evict": span(1, 4)}
+    else:
+        kms = {n: span(i, i + 1) for i, n in
+               enumerate(["beacon_update", "beacon_score", "topk_select", "kv_compact"])}
+    ms = span(0, 4)
     del batch, cache, scores, keep
     torch.cuda.empty_cache()
     return ms, kms, N, P
@@ -355,6 +371,8 @@ def main():
                     help="skip the one-shot side workloads (single head, 32k slots)")
     ap.add_argument("--no-pages", action="store_true",
                     help="skip the page-retention (whole pages, no row moves) passes")
+    ap.add_argument("--no-separate", action="store_true",
+                    help="skip the passes with score, select and compact as separate kernels")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the shared-position (one selection per layer and request) passes")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -428,14 +446,16 @@ def main():
         nk = min(N[0], B)
         return (nk - first).clamp(min=0).sum() * heads
 
-    stream = torch.cuda.current_stream()
-    names = ["beacon_update", "beacon_score", "topk_select", "kv_compact"]
+    # the pass runs maintenance, then the fused score+select+compact kernel;
+    # its events after score, select and compact all follow the fused kernel
+    names = ["beacon_update", "beacon_evict"]
+    sep_names = ["beacon_score", "topk_select", "kv_compact"]
 
-    def run_pass(events=None):
+    def run_pass(events=None, separate=False):
         bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
                           window=W, bonus=wl.bonus, scores_out=scores, keep_out=keep,
                           score_stride=stride, status=status, check=False,
-                          timing_events=events)
+                          timing_events=events, separate_steps=separate)
 
     for _ in range(args.warmup):
         refill()
@@ -455,36 +475,30 @@ def main():
     wall = time.perf_counter() - w0
     bk.check_status(status, "timed passes")
 
-    per_kernel = {n: [] for n in names}
-    pass_ms = []
-    for e in evs:
-        pass_ms.append(e[0].elapsed_time(e[4]))
-        for i, n in enumerate(names):
-            per_kernel[n].append(e[i].elapsed_time(e[i + 1]))
+    pass_ms = [e[0].elapsed_time(e[4]) for e in evs]
     ms = sum(pass_ms) / len(pass_ms)
-    kms = {n: sum(v) / len(v) for n, v in per_kernel.items()}
+    kms = {"beacon_update": sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs),
+           "beacon_evict": sum(e[1].elapsed_time(e[4]) for e in evs) / len(evs)}
     M = float(sum(int(m) for m in moved)) / len(moved)
     hc_per_req = wl.n_layers * H
     abytes = algorithmic_bytes(wl, N, P, M, hc_per_req)
-    total_bytes = sum(abytes.values())
-    ssc_bytes = total_bytes - abytes["beacon_update"]
-    ssc_ms = kms["beacon_score"] + kms["topk_select"] + kms["kv_compact"]
+    total_bytes = abytes["beacon_update"] + abytes["beacon_evict"]
+    ssc_bytes = abytes["beacon_evict"]
+    ssc_ms = kms["beacon_evict"]
     # logits of every key (phase 1) and of every candidate (phase 2)
     score_flops = 2.0 * wl.n_beacons * 128 * hc_per_req * sum(n + (n - p) for n, p in zip(N, P))
     update_flops = 2.0 * wl.steps * wl.group * wl.n_beacons * 128 * HC
 
-    kernels = {}
-    for n in names:
-        gbps = abytes[n] / (kms[n] * 1e-3) / 1e9
-        kernels[n] = {"ms": round(kms[n], 4), "algorithmic_bytes": int(abytes[n]),
-                      "gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
-    for n in names:
+    def kernel_entry(n, ms_, nbytes):
+        gbps = nbytes / (ms_ * 1e-3) / 1e9
+        e = {"ms": round(ms_, 4), "algorithmic_bytes": int(nbytes), "gbps": round(gbps, 1),
+             "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
         tb = stored_traffic(n)
         if tb:
-            kernels[n]["traffic_gbps"] = round(tb / (kms[n] * 1e-3) / 1e9, 1)
-    kernels["beacon_score"]["mfma_tflops"] = round(score_flops / (kms["beacon_score"] * 1e-3) / 1e12, 1)
-    kernels["beacon_score"]["mfma_frac"] = round(
-        score_flops / (kms["beacon_score"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+            e["traffic_gbps"] = round(tb / (ms_ * 1e-3) / 1e9, 1)
+        return e
+
+    kernels = {n: kernel_entry(n, kms[n], abytes[n]) for n in names}
     kernels["beacon_update"]["valu_tflops"] = round(update_flops / (kms["beacon_update"] * 1e-3) / 1e12, 2)
 
     dom = max(names, key=lambda n: kms[n])
@@ -498,6 +512,35 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBPS, 4)}
     roof["kernel"] = dom
     roof["traffic"] = stored_traffic(dom)
+
+    # the same pass with score, select and compact as three kernels: the
+    # per-step breakdown (and what the fused kernel saves)
+    separate = None
+    if not args.no_separate:
+        sruns, smoved = [], []
+        for s in range(args.warmup + args.steps):
+            refill()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+            run_pass(ev, separate=True)
+            if s >= args.warmup:
+                sruns.append(ev)
+                smoved.append(moved_rows())
+        torch.cuda.synchronize()
+        bk.check_status(status, "separate-step passes")
+        sms = sum(e[0].elapsed_time(e[4]) for e in sruns) / len(sruns)
+        skms = {n: sum(e[i + 1].elapsed_time(e[i + 2]) for e in sruns) / len(sruns)
+                for i, n in enumerate(sep_names)}
+        sab = algorithmic_bytes(wl, N, P, float(sum(int(m) for m in smoved)) / len(smoved),
+                                hc_per_req)
+        sk = {n: kernel_entry(n, skms[n], sab[n]) for n in sep_names}
+        stf = score_flops / (skms["beacon_score"] * 1e-3) / 1e12
+        sk["beacon_score"]["mfma_tflops"] = round(stf, 1)
+        sk["beacon_score"]["mfma_frac"] = round(stf / MFMA_BF16_PEAK_TFLOPS, 4)
+        separate = {
+            "passes_per_s": round(1000.0 / sms, 3), "ms": round(sms, 4),
+            "update_ms": round(sum(e[0].elapsed_time(e[1]) for e in sruns) / len(sruns), 4),
+            "score_select_compact_ms": round(sum(skms.values()), 4), "kernels": sk,
+            "note": "the same pass with scoring, selection and compaction as three kernels"}
 
     result = {
         "metric": METRIC,
@@ -532,6 +575,8 @@ def main():
         "wall_ms_per_step_incl_append": round(wall * 1e3 / args.steps, 3),
         "roofline": roof,
     }
+    if separate:
+        result["separate_steps"] = separate
 
     # the consumer of the pass: one decode step of attention over the compacted
     # cache (every layer, request and KV head; the length set to the kept count)
@@ -729,6 +774,9 @@ def main():
     result["copy_ceiling_frac"] = round(result["hbm_gbps"] / copy_gbps, 4)
     for n in names:
         result["kernels"][n]["copy_frac"] = round(result["kernels"][n]["gbps"] / copy_gbps, 4)
+    if separate:
+        for n in sep_names:
+            separate["kernels"][n]["copy_frac"] = round(separate["kernels"][n]["gbps"] / copy_gbps, 4)
     del src, dst
 
     # the other configurations' one-shot shapes, reported beside the line

@@ -25,6 +25,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
 BKV_ABI_VERSION = 6
+# bkv_evict_pass fuses score, select and compact (per-head beacon selection
+# with row compaction) when score_stride + budget is at most this
+FUSED_MAX_ENTRIES = 15872
 BKV_OK, BKV_ERR_NULL, BKV_ERR_INVALID, BKV_ERR_BUDGET, BKV_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BKV_ERR_WORKSPACE, BKV_ERR_HIP, BKV_ERR_LENGTH, BKV_ERR_BLOCK_TABLE = 5, 6, 7, 8
 BKV_SCORE_F32, BKV_SCORE_U32 = 0, 1

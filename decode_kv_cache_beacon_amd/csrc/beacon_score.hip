@@ -230,11 +230,11 @@ __device__ void select_compact(const CacheView& c, const HeadIdx& x, int N, int 
                         i0, B, pos);
 }
 
-// NG row groups of NQ waves (NQ tile phases), MBW 32-row blocks per wave, and
-// a register budget for WPE waves per SIMD; kFuse adds selection and
-// compaction (budget B, nullable keep_out and pos_ids rows).
-template <int NG, int NQ, int MBW, int WPE, bool kFuse>
-__global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
+// The body of both kernels below: NG row groups of NQ waves (NQ tile
+// phases), MBW 32-row blocks per wave; kFuse adds selection and compaction
+// (budget B, nullable keep_out and pos_ids rows).
+template <int NG, int NQ, int MBW, bool kFuse>
+__device__ __forceinline__ void score_head(
     CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
     int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
     int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
@@ -630,14 +630,41 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
                                        pos_ids ? pos_ids + (size_t)hc * pos_stride : nullptr);
 }
 
+// Scoring alone (WPE: register budget for that many waves per SIMD).
+template <int NG, int NQ, int MBW, int WPE>
+__global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
+    CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
+    int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
+    int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
+    Check ck, int32_t* status) {
+    score_head<NG, NQ, MBW, false>(c, beacons, counts, K, window, bonus, scores, stride, lse_out,
+                                   B, keep_out, pos_ids, pos_stride, ck, status);
+}
+
+// Scoring, selection and compaction of each head-cache by its workgroup.
+template <int NG, int NQ, int MBW, int WPE>
+__global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_evict_kernel(
+    CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
+    int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
+    int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
+    Check ck, int32_t* status) {
+    score_head<NG, NQ, MBW, true>(c, beacons, counts, K, window, bonus, scores, stride, lse_out,
+                                  B, keep_out, pos_ids, pos_stride, ck, status);
+}
+
 template <int NG, int NQ, int MBW, int WPE, bool kFuse>
 void launch_cfg(const CacheView& c, const float* beacons, const int32_t* counts, int K,
                 int window, float bonus, float* scores, int stride, float* lse, int B,
                 int32_t* keep_out, int32_t* pos_ids, int pos_stride, Check ck, int32_t* status,
                 hipStream_t s) {
-    hipLaunchKernelGGL((beacon_score_kernel<NG, NQ, MBW, WPE, kFuse>), dim3(c.L * c.R * c.H),
-                       dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, window, bonus, scores,
-                       stride, lse, B, keep_out, pos_ids, pos_stride, ck, status);
+    if constexpr (kFuse)
+        hipLaunchKernelGGL((beacon_evict_kernel<NG, NQ, MBW, WPE>), dim3(c.L * c.R * c.H),
+                           dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, window, bonus,
+                           scores, stride, lse, B, keep_out, pos_ids, pos_stride, ck, status);
+    else
+        hipLaunchKernelGGL((beacon_score_kernel<NG, NQ, MBW, WPE>), dim3(c.L * c.R * c.H),
+                           dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, window, bonus,
+                           scores, stride, lse, B, keep_out, pos_ids, pos_stride, ck, status);
 }
 
 // Layouts measured at 2112 keys per head-cache (two workgroups per CU in

@@ -155,7 +155,7 @@ hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const i
 // (per-head selection).  `scores` is still written (the selection reads it
 // back); keep_out and pos_ids are nullable.  Requires stride + budget <=
 // kFusedMaxEntries, the candidate keys and keep list the kernel holds in LDS.
-constexpr int kFusedMaxEntries = 15872;
+constexpr int kFusedMaxEntries = BKV_FUSED_MAX_ENTRIES;
 hipError_t launch_beacon_evict(const CacheView& c, const float* beacons, const int32_t* counts,
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, int budget, int32_t* keep_out, int32_t* pos_ids,

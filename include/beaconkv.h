@@ -87,6 +87,10 @@ enum { BKV_ROWS_PER_HEAD = 0, BKV_ROWS_PER_LAYER_REQUEST = 1, BKV_ROWS_PER_REQUE
 #define BKV_MAX_BEACONS 256
 #define BKV_MAX_CANDIDATES 32768 /* largest score_stride bkv_topk_select accepts */
 #define BKV_MAX_QUERY_HEADS 8     /* largest G bkv_decode_attention accepts */
+/* Largest score_stride + budget for which bkv_evict_pass fuses scoring,
+ * selection and compaction (the candidate keys and keep list of a head-cache
+ * then fit in the scoring kernel's LDS). */
+#define BKV_FUSED_MAX_ENTRIES 15872
 
 /* A paged bf16 KV cache (vLLM-style pools, one K and one V pool per layer).
  * Layer pool l holds bf16 [num_blocks][n_kv_heads][block_size][head_dim];
@@ -321,8 +325,8 @@ typedef struct bkv_pass_args {
     /* Beacon selector with per-head selection and row compaction: scoring,
      * selection and compaction run as one kernel, each workgroup taking its
      * head-cache through all three (same results as the separate kernels),
-     * whenever score_stride + budget <= 15872.  1 runs them as three kernels
-     * instead (for per-step timing). */
+     * whenever score_stride + budget <= BKV_FUSED_MAX_ENTRIES.  1 runs them
+     * as three kernels instead (for per-step timing). */
     int32_t separate_steps;
 } bkv_pass_args;
 

@@ -27,6 +27,14 @@ def test_every_declared_symbol_is_exported():
     assert sorted(bk.EXPORTS) == names
 
 
+def test_binding_constants_match_the_header():
+    src = open(os.path.join(ROOT, "include", "beaconkv.h")).read()
+    macros = dict(re.findall(r"^#define (BKV_\w+) (\d+)", src, re.M))
+    assert int(macros["BKV_ABI_VERSION"]) == bk.BKV_ABI_VERSION
+    assert int(macros["BKV_FUSED_MAX_ENTRIES"]) == bk.FUSED_MAX_ENTRIES
+    assert int(macros["BKV_MAX_BEACONS"]) == bk.BKV_MAX_BEACONS
+
+
 def test_version_and_status_strings():
     assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 6
     for code in range(0, 9):

@@ -32,6 +32,9 @@ def test_algorithmic_bytes_by_hand():
     # compaction: 100 moved rows, K and V each read and written (102400)
     # + the keep lists (8 x 8192)
     assert b["kv_compact"] == 102400 + 65536
+    # the fused kernel: the scoring bytes, the keep lists written and the
+    # moved rows (its score read-back and LDS keep list are not counted)
+    assert b["beacon_evict"] == 8 * 611600 + 65536 + 102400
 
 
 def test_algorithmic_bytes_scale_with_the_cache():
@@ -45,7 +48,7 @@ def test_algorithmic_bytes_scale_with_the_cache():
     assert b["topk_select"] - a["topk_select"] == 16 * 4
     # two requests cost twice one
     two = bench.algorithmic_bytes(wl, [2112, 2112], [1024, 1024], 0, 1)
-    for k in ("beacon_update", "beacon_score", "topk_select", "kv_compact"):
+    for k in ("beacon_update", "beacon_score", "topk_select", "kv_compact", "beacon_evict"):
         assert two[k] == 2 * a[k]
 
 
@@ -60,6 +63,7 @@ def _write_csv(path, fields, rows):
 
 SCORE = "void bkv::(anonymous namespace)::beacon_score_kernel<4>(bkv::CacheView, int)"
 COMPACT = "void bkv::(anonymous namespace)::kv_compact_kernel(bkv::CacheView)"
+EVICT = "void bkv::(anonymous namespace)::beacon_evict_kernel<2, 2, 2, 2>(bkv::CacheView, int)"
 COPY = "__amd_rocclr_copyBuffer.kd"
 OTHER = "void at::native::elementwise_kernel<128, 4>(int)"
 
@@ -71,7 +75,7 @@ def fake_profiles(tmp_path):
     _write_csv(str(prof / "bench_kernel_trace.csv"),
                ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
                [(SCORE, 0, 1 * ms), (SCORE, 10 * ms, 13 * ms), (COMPACT, 20 * ms, 25 * ms),
-                (OTHER, 30 * ms, 90 * ms)])
+                (OTHER, 30 * ms, 90 * ms), (EVICT, 100 * ms, 107 * ms)])
     cc = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
     # the counters over-read the copy by 25 % and under-read its writes by half:
     # read factor 0.8, write factor 2.0; two small copies do not calibrate
@@ -102,7 +106,9 @@ def test_summary_durations(fake_profiles):
             for r in text.splitlines() if r.startswith("| ") and "kernel" not in r}
     assert rows["beacon_score"] == ["2", "2.000", "1.000", "3.000"]
     assert rows["kv_compact"] == ["1", "5.000", "5.000", "5.000"]
-    assert set(rows) == {"beacon_score", "kv_compact"}  # other kernels are not listed
+    # the fused kernel is told apart from the scoring kernel it shares a source with
+    assert rows["beacon_evict"] == ["1", "7.000", "7.000", "7.000"]
+    assert set(rows) == {"beacon_score", "kv_compact", "beacon_evict"}  # others not listed
     assert bench.PROFILE_CMDS["trace"] in text
 
 
