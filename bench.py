@@ -59,6 +59,7 @@ KERNEL_SOURCES = {
     "topk_select": "topk_select.hip",
     "kv_compact": "kv_compact.hip",
     "random_score": "random_score.hip",
+    "random_evict": "random_score.hip",
     "page_retain": "page_retain.hip",
     "decode_attention": "decode_attention.hip",
 }
@@ -177,6 +178,7 @@ KERNEL_SYMBOLS = {
     "topk_select_kernel": "topk_select",
     "kv_compact_kernel": "kv_compact",
     "random_score_kernel": "random_score",
+    "random_evict_kernel": "random_evict",
     "page_retain_kernel": "page_retain",
     "decode_attention_kernel": "decode_attention",
 }
@@ -219,9 +221,10 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
     lines = [f"# Kernel durations, workload {workload}", "",
              "rocprofv3 kernel trace of one benchmark run: 5 timed + 1 warm-up beacon passes "
              "(maintenance, then the fused score-select-compact kernel), as many with scoring, "
-             "selection and compaction as separate kernels, as many random-selector passes, "
-             "then as many page-retention passes of each selector (maintenance and scoring "
-             "also run in the page-retention beacon passes).", "",
+             "selection and compaction as separate kernels, as many random-selector passes "
+             "(fused draw-select-compact kernel) and as many again with separate kernels, then "
+             "as many page-retention passes of each selector (maintenance and scoring also run "
+             "in the page-retention beacon passes).", "",
              "Command:", "", "    " + PROFILE_CMDS["trace"], "",
              "| kernel | launches | mean ms | min ms | max ms |", "|---|---|---|---|---|"]
     for k in KERNEL_SOURCES:
@@ -606,30 +609,42 @@ def main():
         rid = torch.arange(R, dtype=torch.int64, device=dev)
         pss = torch.zeros(R, dtype=torch.int32, device=dev)
         u = torch.zeros((HC, stride), dtype=torch.int32, device=dev)
-        rms, rk = [], {"random_score": [], "topk_select": [], "kv_compact": []}
-        rmoved = []
-        for s in range(args.warmup + args.steps):
-            pss.fill_(s + 1000)
-            refill()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-            bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed, request_ids=rid,
-                              pass_idx=pss, scores_out=u, keep_out=keep, score_stride=stride,
-                              status=status, check=False, timing_events=ev)
-            if s >= args.warmup:
-                rmoved.append(moved_rows())
-                rms.append(ev)
-        torch.cuda.synchronize()
-        bk.check_status(status, "random passes")
-        rpass = sum(e[0].elapsed_time(e[3]) for e in rms) / len(rms)
-        for i, n in enumerate(rk):
-            rk[n] = round(sum(e[i].elapsed_time(e[i + 1]) for e in rms) / len(rms), 4)
-        rM = float(sum(int(m) for m in rmoved)) / len(rmoved)
-        rbytes = 4 * rM * 256 + HC * (2 * stride * 4 + 2 * B * 4)
+
+        def random_passes(separate, salt):
+            runs, rmoved = [], []
+            for s in range(args.warmup + args.steps):
+                pss.fill_(s + salt)
+                refill()
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed, request_ids=rid,
+                                  pass_idx=pss, scores_out=u, keep_out=keep, score_stride=stride,
+                                  status=status, check=False, timing_events=ev,
+                                  separate_steps=separate)
+                if s >= args.warmup:
+                    rmoved.append(moved_rows())
+                    runs.append(ev)
+            torch.cuda.synchronize()
+            bk.check_status(status, "random passes")
+            rpass = sum(e[0].elapsed_time(e[3]) for e in runs) / len(runs)
+            rk = {n: round(sum(e[i].elapsed_time(e[i + 1]) for e in runs) / len(runs), 4)
+                  for i, n in enumerate(["random_score", "topk_select", "kv_compact"])}
+            rM = float(sum(int(m) for m in rmoved)) / len(rmoved)
+            return rpass, rk, rM
+
+        # the pass's default: draws, selection and compaction in one kernel
+        rpass, _, rM = random_passes(False, 1000)
+        rbytes = 4 * rM * 256 + HC * (stride * 4 + B * 4)
+        sp, sk, sM = random_passes(True, 5000)
         result["random_selector"] = {
-            "passes_per_s": round(1000.0 / rpass, 3), "ms": round(rpass, 4), "kernel_ms": rk,
+            "passes_per_s": round(1000.0 / rpass, 3), "ms": round(rpass, 4),
+            "kernel_ms": {"random_evict": round(rpass, 4)},
             "moved_rows_per_pass": int(rM),
             "gbps": round(rbytes / (rpass * 1e-3) / 1e9, 1),
-            "hbm_frac": round(rbytes / (rpass * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+            "hbm_frac": round(rbytes / (rpass * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "separate_steps": {"passes_per_s": round(1000.0 / sp, 3), "ms": round(sp, 4),
+                               "kernel_ms": sk, "moved_rows_per_pass": int(sM)},
+            "note": "algorithmic bytes: the draws written, the keep lists written and the "
+                    "moved rows (K and V read and written)"}
 
     # shared positions: one selection per (layer, request) for all its heads
     if not args.no_shared:

@@ -165,6 +165,13 @@ hipError_t launch_beacon_evict(const CacheView& c, const float* beacons, const i
 hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
                                const int32_t* pass_idx, int rows, uint32_t* scores, int stride,
                                Check ck, int32_t* status, hipStream_t s);
+// Random draws, top-B selection and compaction of every head-cache in one
+// kernel (per-head selection; draws still written to `scores`; keep_out and
+// pos_ids nullable).  Requires stride + budget <= kFusedMaxEntries.
+hipError_t launch_random_evict(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
+                               const int32_t* pass_idx, uint32_t* scores, int stride, int budget,
+                               int32_t* keep_out, int32_t* pos_ids, int pos_stride, Check ck,
+                               int32_t* status, hipStream_t s);
 hipError_t launch_decode_attention(const CacheView& c, const uint16_t* q, int G, float scale,
                                    float* out, int32_t* status, hipStream_t s);
 hipError_t launch_page_retain(const CacheView& c, const void* scores, int kind, int stride,

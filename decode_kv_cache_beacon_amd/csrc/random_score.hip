@@ -12,7 +12,8 @@
 // two 64x64->128-bit multiplies with a Weyl-sequence key schedule.  One thread
 // evaluates one counter and scores the four slots 4g .. 4g+3.
 
-#include "bkv_internal.h"
+#include "compact_util.h"
+#include "select_util.h"
 
 namespace bkv {
 namespace {
@@ -73,7 +74,99 @@ __global__ __launch_bounds__(kThreads) void random_score_kernel(
     }
 }
 
+// Fused per-head pass: each workgroup draws its head-cache's candidate
+// scores (written to the score buffer and kept in LDS as keys), selects the
+// top B - P with the radix select, and compacts the head-cache in place --
+// the same results as random_score_kernel, topk_select_kernel and
+// kv_compact_kernel in turn, in one launch and without the keys or the keep
+// list leaving the workgroup.  Dynamic LDS holds the stride candidate keys
+// followed by the keep list.
+__global__ __launch_bounds__(kThreads) void random_evict_kernel(
+    CacheView c, uint64_t seed, const uint64_t* __restrict__ req_ids,
+    const int32_t* __restrict__ pass_idx, uint32_t* __restrict__ scores, int stride, int B,
+    int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride, Check ck,
+    int32_t* status) {
+    extern __shared__ uint32_t s_key[];  // [stride] keys, then the keep list
+    __shared__ int s_bt[kMaxBlocksPerReq];
+    __shared__ RadixScratch s_rs;
+    __shared__ int s_wsum[kThreads / kWave];
+    __shared__ int s_drop;
+
+    const int hc = blockIdx.x;
+    const HeadIdx x = split_hc(c, hc);
+    if (!request_ok(c, x.layer, x.req, ck, status)) return;
+    const int N = c.seq_len[x.req];
+    const int P = c.prompt_len[x.req];
+    const int tid = threadIdx.x;
+    int32_t* keep_row = keep_out ? keep_out + (size_t)hc * B : nullptr;
+    uint32_t* out = scores + (size_t)hc * stride;
+
+    // draws of the candidates [P, N), one counter per four slots
+    U64x4 ctr;
+    ctr.v[1] = (uint64_t)(uint32_t)pass_idx[x.req];
+    ctr.v[2] = ((uint64_t)(uint32_t)x.layer << 32) | (uint64_t)(uint32_t)x.head;
+    ctr.v[3] = req_ids[x.req];
+    for (int g = P / 4 + tid; 4 * g < N; g += kThreads) {
+        ctr.v[0] = (uint64_t)g;
+        const U64x4 w = philox4x64_10(ctr, seed, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int n = 4 * g + k;
+            if (n >= P && n < N) {
+                const uint32_t v = (uint32_t)(w.v[k] >> 32);
+                out[n - P] = v;
+                s_key[n - P] = v;
+            }
+        }
+    }
+    if (N <= B) {  // nothing to evict: every slot stays where it is
+        if (keep_row)
+            for (int i = tid; i < B; i += kThreads) keep_row[i] = (i < N) ? i : -1;
+        return;
+    }
+    if (keep_row)
+        for (int i = tid; i < P; i += kThreads) keep_row[i] = i;
+    const int m = N - P, k = B - P;
+    if (k == 0) return;  // only the prompt survives, and it does not move
+    const int nb = (N + kBlock - 1) / kBlock;
+    const int32_t* bt = c.block_table + (size_t)x.req * c.max_blocks;
+    for (int i = tid; i < nb; i += kThreads) s_bt[i] = bt[i];
+    if (tid == 0) s_drop = m;
+    int* s_keep = reinterpret_cast<int*>(s_key + stride);  // kept candidate r -> its slot
+    int need;  // radix_select starts with a barrier: the keys above are complete
+    const uint32_t T = radix_select<kThreads>(s_key, m, k, &s_rs, &need);
+    emit_selected<kThreads>(
+        s_key, m, T, need, s_wsum,
+        [&](int r, int i) {
+            s_keep[r] = P + i;
+            if (keep_row) keep_row[P + r] = P + i;
+        },
+        [&](int i) { atomicMin(&s_drop, i); });
+    __syncthreads();
+    // survivors before the first dropped candidate keep their slots
+    move_rows<kThreads>(c.k_pools[x.layer], c.v_pools[x.layer], s_bt, c.H, x.head, s_keep, P,
+                        P + s_drop, B, pos_ids ? pos_ids + (size_t)hc * pos_stride : nullptr);
+}
+
 }  // namespace
+
+hipError_t launch_random_evict(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
+                               const int32_t* pass_idx, uint32_t* scores, int stride, int budget,
+                               int32_t* keep_out, int32_t* pos_ids, int pos_stride, Check ck,
+                               int32_t* status, hipStream_t s) {
+    const int HC = c.L * c.R * c.H;
+    if (HC == 0) return hipSuccess;
+    const size_t lds = (size_t)(stride + budget) * sizeof(uint32_t);
+    if (lds > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute((const void*)random_evict_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(random_evict_kernel, dim3(HC), dim3(kThreads), lds, s, c, seed, req_ids,
+                       pass_idx, scores, stride, budget, keep_out, pos_ids, pos_stride, ck,
+                       status);
+    return hipGetLastError();
+}
 
 hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,
                                const int32_t* pass_idx, int rows, uint32_t* scores, int stride,

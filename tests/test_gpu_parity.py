@@ -342,7 +342,7 @@ def _pass_case(wl, N, P, B, selector, seed=17, shared=False, separate=False):
         sc = torch.zeros((L * R if shared else HC, S), dtype=torch.int32).cuda()
         bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=seed, request_ids=rid,
                           pass_idx=pss, pos_ids=pos_dev, scores_out=sc, keep_out=keep,
-                          shared_positions=shared)
+                          shared_positions=shared, separate_steps=separate)
     torch.cuda.synchronize()
     k_out, v_out = host_pools(cache)
     kn, scn, posn = keep.cpu().numpy(), sc.cpu().numpy(), pos_dev.cpu().numpy()
@@ -414,7 +414,7 @@ def _pass_case(wl, N, P, B, selector, seed=17, shared=False, separate=False):
 
 
 @pytest.mark.parametrize("selector,separate", [("beacon", False), ("beacon", True),
-                                               ("random", False)])
+                                               ("random", False), ("random", True)])
 def test_evict_pass_end_to_end(selector, separate):
     say("pass", selector, "separate" if separate else "fused")
     wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=512, prompt_len=200, seq_len=576)
@@ -422,14 +422,15 @@ def test_evict_pass_end_to_end(selector, separate):
                separate=separate)
 
 
-@pytest.mark.parametrize("K", [64, 128, 256])
-def test_fused_pass_matches_separate_steps(K):
+@pytest.mark.parametrize("selector,K", [("beacon", 64), ("beacon", 128), ("beacon", 256),
+                                        ("random", 128)])
+def test_fused_pass_matches_separate_steps(selector, K):
     """The fused score-select-compact kernel leaves every output byte for byte
     as the three separate kernels do, with and without the optional keep and
     pos outputs, at lengths that exercise each branch: eviction, N <= B (no
     move), B == P (only the prompt survives), an empty cache, one eviction
     without a prompt, and a ragged last tile."""
-    say("fused vs separate, K", K)
+    say("fused vs separate,", selector, "K", K)
     wl = small(n_layers=2, n_requests=6, n_kv_heads=2, budget=512, prompt_len=200, seq_len=608,
                n_beacons=K, steps=8)
     N, P, B = [576, 400, 600, 0, 513, 607], [200, 100, 512, 0, 0, 31], 512
@@ -441,9 +442,17 @@ def test_fused_pass_matches_separate_steps(K):
         q, b, c = batch.queries.cuda(), batch.beacons.cuda(), batch.counts.cuda()
         pos = torch.arange(S, dtype=torch.int32).repeat(HC, 1).cuda() if optional else None
         keep = torch.full((HC, B), -7, dtype=torch.int32).cuda() if optional else None
-        sc = torch.zeros((HC, S)).cuda()
-        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
-                          pos_ids=pos, keep_out=keep, scores_out=sc, separate_steps=separate)
+        if selector == "beacon":
+            sc = torch.zeros((HC, S)).cuda()
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                              pos_ids=pos, keep_out=keep, scores_out=sc, separate_steps=separate)
+        else:
+            sc = torch.zeros((HC, S), dtype=torch.int32).cuda()
+            rid = torch.arange(40, 40 + cache.n_requests, dtype=torch.int64).cuda()
+            pss = torch.arange(cache.n_requests, dtype=torch.int32).cuda()
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=11, request_ids=rid,
+                              pass_idx=pss, pos_ids=pos, keep_out=keep, scores_out=sc,
+                              separate_steps=separate)
         torch.cuda.synchronize()
         k_out, v_out = host_pools(cache)
         outs.append(dict(b=b.cpu().numpy().view(np.int32), c=c.cpu().numpy(),
