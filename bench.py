@@ -55,6 +55,7 @@ SHARED_HEADERS = ("bkv_internal.h", "select_util.h", "compact_util.h")
 KERNEL_SOURCES = {
     "beacon_update": "beacon_update.hip",
     "beacon_evict": "beacon_score.hip",
+    "beacon_evict_shared": "beacon_score.hip",
     "beacon_score": "beacon_score.hip",
     "topk_select": "topk_select.hip",
     "kv_compact": "kv_compact.hip",
@@ -173,6 +174,7 @@ def stored_traffic(kernel):
 # kernel symbol fragment -> kernel id
 KERNEL_SYMBOLS = {
     "beacon_update_kernel": "beacon_update",
+    "beacon_evict_shared_kernel": "beacon_evict_shared",
     "beacon_evict_kernel": "beacon_evict",
     "beacon_score_kernel": "beacon_score",
     "topk_select_kernel": "topk_select",
@@ -438,6 +440,19 @@ def main():
             cache.k_pools[layer][tail_blocks] = fk
             cache.v_pools[layer][tail_blocks] = fv
 
+    # Every section that compares the fused kernels with the separate ones
+    # starts from this same state (pools, beacons, counts), so both sides run
+    # the same sequence of passes and move the same rows (their outputs are
+    # bit-identical, so the state evolves identically).
+    state0 = ([k.clone() for k in cache.k_pools], [v.clone() for v in cache.v_pools],
+              batch.beacons.clone(), batch.counts.clone())
+
+    def restore_state():
+        for dst, src in zip(cache.k_pools + cache.v_pools, state0[0] + state0[1]):
+            dst.copy_(src)
+        batch.beacons.copy_(state0[2])
+        batch.counts.copy_(state0[3])
+
     ar = torch.arange(B, device=dev, dtype=torch.int32)
 
     def moved_rows(kp=None, heads=1):
@@ -520,6 +535,7 @@ def main():
     # per-step breakdown (and what the fused kernel saves)
     separate = None
     if not args.no_separate:
+        restore_state()
         sruns, smoved = [], []
         for s in range(args.warmup + args.steps):
             refill()
@@ -541,6 +557,7 @@ def main():
         sk["beacon_score"]["mfma_frac"] = round(stf / MFMA_BF16_PEAK_TFLOPS, 4)
         separate = {
             "passes_per_s": round(1000.0 / sms, 3), "ms": round(sms, 4),
+            "same_moved_rows_as_fused": [int(m) for m in smoved] == [int(m) for m in moved],
             "update_ms": round(sum(e[0].elapsed_time(e[1]) for e in sruns) / len(sruns), 4),
             "score_select_compact_ms": round(sum(skms.values()), 4), "kernels": sk,
             "note": "the same pass with scoring, selection and compaction as three kernels"}
@@ -611,6 +628,7 @@ def main():
         u = torch.zeros((HC, stride), dtype=torch.int32, device=dev)
 
         def random_passes(separate, salt):
+            restore_state()
             runs, rmoved = [], []
             for s in range(args.warmup + args.steps):
                 pss.fill_(s + salt)
@@ -629,12 +647,12 @@ def main():
             rk = {n: round(sum(e[i].elapsed_time(e[i + 1]) for e in runs) / len(runs), 4)
                   for i, n in enumerate(["random_score", "topk_select", "kv_compact"])}
             rM = float(sum(int(m) for m in rmoved)) / len(rmoved)
-            return rpass, rk, rM
+            return rpass, rk, rM, [int(m) for m in rmoved]
 
         # the pass's default: draws, selection and compaction in one kernel
-        rpass, _, rM = random_passes(False, 1000)
+        rpass, _, rM, rlist = random_passes(False, 1000)
         rbytes = 4 * rM * 256 + HC * (stride * 4 + B * 4)
-        sp, sk, sM = random_passes(True, 5000)
+        sp, sk, sM, slist = random_passes(True, 1000)
         result["random_selector"] = {
             "passes_per_s": round(1000.0 / rpass, 3), "ms": round(rpass, 4),
             "kernel_ms": {"random_evict": round(rpass, 4)},
@@ -642,7 +660,8 @@ def main():
             "gbps": round(rbytes / (rpass * 1e-3) / 1e9, 1),
             "hbm_frac": round(rbytes / (rpass * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "separate_steps": {"passes_per_s": round(1000.0 / sp, 3), "ms": round(sp, 4),
-                               "kernel_ms": sk, "moved_rows_per_pass": int(sM)},
+                               "kernel_ms": sk, "moved_rows_per_pass": int(sM),
+                               "same_moved_rows_as_fused": slist == rlist},
             "note": "algorithmic bytes: the draws written, the keep lists written and the "
                     "moved rows (K and V read and written)"}
 
@@ -654,8 +673,9 @@ def main():
         pss = torch.zeros(R, dtype=torch.int32, device=dev)
         us = torch.zeros((LR, stride), dtype=torch.int32, device=dev)
         shared = {}
-        for sel in ("beacon", "random"):
+        for sel, sep in (("beacon", False), ("beacon", True), ("random", False)):
             n_ev = 5 if sel == "beacon" else 4
+            restore_state()
             runs, smoved = [], []
             for s in range(args.warmup + args.steps):
                 refill()
@@ -664,7 +684,8 @@ def main():
                     bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b,
                                       counts=c, window=W, bonus=wl.bonus, scores_out=scores,
                                       keep_out=keep_s, score_stride=stride, status=status,
-                                      check=False, timing_events=ev, shared_positions=True)
+                                      check=False, timing_events=ev, shared_positions=True,
+                                      separate_steps=sep)
                 else:
                     pss.fill_(s + 2000)
                     bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed,
@@ -676,16 +697,30 @@ def main():
                     runs.append(ev)
             torch.cuda.synchronize()
             bk.check_status(status, f"shared-position {sel} passes")
-            kn_ = (["beacon_update", "beacon_score"] if sel == "beacon" else ["random_score"]) + \
-                ["topk_select", "kv_compact"]
-            tpass = sum(e[0].elapsed_time(e[-1]) for e in runs) / len(runs)
-            shared[sel] = {
-                "passes_per_s": round(1000.0 / tpass, 3), "ms": round(tpass, 4),
-                "kernel_ms": {n: round(sum(e[i].elapsed_time(e[i + 1]) for e in runs) / len(runs), 4)
-                              for i, n in enumerate(kn_)},
-                "moved_rows_per_pass": int(float(sum(int(m) for m in smoved)) / len(smoved))}
+
+            def span(i, j):
+                return round(sum(e[i].elapsed_time(e[j]) for e in runs) / len(runs), 4)
+
+            if sel == "beacon" and not sep:  # maintenance, then the fused shared kernel
+                kms_ = {"beacon_update": span(0, 1), "beacon_evict_shared": span(1, 4)}
+            else:
+                kn_ = (["beacon_update", "beacon_score"] if sel == "beacon" else
+                       ["random_score"]) + ["topk_select", "kv_compact"]
+                kms_ = {n: span(i, i + 1) for i, n in enumerate(kn_)}
+            tpass = span(0, n_ev - 1)
+            entry = {"passes_per_s": round(1000.0 / tpass, 3), "ms": tpass, "kernel_ms": kms_,
+                     "moved_rows_per_pass": int(float(sum(int(m) for m in smoved)) / len(smoved))}
+            if sep:
+                entry["same_moved_rows_as_fused"] = smoved_list == [int(m) for m in smoved]
+                shared["beacon"]["separate_steps"] = entry
+            else:
+                shared[sel] = entry
+                if sel == "beacon":
+                    smoved_list = [int(m) for m in smoved]
         shared["note"] = ("one keep list per (layer, request) for all KV heads: beacon scores "
-                          "merged by their maximum over heads, random draws one row")
+                          "merged by their maximum over heads (one fused kernel: a workgroup "
+                          "scores the heads of its (layer, request), selects once and compacts "
+                          "every head), random draws one row")
         result["shared_positions"] = shared
 
     # page retention: whole pages per request, the block table rewritten in

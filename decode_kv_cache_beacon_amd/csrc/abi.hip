@@ -332,18 +332,20 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
     };
     hipError_t he = mark();
     if (he != hipSuccess) return BKV_ERR_HIP;
-    // per-head selection with row compaction: one kernel for score, select
-    // and compact when its LDS holds the candidates and keep list
-    const bool fused = !shared && !pages && !a->separate_steps &&
+    // row compaction: one kernel for score, select and compact when its LDS
+    // holds the candidates and keep list (per head for either selector, or
+    // shared positions for the beacon selector)
+    const bool fused = !pages && !a->separate_steps && (!shared || beacon) &&
                        (int64_t)L.stride + a->budget <= kFusedMaxEntries;
     if (fused && beacon) {
         he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
                                   a->assign, a->count_cap, &v, all, status, s);
         if (he == hipSuccess) he = mark();
         if (he == hipSuccess)
-            he = launch_beacon_evict(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
-                                     static_cast<float*>(sc), L.stride, a->lse, a->budget,
-                                     a->keep_out, a->pos_ids, a->pos_stride, all, status, s);
+            he = (shared ? launch_beacon_evict_shared : launch_beacon_evict)(
+                v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
+                static_cast<float*>(sc), L.stride, a->lse, a->budget, a->keep_out, a->pos_ids,
+                a->pos_stride, all, status, s);
         for (int i = 0; i < 3 && he == hipSuccess; ++i) he = mark();
         return hip_status(he);
     }

@@ -40,14 +40,17 @@
 // Scaling by 1/sqrt(d) happens in fp32 after accumulation; the bf16 beacons
 // are never pre-scaled.
 //
-// Fused eviction (the kFuse instances): the same workgroup then selects the
+// Fused eviction (beacon_evict_kernel): the same workgroup then selects the
 // head-cache's top-B slots from the scores it has just written and compacts
 // the head-cache in place.  Selection and compaction are per head-cache, so
 // nothing waits on other workgroups; the compaction's key reads follow the
 // phase-2 stream of the same keys closely enough to be served mostly by the
 // memory-side cache, and one workgroup's compaction overlaps the other's
 // scoring on the CU.  The LDS ring, idle once phase 2 is done, holds the
-// candidate keys, the keep list and the radix-select scratch.
+// candidate keys, the keep list and the radix-select scratch.  With shared
+// positions (beacon_evict_shared_kernel) a workgroup scores the H heads of a
+// (layer, request) in turn, then selects once from their largest scores and
+// compacts every head.
 
 #include "compact_util.h"
 #include "select_util.h"
@@ -233,18 +236,75 @@ __device__ void select_compact(const CacheView& c, const HeadIdx& x, int N, int 
                            P, i0, B, pos);
 }
 
-// The body of both kernels below: NG row groups of NQ waves (NQ tile
-// phases), MBW 32-row blocks per wave; kFuse adds selection and compaction
-// (budget B, nullable keep_out and pos_ids rows).
-template <int NG, int NQ, int MBW, bool kFuse>
-__device__ __forceinline__ void score_head(
+// Shared positions: one selection for the H heads of a (layer, request),
+// from the largest of their scores (rows[h * stride + i], h < H), applied to
+// every head's rows -- the same results as bkv_topk_select_shared followed by
+// bkv_kv_compact with keep_shared.  Called once all H heads are scored.
+template <int kThreads>
+__device__ void shared_select_compact(const CacheView& c, const HeadIdx& x, int N, int P, int B,
+                                      const float* rows, int stride, const int* s_bt,
+                                      uint8_t* scratch, int32_t* keep_row, int32_t* pos0,
+                                      int pos_stride) {
+    const int tid = threadIdx.x;
+    if (N <= B) {  // nothing to evict
+        if (keep_row)
+            for (int i = tid; i < B; i += kThreads) keep_row[i] = (i < N) ? i : -1;
+        return;
+    }
+    if (keep_row)
+        for (int i = tid; i < P; i += kThreads) keep_row[i] = i;
+    const int m = N - P, k = B - P;
+    if (k == 0) return;
+    RadixScratch* rs = reinterpret_cast<RadixScratch*>(scratch);
+    int* s_wsum = reinterpret_cast<int*>(scratch + kFuseWsumOff);
+    int* s_drop = s_wsum + kThreads / kWave;
+    uint32_t* s_key = reinterpret_cast<uint32_t*>(scratch + kFuseKeyOff);
+    int* s_keep = reinterpret_cast<int*>(s_key + m);
+    __syncthreads();  // every head's scores are visible to every thread
+    for (int i = tid; i < m; i += kThreads) {
+        uint32_t v = 0;
+        for (int h = 0; h < c.H; ++h) {
+            const uint32_t w = __float_as_uint(rows[(size_t)h * stride + i]);
+            v = max(v, (w >> 31) ? 0u : w);
+        }
+        s_key[i] = v;
+    }
+    if (tid == 0) *s_drop = m;
+    int need;
+    const uint32_t T = radix_select<kThreads>(s_key, m, k, rs, &need);
+    emit_selected<kThreads>(
+        s_key, m, T, need, s_wsum,
+        [&](int r, int i) {
+            s_keep[r] = P + i;
+            if (keep_row) keep_row[P + r] = P + i;
+        },
+        [&](int i) { atomicMin(s_drop, i); });
+    __syncthreads();
+    const int i0 = P + *s_drop;
+    for (int h = 0; h < c.H; ++h)
+        move_rows<kThreads, 4>(c.k_pools[x.layer], c.v_pools[x.layer], s_bt, c.H, h, s_keep, P,
+                               i0, B, pos0 ? pos0 + (size_t)h * pos_stride : nullptr);
+}
+
+// What the score body does after scoring: nothing, the per-head selection
+// and compaction, or (shared positions) the selection and compaction of the
+// (layer, request) once its last head is scored.
+enum { kScoreOnly = 0, kEvictHead = 1, kEvictShared = 2 };
+
+// The body of the kernels below, for head-cache hc: NG row groups of NQ waves
+// (NQ tile phases), MBW 32-row blocks per wave; kMode as above (budget B,
+// nullable keep_out and pos_ids rows).  Returns false when the request fails
+// its checks.
+template <int NG, int NQ, int MBW, int kMode>
+__device__ __forceinline__ bool score_head(
     CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
     int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
     int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
-    Check ck, int32_t* status) {
+    Check ck, int32_t* status, const int hc) {
     constexpr int kGroups = NG, kQ = NQ, kWaves = NG * NQ;
     constexpr int kRingTiles = kQ * kRingIters;
-    static_assert(!kFuse || kRingTiles * kTileBytes >= kFuseKeyOff + 4 * kFusedMaxEntries,
+    static_assert(kMode == kScoreOnly ||
+                      kRingTiles * kTileBytes >= kFuseKeyOff + 4 * kFusedMaxEntries,
                   "the ring cannot hold the fused selection");
     static_assert(kWaves <= 16, "fused scan slots");
     __shared__ __attribute__((aligned(1024))) uint8_t s_ring[kRingTiles * kTileBytes];
@@ -257,9 +317,8 @@ __device__ __forceinline__ void score_head(
     __shared__ float s_pmax[3][kGroups - 1][kQ][32];
     __shared__ int s_rescue;
 
-    const int hc = blockIdx.x;
     const HeadIdx x = split_hc(c, hc);
-    if (!request_ok(c, x.layer, x.req, ck, status)) return;
+    if (!request_ok(c, x.layer, x.req, ck, status)) return false;
     const int N = c.seq_len[x.req];
     const int P = c.prompt_len[x.req];
 
@@ -284,15 +343,19 @@ __device__ __forceinline__ void score_head(
     if (tid == 0) s_rescue = 0;
     __syncthreads();
 
-    int32_t* keep_row = (kFuse && keep_out) ? keep_out + (size_t)hc * B : nullptr;
+    // the keep-list row: per head-cache, or per (layer, request) when shared
+    int32_t* keep_row = nullptr;
+    if (kMode != kScoreOnly && keep_out)
+        keep_row = keep_out + (size_t)(kMode == kEvictShared ? hc / c.H : hc) * B;
+    const bool last_head = x.head == c.H - 1;
     if (N == 0) {  // empty cache: nothing to score, every live lse is log(0)
         for (int j = tid; j < K; j += blockDim.x)
             if (lse_out)
                 lse_out[(size_t)hc * K + j] = s_live[j] ? -INFINITY : __int_as_float(0x7fc00000);
-        if constexpr (kFuse)
+        if (kMode == kEvictHead || (kMode == kEvictShared && last_head))
             for (int i = tid; i < B; i += blockDim.x)
                 if (keep_row) keep_row[i] = -1;
-        return;
+        return true;
     }
 
     const uint64_t kpool = c.k_pools[x.layer];
@@ -628,9 +691,16 @@ __device__ __forceinline__ void score_head(
     if (group == 0 && iters2 > 0) finalize(iters2 - 1, mx_prev);
     // Every ring load has landed (the loaders waited for all of them before
     // the last hand-over) and every ring read is done: the ring is free.
-    if constexpr (kFuse)
+    if constexpr (kMode == kEvictHead)
         select_compact<kWaves * kWave>(c, x, N, P, B, out, s_bt, s_ring, keep_row,
                                        pos_ids ? pos_ids + (size_t)hc * pos_stride : nullptr);
+    if constexpr (kMode == kEvictShared)
+        if (last_head)
+            shared_select_compact<kWaves * kWave>(
+                c, x, N, P, B, scores + (size_t)(hc - x.head) * stride, stride, s_bt, s_ring,
+                keep_row, pos_ids ? pos_ids + (size_t)(hc - x.head) * pos_stride : nullptr,
+                pos_stride);
+    return true;
 }
 
 // Scoring alone (WPE: register budget for that many waves per SIMD).
@@ -640,8 +710,9 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_kernel(
     int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
     int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
     Check ck, int32_t* status) {
-    score_head<NG, NQ, MBW, false>(c, beacons, counts, K, window, bonus, scores, stride, lse_out,
-                                   B, keep_out, pos_ids, pos_stride, ck, status);
+    score_head<NG, NQ, MBW, kScoreOnly>(c, beacons, counts, K, window, bonus, scores, stride,
+                                        lse_out, B, keep_out, pos_ids, pos_stride, ck, status,
+                                        blockIdx.x);
 }
 
 // Scoring, selection and compaction of each head-cache by its workgroup.
@@ -651,16 +722,38 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_evict_kernel(
     int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
     int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
     Check ck, int32_t* status) {
-    score_head<NG, NQ, MBW, true>(c, beacons, counts, K, window, bonus, scores, stride, lse_out,
-                                  B, keep_out, pos_ids, pos_stride, ck, status);
+    score_head<NG, NQ, MBW, kEvictHead>(c, beacons, counts, K, window, bonus, scores, stride,
+                                        lse_out, B, keep_out, pos_ids, pos_stride, ck, status,
+                                        blockIdx.x);
 }
 
-template <int NG, int NQ, int MBW, int WPE, bool kFuse>
+// Shared positions: one workgroup per (layer, request) scores its H heads in
+// turn, then selects once and compacts every head.
+template <int NG, int NQ, int MBW, int WPE>
+__global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_evict_shared_kernel(
+    CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
+    int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
+    int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
+    Check ck, int32_t* status) {
+    for (int h = 0; h < c.H; ++h) {
+        if (h) __syncthreads();  // the previous head's body is done with every LDS array
+        if (!score_head<NG, NQ, MBW, kEvictShared>(c, beacons, counts, K, window, bonus, scores,
+                                                   stride, lse_out, B, keep_out, pos_ids,
+                                                   pos_stride, ck, status, blockIdx.x * c.H + h))
+            return;
+    }
+}
+
+template <int NG, int NQ, int MBW, int WPE, int kMode>
 void launch_cfg(const CacheView& c, const float* beacons, const int32_t* counts, int K,
                 int window, float bonus, float* scores, int stride, float* lse, int B,
                 int32_t* keep_out, int32_t* pos_ids, int pos_stride, Check ck, int32_t* status,
                 hipStream_t s) {
-    if constexpr (kFuse)
+    if constexpr (kMode == kEvictShared)
+        hipLaunchKernelGGL((beacon_evict_shared_kernel<NG, NQ, MBW, WPE>), dim3(c.L * c.R),
+                           dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, window, bonus,
+                           scores, stride, lse, B, keep_out, pos_ids, pos_stride, ck, status);
+    else if constexpr (kMode == kEvictHead)
         hipLaunchKernelGGL((beacon_evict_kernel<NG, NQ, MBW, WPE>), dim3(c.L * c.R * c.H),
                            dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, window, bonus,
                            scores, stride, lse, B, keep_out, pos_ids, pos_stride, ck, status);
@@ -676,20 +769,20 @@ void launch_cfg(const CacheView& c, const float* beacons, const int32_t* counts,
 //   K <= 128: 2 groups x 2 phases, 64 rows per wave; every tile is read
 //             from LDS by two waves (four 32-row waves took 5% longer)
 //   K <= 256: 4 groups x 2 phases, 64 rows per wave
-template <bool kFuse>
+template <int kMode>
 hipError_t launch_any(const CacheView& c, const float* beacons, const int32_t* counts, int K,
                       int window, float bonus, float* scores, int stride, float* lse, int B,
                       int32_t* keep_out, int32_t* pos_ids, int pos_stride, Check ck,
                       int32_t* status, hipStream_t s) {
     if (c.L * c.R * c.H == 0) return hipSuccess;
     if (K <= 64)
-        launch_cfg<2, 2, 1, 2, kFuse>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
+        launch_cfg<2, 2, 1, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
                                       keep_out, pos_ids, pos_stride, ck, status, s);
     else if (K <= 128)
-        launch_cfg<2, 2, 2, 2, kFuse>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
+        launch_cfg<2, 2, 2, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
                                       keep_out, pos_ids, pos_stride, ck, status, s);
     else
-        launch_cfg<4, 2, 2, 2, kFuse>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
+        launch_cfg<4, 2, 2, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
                                       keep_out, pos_ids, pos_stride, ck, status, s);
     return hipGetLastError();
 }
@@ -699,16 +792,25 @@ hipError_t launch_any(const CacheView& c, const float* beacons, const int32_t* c
 hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const int32_t* counts,
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, Check ck, int32_t* status, hipStream_t s) {
-    return launch_any<false>(c, beacons, counts, K, window, bonus, scores, stride, lse, 0,
-                             nullptr, nullptr, 0, ck, status, s);
+    return launch_any<kScoreOnly>(c, beacons, counts, K, window, bonus, scores, stride, lse, 0,
+                                  nullptr, nullptr, 0, ck, status, s);
 }
 
 hipError_t launch_beacon_evict(const CacheView& c, const float* beacons, const int32_t* counts,
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, int budget, int32_t* keep_out, int32_t* pos_ids,
                                int pos_stride, Check ck, int32_t* status, hipStream_t s) {
-    return launch_any<true>(c, beacons, counts, K, window, bonus, scores, stride, lse, budget,
-                            keep_out, pos_ids, pos_stride, ck, status, s);
+    return launch_any<kEvictHead>(c, beacons, counts, K, window, bonus, scores, stride, lse,
+                                  budget, keep_out, pos_ids, pos_stride, ck, status, s);
+}
+
+hipError_t launch_beacon_evict_shared(const CacheView& c, const float* beacons,
+                                      const int32_t* counts, int K, int window, float bonus,
+                                      float* scores, int stride, float* lse, int budget,
+                                      int32_t* keep_out, int32_t* pos_ids, int pos_stride,
+                                      Check ck, int32_t* status, hipStream_t s) {
+    return launch_any<kEvictShared>(c, beacons, counts, K, window, bonus, scores, stride, lse,
+                                    budget, keep_out, pos_ids, pos_stride, ck, status, s);
 }
 
 }  // namespace bkv

@@ -160,6 +160,14 @@ hipError_t launch_beacon_evict(const CacheView& c, const float* beacons, const i
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, int budget, int32_t* keep_out, int32_t* pos_ids,
                                int pos_stride, Check ck, int32_t* status, hipStream_t s);
+// The same with shared positions: one workgroup per (layer, request) scores
+// its H heads, selects once from their largest scores (keep_out rows per
+// (layer, request)) and compacts every head.
+hipError_t launch_beacon_evict_shared(const CacheView& c, const float* beacons,
+                                      const int32_t* counts, int K, int window, float bonus,
+                                      float* scores, int stride, float* lse, int budget,
+                                      int32_t* keep_out, int32_t* pos_ids, int pos_stride,
+                                      Check ck, int32_t* status, hipStream_t s);
 // `shared`: one row / keep list per (layer, request) instead of per head-cache.
 // `rows` of the random scorer: BKV_ROWS_PER_HEAD, _PER_LAYER_REQUEST or _PER_REQUEST.
 hipError_t launch_random_score(const CacheView& c, uint64_t seed, const uint64_t* req_ids,

@@ -322,12 +322,14 @@ typedef struct bkv_pass_args {
      * smaller than that. */
     void* const* timing_events;
     int32_t n_timing_events;
-    /* Per-head selection with row compaction (either selector): scoring (or
-     * the random draws), selection and compaction run as one kernel, each
-     * workgroup taking its head-cache through all three (same results as the
-     * separate kernels; scores are still written), whenever score_stride +
-     * budget <= BKV_FUSED_MAX_ENTRIES.  1 runs them as three kernels instead
-     * (for per-step timing). */
+    /* Row compaction with per-head selection (either selector) or with
+     * shared positions (beacon selector): scoring (or the random draws),
+     * selection and compaction run as one kernel, each workgroup taking its
+     * head-cache -- or, shared, the H heads of its (layer, request) --
+     * through all three (same results as the separate kernels; scores are
+     * still written), whenever score_stride + budget <=
+     * BKV_FUSED_MAX_ENTRIES.  1 runs them as three kernels instead (for
+     * per-step timing). */
     int32_t separate_steps;
 } bkv_pass_args;
 

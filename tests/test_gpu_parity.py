@@ -423,7 +423,7 @@ def test_evict_pass_end_to_end(selector, separate):
 
 
 @pytest.mark.parametrize("selector,K", [("beacon", 64), ("beacon", 128), ("beacon", 256),
-                                        ("random", 128)])
+                                        ("random", 128), ("shared", 128), ("shared", 256)])
 def test_fused_pass_matches_separate_steps(selector, K):
     """The fused score-select-compact kernel leaves every output byte for byte
     as the three separate kernels do, with and without the optional keep and
@@ -441,8 +441,14 @@ def test_fused_pass_matches_separate_steps(selector, K):
         HC, S = cache.n_head_caches, cache.max_slots
         q, b, c = batch.queries.cuda(), batch.beacons.cuda(), batch.counts.cuda()
         pos = torch.arange(S, dtype=torch.int32).repeat(HC, 1).cuda() if optional else None
-        keep = torch.full((HC, B), -7, dtype=torch.int32).cuda() if optional else None
-        if selector == "beacon":
+        rows = HC if selector != "shared" else cache.n_layers * cache.n_requests
+        keep = torch.full((rows, B), -7, dtype=torch.int32).cuda() if optional else None
+        if selector == "shared":
+            sc = torch.zeros((HC, S)).cuda()
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                              pos_ids=pos, keep_out=keep, scores_out=sc, separate_steps=separate,
+                              shared_positions=True)
+        elif selector == "beacon":
             sc = torch.zeros((HC, S)).cuda()
             bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
                               pos_ids=pos, keep_out=keep, scores_out=sc, separate_steps=separate)
@@ -471,7 +477,7 @@ def test_fused_pass_matches_separate_steps(selector, K):
     # check the branches' keep lists directly
     kn = ref["keep"]
     for hc, layer, r, h in head_iter(cache):
-        row = keep_rows(kn[hc])
+        row = keep_rows(kn[layer * cache.n_requests + r if selector == "shared" else hc])
         if N[r] <= B:
             assert np.array_equal(row, np.arange(N[r])), hc
         elif B == P[r]:
@@ -480,11 +486,13 @@ def test_fused_pass_matches_separate_steps(selector, K):
             assert len(row) == B and np.all(np.diff(row) > 0), hc
 
 
-@pytest.mark.parametrize("selector", ["beacon", "random"])
-def test_evict_pass_shared_positions(selector):
-    say("pass shared", selector)
+@pytest.mark.parametrize("selector,separate", [("beacon", False), ("beacon", True),
+                                               ("random", False)])
+def test_evict_pass_shared_positions(selector, separate):
+    say("pass shared", selector, "separate" if separate else "default")
     wl = small(n_layers=2, n_requests=3, n_kv_heads=4, budget=512, prompt_len=200, seq_len=576)
-    _pass_case(wl, N=[576, 541, 400], P=[200, 333, 100], B=512, selector=selector, shared=True)
+    _pass_case(wl, N=[576, 541, 400], P=[200, 333, 100], B=512, selector=selector, shared=True,
+               separate=separate)
 
 
 def test_shared_select_standalone_entry_points():
