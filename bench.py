@@ -188,13 +188,13 @@ COPY_SYMBOL = "__amd_rocclr_copyBuffer"
 PROFILE_CMDS = {
     "trace": ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -f csv -d <prof-dir> "
               "-o bench -- python3 <repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline "
-              "--no-shared --no-side --count-cap 0"),
+              "--no-side --count-cap 0"),
     "pmc": ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} -f csv -d <pmc-dir>/{c} -o {c} -- "
-            "python3 <repo>/bench.py --steps 2 --warmup 0 --no-random --no-cpu-baseline "
+            "python3 <repo>/bench.py --steps 2 --warmup 0 --no-cpu-baseline "
             "--no-shared --no-pages --no-side --count-cap 0"),
     "pmc_mfma": ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16 "
                  "-f csv -d <pmc-dir>/MFMA -o MFMA -- python3 <repo>/bench.py --steps 2 "
-                 "--warmup 0 --no-random --no-cpu-baseline --no-shared --no-pages --no-side "
+                 "--warmup 0 --no-cpu-baseline --no-shared --no-pages --no-side "
                  "--count-cap 0"),
     "summary": "python bench.py --summarize-profiles <prof-dir> <pmc-dir>",
 }
@@ -224,7 +224,8 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
              "rocprofv3 kernel trace of one benchmark run: 5 timed + 1 warm-up beacon passes "
              "(maintenance, then the fused score-select-compact kernel), as many with scoring, "
              "selection and compaction as separate kernels, as many random-selector passes "
-             "(fused draw-select-compact kernel) and as many again with separate kernels, then "
+             "(fused draw-select-compact kernel) and as many again with separate kernels, "
+             "shared-position passes (beacon fused, beacon with separate kernels, random), then "
              "as many page-retention passes of each selector (maintenance and scoring also run "
              "in the page-retention beacon passes).", "",
              "Command:", "", "    " + PROFILE_CMDS["trace"], "",
@@ -264,8 +265,8 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
         "commands": [PROFILE_CMDS["pmc"].format(c="FETCH_SIZE"),
                      PROFILE_CMDS["pmc"].format(c="WRITE_SIZE"), PROFILE_CMDS["summary"]]}}
     lines = [f"# HBM traffic per launch, workload {workload}", "",
-             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the dispatches of the beacon "
-             "passes) from two rocprofv3 counter runs, each scaled by what the same counter reads "
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over each kernel's dispatches in the "
+             "profiled passes) from two rocprofv3 counter runs, each scaled by what the same counter reads "
              f"for a plain 4 GiB device copy: read factor {f_read:.4f}, write factor "
              f"{f_write:.4f}.", "", "Commands:", "",
              "    " + PROFILE_CMDS["pmc"].format(c="FETCH_SIZE"),
@@ -304,7 +305,7 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
                  "rocprofv3's derived MfmaUtil (MFMA-busy cycles summed over SIMDs, over "
                  "GPU-active cycles times the SIMD count, in percent) and the bf16 MFMA "
                  "operations (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = flop), mean over the "
-                 "dispatches of the beacon passes; TFLOP/s uses the kernel-trace mean duration. "
+                 "dispatches in the profiled passes; TFLOP/s uses the kernel-trace mean duration. "
                  f"Dense bf16 peak {MFMA_BF16_PEAK_TFLOPS:.0f} TFLOP/s.", "", "Command:", "",
                  "    " + PROFILE_CMDS["pmc_mfma"], "",
                  "| kernel | MfmaUtil % | bf16 MFMA flop per launch | TFLOP/s | % of peak |",
