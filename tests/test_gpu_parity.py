@@ -810,8 +810,12 @@ def test_evict_pass_k256_group8():
     _pass_case(wl, N=[1088, 1000], P=[512, 512], B=1024, selector="beacon")
 
 
-def test_evict_pass_skips_invalid_request_entirely():
-    say("pass atomic skip")
+@pytest.mark.parametrize("mode", ["beacon", "beacon-separate", "shared", "random"])
+def test_evict_pass_skips_invalid_request_entirely(mode):
+    """A request that fails a device check is left untouched by every kernel
+    of the pass (fused or separate, per head or shared), and the others
+    proceed."""
+    say("pass atomic skip", mode)
     wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=256, prompt_len=100, seq_len=320)
     batch = synth.make_batch(wl)
     bt = batch.block_table.clone()
@@ -820,23 +824,32 @@ def test_evict_pass_skips_invalid_request_entirely():
     cache = device_cache(batch, [320, 320, 320], [100, 300, 100])   # request 1: P > B
     k_in, v_in = host_pools(cache)
     q, b, c = batch.queries.cuda(), batch.beacons.cuda(), batch.counts.cuda()
-    st = bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, 256, queries=q, beacons=b, counts=c,
-                           check=False)
+    if mode == "random":
+        rid = torch.arange(3, dtype=torch.int64).cuda()
+        pss = torch.zeros(3, dtype=torch.int32).cuda()
+        st = bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, 256, seed=5, request_ids=rid,
+                               pass_idx=pss, check=False)
+    else:
+        st = bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, 256, queries=q, beacons=b, counts=c,
+                               check=False, separate_steps=mode == "beacon-separate",
+                               shared_positions=mode == "shared")
     torch.cuda.synchronize()
     assert int(st.item()) == (1 << bk.BKV_ERR_BUDGET) | (1 << bk.BKV_ERR_BLOCK_TABLE)
     k_out, v_out = host_pools(cache)
     bn = b.cpu().numpy()
     cn = c.cpu().numpy()
     btn = batch.block_table.numpy()
-    for hc, layer, r, h in head_iter(cache):
-        if r in (1, 2):
-            assert np.array_equal(bn[hc].view(np.int32), batch.beacons[hc].numpy().view(np.int32))
-            assert np.array_equal(cn[hc], batch.counts[hc].numpy())
-        else:
-            assert cn[hc].sum() == batch.counts[hc].numpy().sum() + q.shape[1] * q.shape[2]
-    # request 1's blocks are untouched; request 0 was compacted
+    if mode != "random":
+        for hc, layer, r, h in head_iter(cache):
+            if r in (1, 2):
+                assert np.array_equal(bn[hc].view(np.int32),
+                                      batch.beacons[hc].numpy().view(np.int32))
+                assert np.array_equal(cn[hc], batch.counts[hc].numpy())
+            else:
+                assert cn[hc].sum() == batch.counts[hc].numpy().sum() + q.shape[1] * q.shape[2]
+    # request 1's blocks and request 2's valid blocks are untouched; request 0 was compacted
     for layer in range(2):
-        for blk in btn[1]:
+        for blk in list(btn[1]) + [x for x in btn[2] if x < wl.num_blocks]:
             assert np.array_equal(k_in[layer][blk], k_out[layer][blk])
             assert np.array_equal(v_in[layer][blk], v_out[layer][blk])
     assert any(not np.array_equal(k_in[0][blk], k_out[0][blk]) for blk in btn[0])
