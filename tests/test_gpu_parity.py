@@ -855,12 +855,14 @@ def test_evict_pass_skips_invalid_request_entirely(mode):
     assert any(not np.array_equal(k_in[0][blk], k_out[0][blk]) for blk in btn[0])
 
 
-def test_evict_pass_replays_from_a_hip_graph():
+@pytest.mark.parametrize("mode", ["beacon", "shared", "random"])
+def test_evict_pass_replays_from_a_hip_graph(mode):
     """The pass allocates nothing and sets no memory, so it can be captured: a
-    captured beacon pass, replayed several times from restored inputs (eager
-    copies and synchronisations between replays), matches the eager pass
-    byte for byte every time."""
-    say("graph replay")
+    captured pass (each fused kernel: per-head beacon, shared beacon, random),
+    replayed several times from restored inputs (eager copies and
+    synchronisations between replays), matches the eager pass byte for byte
+    every time."""
+    say("graph replay", mode)
     wl = small(n_layers=2, n_requests=3, n_kv_heads=2, budget=512, prompt_len=200, seq_len=576)
     batch = synth.make_batch(wl)
     N, P, B = [576, 541, 400], [200, 333, 100], 512
@@ -871,10 +873,13 @@ def test_evict_pass_replays_from_a_hip_graph():
     k0 = [k.clone() for k in cache.k_pools]
     v0 = [v.clone() for v in cache.v_pools]
     b, c = b0.clone(), c0.clone()
-    sc = torch.zeros((HC, S)).cuda()
-    keep = torch.zeros((HC, B), dtype=torch.int32).cuda()
+    sc = torch.zeros((HC, S), dtype=torch.int32 if mode == "random" else torch.float32).cuda()
+    rows = cache.n_layers * cache.n_requests if mode == "shared" else HC
+    keep = torch.zeros((rows, B), dtype=torch.int32).cuda()
     st = torch.zeros(1, dtype=torch.int32).cuda()
     ws = torch.empty(1 << 20, dtype=torch.uint8).cuda()
+    rid = torch.arange(7, 7 + cache.n_requests, dtype=torch.int64).cuda()
+    pss = torch.full((cache.n_requests,), 3, dtype=torch.int32).cuda()
 
     def restore():
         b.copy_(b0)
@@ -883,8 +888,14 @@ def test_evict_pass_replays_from_a_hip_graph():
             dst.copy_(src)
 
     def run():
-        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
-                          scores_out=sc, keep_out=keep, status=st, check=False, workspace=ws)
+        if mode == "random":
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=9, request_ids=rid,
+                              pass_idx=pss, scores_out=sc, keep_out=keep, status=st, check=False,
+                              workspace=ws)
+        else:
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                              scores_out=sc, keep_out=keep, status=st, check=False,
+                              workspace=ws, shared_positions=mode == "shared")
 
     run()                                   # eager reference
     torch.cuda.synchronize()
