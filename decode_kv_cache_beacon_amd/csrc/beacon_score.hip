@@ -53,7 +53,6 @@
 // compacts every head.
 
 #include "compact_util.h"
-#include "select_util.h"
 
 namespace bkv {
 namespace {
@@ -187,15 +186,20 @@ constexpr int kFuseWsumOff = (sizeof(RadixScratch) + 15) & ~15;
 constexpr int kFuseKeyOff = 2048;
 static_assert(kFuseWsumOff + 4 * (16 + 1) <= kFuseKeyOff, "fused scratch overlaps the keys");
 
-// Top-B selection of one head-cache from the scores its workgroup has just
-// written (row_scores: the N - P candidates), then the in-place compaction.
-// Same results as topk_select_kernel followed by kv_compact_kernel: the prompt
-// is kept, the B - P best candidates survive with ties to the earlier slot,
-// and the survivors move to the front in slot order.
+// Top-B selection from the scores the workgroup has just written, then the
+// in-place compaction.  `rows` holds n score rows of the N - P candidates
+// (stride apart), merged by their maximum: one row for a head-cache, or the H
+// heads of a (layer, request) with shared positions.  The selection is
+// applied to the n heads x.head0 .. x.head0 + n - 1 (pos0: the first one's
+// pos ids row).  Same results as topk_select_kernel (or its shared form)
+// followed by kv_compact_kernel: the prompt is kept, the B - P best
+// candidates survive with ties to the earlier slot, and the survivors move to
+// the front in slot order.
 template <int kThreads>
-__device__ void select_compact(const CacheView& c, const HeadIdx& x, int N, int P, int B,
-                               const float* row_scores, const int* s_bt, uint8_t* scratch,
-                               int32_t* keep_row, int32_t* pos) {
+__device__ void select_compact(const CacheView& c, int layer, int head0, int n, int N, int P,
+                               int B, const float* rows, int stride, const int* s_bt,
+                               uint8_t* scratch, int32_t* keep_row, int32_t* pos0,
+                               int pos_stride) {
     const int tid = threadIdx.x;
     if (N <= B) {  // nothing to evict: every slot stays where it is
         if (keep_row)
@@ -206,84 +210,25 @@ __device__ void select_compact(const CacheView& c, const HeadIdx& x, int N, int 
         for (int i = tid; i < P; i += kThreads) keep_row[i] = i;
     const int m = N - P, k = B - P;
     if (k == 0) return;  // only the prompt survives, and it does not move
-    RadixScratch* rs = reinterpret_cast<RadixScratch*>(scratch);
     int* s_wsum = reinterpret_cast<int*>(scratch + kFuseWsumOff);
-    int* s_drop = s_wsum + kThreads / kWave;
     uint32_t* s_key = reinterpret_cast<uint32_t*>(scratch + kFuseKeyOff);
-    int* s_keep = reinterpret_cast<int*>(s_key + m);  // kept candidate r -> its slot
     __syncthreads();  // the scores written by group 0 are visible to every thread
     for (int i = tid; i < m; i += kThreads) {
-        const uint32_t w = __float_as_uint(row_scores[i]);
-        s_key[i] = (w >> 31) ? 0u : w;  // non-negative fp32 orders like its bits
-    }
-    if (tid == 0) *s_drop = m;
-    int need;
-    const uint32_t T = radix_select<kThreads>(s_key, m, k, rs, &need);
-    emit_selected<kThreads>(
-        s_key, m, T, need, s_wsum,
-        [&](int r, int i) {
-            s_keep[r] = P + i;
-            if (keep_row) keep_row[P + r] = P + i;
-        },
-        [&](int i) { atomicMin(s_drop, i); });
-    __syncthreads();
-    // Survivors before the first dropped candidate keep their slots.  Four
-    // rounds per barrier (64 rows with 256 threads): shorter rounds than the
-    // standalone compaction's interleave better with the CU's other workgroup,
-    // which is scoring (about 2% faster than eight at the serving shape).
-    const int i0 = P + *s_drop;
-    move_rows<kThreads, 4>(c.k_pools[x.layer], c.v_pools[x.layer], s_bt, c.H, x.head, s_keep,
-                           P, i0, B, pos);
-}
-
-// Shared positions: one selection for the H heads of a (layer, request),
-// from the largest of their scores (rows[h * stride + i], h < H), applied to
-// every head's rows -- the same results as bkv_topk_select_shared followed by
-// bkv_kv_compact with keep_shared.  Called once all H heads are scored.
-template <int kThreads>
-__device__ void shared_select_compact(const CacheView& c, const HeadIdx& x, int N, int P, int B,
-                                      const float* rows, int stride, const int* s_bt,
-                                      uint8_t* scratch, int32_t* keep_row, int32_t* pos0,
-                                      int pos_stride) {
-    const int tid = threadIdx.x;
-    if (N <= B) {  // nothing to evict
-        if (keep_row)
-            for (int i = tid; i < B; i += kThreads) keep_row[i] = (i < N) ? i : -1;
-        return;
-    }
-    if (keep_row)
-        for (int i = tid; i < P; i += kThreads) keep_row[i] = i;
-    const int m = N - P, k = B - P;
-    if (k == 0) return;
-    RadixScratch* rs = reinterpret_cast<RadixScratch*>(scratch);
-    int* s_wsum = reinterpret_cast<int*>(scratch + kFuseWsumOff);
-    int* s_drop = s_wsum + kThreads / kWave;
-    uint32_t* s_key = reinterpret_cast<uint32_t*>(scratch + kFuseKeyOff);
-    int* s_keep = reinterpret_cast<int*>(s_key + m);
-    __syncthreads();  // every head's scores are visible to every thread
-    for (int i = tid; i < m; i += kThreads) {
         uint32_t v = 0;
-        for (int h = 0; h < c.H; ++h) {
+        for (int h = 0; h < n; ++h) {
             const uint32_t w = __float_as_uint(rows[(size_t)h * stride + i]);
-            v = max(v, (w >> 31) ? 0u : w);
+            v = max(v, (w >> 31) ? 0u : w);  // non-negative fp32 orders like its bits
         }
         s_key[i] = v;
     }
-    if (tid == 0) *s_drop = m;
-    int need;
-    const uint32_t T = radix_select<kThreads>(s_key, m, k, rs, &need);
-    emit_selected<kThreads>(
-        s_key, m, T, need, s_wsum,
-        [&](int r, int i) {
-            s_keep[r] = P + i;
-            if (keep_row) keep_row[P + r] = P + i;
-        },
-        [&](int i) { atomicMin(s_drop, i); });
-    __syncthreads();
-    const int i0 = P + *s_drop;
-    for (int h = 0; h < c.H; ++h)
-        move_rows<kThreads, 4>(c.k_pools[x.layer], c.v_pools[x.layer], s_bt, c.H, h, s_keep, P,
-                               i0, B, pos0 ? pos0 + (size_t)h * pos_stride : nullptr);
+    // Four rounds per barrier (64 rows with 256 threads): shorter rounds than
+    // the standalone compaction's interleave better with the CU's other
+    // workgroup, which is scoring (about 2% faster than eight at the serving
+    // shape).
+    select_and_move<kThreads, 4>(c, layer, head0, n, P, B, m, s_key,
+                                 reinterpret_cast<int*>(s_key + m),
+                                 reinterpret_cast<RadixScratch*>(scratch), s_wsum,
+                                 s_wsum + kThreads / kWave, s_bt, keep_row, pos0, pos_stride);
 }
 
 // What the score body does after scoring: nothing, the per-head selection
@@ -692,14 +637,16 @@ __device__ __forceinline__ bool score_head(
     // Every ring load has landed (the loaders waited for all of them before
     // the last hand-over) and every ring read is done: the ring is free.
     if constexpr (kMode == kEvictHead)
-        select_compact<kWaves * kWave>(c, x, N, P, B, out, s_bt, s_ring, keep_row,
-                                       pos_ids ? pos_ids + (size_t)hc * pos_stride : nullptr);
+        select_compact<kWaves * kWave>(c, x.layer, x.head, 1, N, P, B, out, stride, s_bt,
+                                       s_ring, keep_row,
+                                       pos_ids ? pos_ids + (size_t)hc * pos_stride : nullptr,
+                                       pos_stride);
     if constexpr (kMode == kEvictShared)
-        if (last_head)
-            shared_select_compact<kWaves * kWave>(
-                c, x, N, P, B, scores + (size_t)(hc - x.head) * stride, stride, s_bt, s_ring,
-                keep_row, pos_ids ? pos_ids + (size_t)(hc - x.head) * pos_stride : nullptr,
-                pos_stride);
+        if (last_head)  // every head of the (layer, request) is scored
+            select_compact<kWaves * kWave>(
+                c, x.layer, 0, c.H, N, P, B, scores + (size_t)(hc - x.head) * stride, stride,
+                s_bt, s_ring, keep_row,
+                pos_ids ? pos_ids + (size_t)(hc - x.head) * pos_stride : nullptr, pos_stride);
     return true;
 }
 

@@ -1,9 +1,10 @@
 // compact_util.h -- the order-preserving in-place row move shared by the
-// compaction kernel and the fused score-select-compact kernel.  Called by all
-// threads of the block; it synchronises.
+// compaction kernel and the fused kernels, and the fused kernels' common
+// selection-and-move tail.  Called by all threads of the block; they
+// synchronise.
 #pragma once
 
-#include "bkv_internal.h"
+#include "select_util.h"
 
 namespace bkv {
 
@@ -59,6 +60,38 @@ __device__ void move_rows(uint64_t kbase, uint64_t vbase, const int* s_bt, int H
             }
         }
     }
+}
+
+// The tail of the fused kernels.  The m = N - P candidate keys of one
+// selection are staged in s_key (the writes of every thread issued before the
+// call: radix_select opens with a barrier), and the request has N > B and
+// B > P.  Selects the top B - P keys (ties to the earlier slot), writes the
+// kept candidates' slots in order to s_keep and to keep_row (nullable, after
+// the prompt entries the caller has written), and moves the survivors of the
+// n heads head0 .. head0 + n - 1 of `layer` in place (pos0: the first head's
+// pos ids row, nullable).  Survivors before the first dropped candidate keep
+// their slots.
+template <int kThreads, int kRounds>
+__device__ void select_and_move(const CacheView& c, int layer, int head0, int n, int P, int B,
+                                int m, const uint32_t* s_key, int* s_keep, RadixScratch* rs,
+                                int* s_wsum, int* s_drop, const int* s_bt, int32_t* keep_row,
+                                int32_t* pos0, int pos_stride) {
+    if (threadIdx.x == 0) *s_drop = m;
+    int need;
+    const uint32_t T = radix_select<kThreads>(s_key, m, B - P, rs, &need);
+    emit_selected<kThreads>(
+        s_key, m, T, need, s_wsum,
+        [&](int r, int i) {
+            s_keep[r] = P + i;
+            if (keep_row) keep_row[P + r] = P + i;
+        },
+        [&](int i) { atomicMin(s_drop, i); });
+    __syncthreads();
+    const int i0 = P + *s_drop;
+    for (int h = 0; h < n; ++h)
+        move_rows<kThreads, kRounds>(c.k_pools[layer], c.v_pools[layer], s_bt, c.H, head0 + h,
+                                     s_keep, P, i0, B,
+                                     pos0 ? pos0 + (size_t)h * pos_stride : nullptr);
 }
 
 }  // namespace bkv

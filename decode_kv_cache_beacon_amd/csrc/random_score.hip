@@ -13,7 +13,6 @@
 // evaluates one counter and scores the four slots 4g .. 4g+3.
 
 #include "compact_util.h"
-#include "select_util.h"
 
 namespace bkv {
 namespace {
@@ -131,21 +130,12 @@ __global__ __launch_bounds__(kThreads) void random_evict_kernel(
     const int nb = (N + kBlock - 1) / kBlock;
     const int32_t* bt = c.block_table + (size_t)x.req * c.max_blocks;
     for (int i = tid; i < nb; i += kThreads) s_bt[i] = bt[i];
-    if (tid == 0) s_drop = m;
-    int* s_keep = reinterpret_cast<int*>(s_key + stride);  // kept candidate r -> its slot
-    int need;  // radix_select starts with a barrier: the keys above are complete
-    const uint32_t T = radix_select<kThreads>(s_key, m, k, &s_rs, &need);
-    emit_selected<kThreads>(
-        s_key, m, T, need, s_wsum,
-        [&](int r, int i) {
-            s_keep[r] = P + i;
-            if (keep_row) keep_row[P + r] = P + i;
-        },
-        [&](int i) { atomicMin(&s_drop, i); });
-    __syncthreads();
-    // survivors before the first dropped candidate keep their slots
-    move_rows<kThreads>(c.k_pools[x.layer], c.v_pools[x.layer], s_bt, c.H, x.head, s_keep, P,
-                        P + s_drop, B, pos_ids ? pos_ids + (size_t)hc * pos_stride : nullptr);
+    // kept candidate r -> its slot, after the stride keys
+    select_and_move<kThreads, 8>(c, x.layer, x.head, 1, P, B, m, s_key,
+                                 reinterpret_cast<int*>(s_key + stride), &s_rs, s_wsum, &s_drop,
+                                 s_bt, keep_row,
+                                 pos_ids ? pos_ids + (size_t)hc * pos_stride : nullptr,
+                                 pos_stride);
 }
 
 }  // namespace
