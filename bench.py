@@ -326,43 +326,89 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
           f"in {out}")
 
 
-def side_pass(torch, bk, synth, wl, steps, warmup, dev):
-    """Mean per-kernel milliseconds of `steps` whole beacon passes over a
-    freshly generated workload (no refill between passes: the lengths stay,
-    so every pass does the same work)."""
+def side_pass(torch, bk, synth, wl, steps, warmup, dev, selector="beacon"):
+    """Mean per-kernel milliseconds of `steps` whole passes over a freshly
+    generated workload (no refill between passes: the lengths stay, so every
+    pass scores and selects the same number of slots), and the mean number of
+    rows the compaction moved."""
     batch = synth.make_batch(wl, dev)
     cache = bk.PagedCache(batch.k_pools, batch.v_pools, batch.block_table, batch.seq_len,
                           batch.prompt_len)
-    HC, B = cache.n_head_caches, wl.budget
+    HC, R, B = cache.n_head_caches, cache.n_requests, wl.budget
     N = batch.seq_len.cpu().tolist()
     P = batch.prompt_len.cpu().tolist()
     stride = max(n - p for n, p in zip(N, P))
-    scores = torch.zeros((HC, stride), dtype=torch.float32, device=dev)
+    beacon = selector == "beacon"
+    scores = torch.zeros((HC, stride), dtype=torch.float32 if beacon else torch.int32,
+                         device=dev)
     keep = torch.zeros((HC, B), dtype=torch.int32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    runs = []
+    rid = torch.arange(R, dtype=torch.int64, device=dev)
+    pss = torch.zeros(R, dtype=torch.int32, device=dev)
+    ar = torch.arange(B, device=dev, dtype=torch.int32)
+    nk = torch.tensor([min(N[(hc // cache.n_kv_heads) % R], B) for hc in range(HC)],
+                      device=dev)
+    runs, moved = [], []
+    n_ev = 5 if beacon else 4
     for s in range(warmup + steps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-        bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=batch.queries,
-                          beacons=batch.beacons, counts=batch.counts, window=wl.window,
-                          bonus=wl.bonus, scores_out=scores, keep_out=keep, score_stride=stride,
-                          status=status, check=False, timing_events=ev)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        if beacon:
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=batch.queries,
+                              beacons=batch.beacons, counts=batch.counts, window=wl.window,
+                              bonus=wl.bonus, scores_out=scores, keep_out=keep,
+                              score_stride=stride, status=status, check=False, timing_events=ev)
+        else:
+            pss.fill_(s)
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed, request_ids=rid,
+                              pass_idx=pss, scores_out=scores, keep_out=keep,
+                              score_stride=stride, status=status, check=False, timing_events=ev)
         if s >= warmup:
             runs.append(ev)
+            neq = keep != ar
+            first = torch.where(neq.any(1), neq.int().argmax(1), torch.full_like(nk, B))
+            moved.append((nk - first).clamp(min=0).sum())
     torch.cuda.synchronize()
     bk.check_status(status, f"{wl.name} side passes")
+
     def span(i, j):
         return sum(e[i].elapsed_time(e[j]) for e in runs) / len(runs)
 
-    if stride + B <= bk.FUSED_MAX_ENTRIES:  # the pass ran the fused kernel
+    fused = stride + B <= bk.FUSED_MAX_ENTRIES
+    if beacon and fused:
         kms = {"beacon_update": span(0, 1), "beacon_evict": span(1, 4)}
-    else:
+    elif beacon:
         kms = {n: span(i, i + 1) for i, n in
                enumerate(["beacon_update", "beacon_score", "topk_select", "kv_compact"])}
-    ms = span(0, 4)
+    elif fused:
+        kms = {"random_evict": span(0, 3)}
+    else:
+        kms = {n: span(i, i + 1) for i, n in
+               enumerate(["random_score", "topk_select", "kv_compact"])}
+    ms = span(0, n_ev - 1)
+    M = float(sum(int(m) for m in moved)) / len(moved)
     del batch, cache, scores, keep
     torch.cuda.empty_cache()
-    return ms, kms, N, P
+    return ms, kms, N, P, M
+
+
+def side_line(wl, ms, kms, N, P, M, selector):
+    """A side workload's pass rate and, for the fused kernel, its algorithmic
+    GB/s against the HBM peak."""
+    e = {"ms_per_pass": round(ms, 4), "passes_per_s": round(1000.0 / ms, 3),
+         "kernel_ms": {k: round(v, 4) for k, v in kms.items()}, "moved_rows_per_pass": int(M)}
+    hc_per_req = wl.n_layers * wl.n_kv_heads
+    if selector == "beacon" and "beacon_evict" in kms:
+        nbytes = algorithmic_bytes(wl, N, P, M, hc_per_req)["beacon_evict"]
+        gbps = nbytes / (kms["beacon_evict"] * 1e-3) / 1e9
+        e.update({"fused_algorithmic_bytes": int(nbytes), "fused_gbps": round(gbps, 1),
+                  "fused_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)})
+    elif selector == "random" and "random_evict" in kms:
+        nbytes = 4 * M * 256 + hc_per_req * sum((n - p) * 4 + wl.budget * 4
+                                                for n, p in zip(N, P))
+        gbps = nbytes / (kms["random_evict"] * 1e-3) / 1e9
+        e.update({"fused_algorithmic_bytes": int(nbytes), "fused_gbps": round(gbps, 1),
+                  "fused_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)})
+    return e
 
 
 def main():
@@ -833,14 +879,14 @@ def main():
     # the other configurations' one-shot shapes, reported beside the line
     if not args.no_side:
         twl = synth.WORKLOADS["tiny"]
-        tms, tk, _, _ = side_pass(torch, bk, synth, twl, 20, 3, dev)
+        tms, tk, _, _, _ = side_pass(torch, bk, synth, twl, 20, 3, dev)
         result["tiny_one_shot"] = {
             "us_per_pass": round(tms * 1e3, 1),
             "kernel_us": {k: round(v * 1e3, 1) for k, v in tk.items()},
             "note": "one head-cache, N = 4096 (512 prompt), K = 64, B = 1024, 256 queries: "
                     "latency-bound, one workgroup per kernel"}
         owl = synth.WORKLOADS["qwen3_32b_r32"].with_(n_layers=1, seq_len=32768)
-        oms, ok, oN, oP = side_pass(torch, bk, synth, owl, 5, 1, dev)
+        oms, ok, oN, oP, _ = side_pass(torch, bk, synth, owl, 5, 1, dev)
         ohc = owl.n_head_caches
         oflops = 2.0 * owl.n_beacons * owl.head_dim * ohc * (oN[0] + (oN[0] - oP[0]))
         otf = oflops / (ok["beacon_score"] * 1e-3) / 1e12
@@ -851,6 +897,21 @@ def main():
             "note": f"one layer of the 64-layer shape: {ohc} head-caches, N = 32768 "
                     f"({oP[0]} prompt), K = {owl.n_beacons}, B = {owl.budget}, "
                     f"G = {owl.group}; scoring flops count both logit passes"}
+        # the 64-layer K = 256 batch at the three budgets, steady state N = B + 64
+        c4 = {}
+        for Bx in (1024, 2048, 4096):
+            w4 = synth.WORKLOADS["qwen3_32b_r32"].with_(budget=Bx, seq_len=Bx + 64)
+            c4[f"B{Bx}"] = side_line(w4, *side_pass(torch, bk, synth, w4, 8, 2, dev), "beacon")
+        c4["note"] = ("64 layers, 32 requests, 8 KV heads, G = 8, K = 256, P = 512, "
+                      "N = B + 64: maintenance, then the fused kernel")
+        result["qwen3_32b_budgets"] = c4
+        # the long-prompt serving variant, both selectors on the same shape
+        lwl = synth.WORKLOADS["long_prompt_r128"]
+        result["long_prompt"] = {
+            sel: side_line(lwl, *side_pass(torch, bk, synth, lwl, 8, 2, dev, sel), sel)
+            for sel in ("beacon", "random")}
+        result["long_prompt"]["note"] = ("serving shape with prompts drawn from 256..1536, "
+                                         "B = 3072, N = 3136")
 
     if args.copy_calibration:
         src = torch.empty(1 << 31, dtype=torch.int16, device=dev)
