@@ -25,8 +25,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
 BKV_ABI_VERSION = 6
-# bkv_evict_pass fuses score, select and compact (per-head selection with row
-# compaction, either selector) when score_stride + budget is at most this
+# bkv_evict_pass fuses score, select and compact (row compaction with per-head
+# selection, or shared positions for the beacon selector) when score_stride +
+# budget is at most this
 FUSED_MAX_ENTRIES = 15872
 BKV_OK, BKV_ERR_NULL, BKV_ERR_INVALID, BKV_ERR_BUDGET, BKV_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BKV_ERR_WORKSPACE, BKV_ERR_HIP, BKV_ERR_LENGTH, BKV_ERR_BLOCK_TABLE = 5, 6, 7, 8
@@ -521,8 +522,8 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
     pages per request instead (no rows move; keep_out is then the kept pages).
 
     separate_steps: run score, select and compact as three kernels even where
-    the fused kernel applies (per-head selection with row compaction, either
-    selector).
+    a fused kernel applies (row compaction with per-head selection for either
+    selector, or with shared positions for the beacon selector).
 
     timing_events: optional list of torch.cuda.Event(enable_timing=True), 5 for
     the beacon selector and 4 for the random one, recorded around each step

@@ -340,7 +340,9 @@ int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, si
 
 /* Runs, on `stream`: (beacon) maintenance -> beacon scoring -> selection ->
  * compaction, or (random) random scoring -> selection -> compaction; with
- * page_retention, bkv_page_retain takes the place of the last two.
+ * page_retention, bkv_page_retain takes the place of the last two.  Scoring,
+ * selection and compaction run as one fused kernel where separate_steps
+ * allows it (see there); the results are those of the separate kernels.
  * A request that fails a device check (lengths, block ids, budget) is left
  * entirely untouched -- beacons, counts, cache and pos_ids -- and flagged in
  * *status. */
