@@ -722,6 +722,25 @@ hipError_t launch_any(const CacheView& c, const float* beacons, const int32_t* c
                       int32_t* keep_out, int32_t* pos_ids, int pos_stride, Check ck,
                       int32_t* status, hipStream_t s) {
     if (c.L * c.R * c.H == 0) return hipSuccess;
+    // At most one workgroup per CU (a small batch, a single head-cache): with
+    // K <= 128, four tile phases instead of two keep twice the key tiles in
+    // flight in the CU's one workgroup (the ring takes 128 KiB; one workgroup
+    // per CU fits).  The fused kernel of one 4096-key head-cache at K = 64
+    // took 100 us instead of 146.  At K = 256 the wider layout was no faster.
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 0;
+    const long units = kMode == kEvictShared ? (long)c.L * c.R : (long)c.L * c.R * c.H;
+    if (units <= cus && K <= 128) {
+        if (K <= 64)
+            launch_cfg<2, 4, 1, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse,
+                                          B, keep_out, pos_ids, pos_stride, ck, status, s);
+        else
+            launch_cfg<2, 4, 2, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse,
+                                          B, keep_out, pos_ids, pos_stride, ck, status, s);
+        return hipGetLastError();
+    }
     if (K <= 64)
         launch_cfg<2, 2, 1, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
                                       keep_out, pos_ids, pos_stride, ck, status, s);
