@@ -810,6 +810,50 @@ def test_evict_pass_k256_group8():
     _pass_case(wl, N=[1088, 1000], P=[512, 512], B=1024, selector="beacon")
 
 
+@pytest.mark.parametrize("selector", ["beacon", "random"])
+def test_fused_kernels_at_their_lds_capacity(selector):
+    """score_stride + budget exactly at the fused limit: the candidate keys and
+    the keep list fill the LDS the fused kernels hold them in (more head-caches
+    than CUs, so the standard layout runs), and the result equals the separate
+    kernels'; one entry more and the pass runs the separate kernels."""
+    say("fused at LDS capacity", selector)
+    B, P, N = 4096, 0, 11776
+    assert (N - P) + B == bk.FUSED_MAX_ENTRIES
+    wl = small(n_layers=1, n_requests=33, n_kv_heads=8, n_beacons=64, budget=B, prompt_len=0,
+               seq_len=N, steps=2)
+    batch = synth.make_batch(wl)
+    R = wl.n_requests
+    outs = []
+    for stride, separate in ((N - P, False), (N - P, True), (N - P + 1, False)):
+        cache = device_cache(batch, [N] * R, [P] * R)
+        HC = cache.n_head_caches
+        assert HC > 256
+        keep = torch.full((HC, B), -7, dtype=torch.int32).cuda()
+        pos = torch.arange(cache.max_slots, dtype=torch.int32).repeat(HC, 1).cuda()
+        if selector == "beacon":
+            sc = torch.zeros((HC, stride)).cuda()
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=batch.queries.cuda(),
+                              beacons=batch.beacons.cuda(), counts=batch.counts.cuda(),
+                              keep_out=keep, scores_out=sc, pos_ids=pos, score_stride=stride,
+                              separate_steps=separate)
+        else:
+            sc = torch.zeros((HC, stride), dtype=torch.int32).cuda()
+            bk.bkv_evict_pass(cache, bk.BKV_SELECT_RANDOM, B, seed=3,
+                              request_ids=torch.arange(R, dtype=torch.int64).cuda(),
+                              pass_idx=torch.ones(R, dtype=torch.int32).cuda(), keep_out=keep,
+                              scores_out=sc, pos_ids=pos, score_stride=stride,
+                              separate_steps=separate)
+        torch.cuda.synchronize()
+        outs.append((keep.cpu(), pos.cpu(), sc[:, :N - P].cpu(),
+                     cache.k_pools[0].view(torch.int16).cpu(),
+                     cache.v_pools[0].view(torch.int16).cpu()))
+    for got in outs[1:]:
+        for x, y in zip(got, outs[0]):
+            assert torch.equal(x, y)
+    kn = outs[0][0].numpy()
+    assert all(len(keep_rows(r)) == B and np.all(np.diff(keep_rows(r)) > 0) for r in kn)
+
+
 @pytest.mark.parametrize("mode", ["beacon", "beacon-separate", "shared", "random"])
 def test_evict_pass_skips_invalid_request_entirely(mode):
     """A request that fails a device check is left untouched by every kernel
