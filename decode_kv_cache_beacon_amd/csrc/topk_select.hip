@@ -23,9 +23,12 @@
 namespace bkv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+// kThreads: 256 for the serving shapes (about a thousand candidates; 64 and
+// 128 threads were slower), 1024 from kWideFrom candidates on, where one
+// workgroup per CU is typical (one-shot passes over long caches).
+constexpr int kWideFrom = 8192;
 
+template <int kThreads>
 __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
                                                                const uint32_t* __restrict__ scores,
                                                                int is_f32, int stride,
@@ -34,7 +37,7 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
                                                                int32_t* status) {
     extern __shared__ uint32_t s_key[];  // [stride]
     __shared__ RadixScratch s_rs;
-    __shared__ int s_wsum[kWaves];
+    __shared__ int s_wsum[kThreads / kWave];
 
     const int unit = blockIdx.x;  // head-cache, or (layer, request) when shared
     const HeadIdx x = shared ? HeadIdx{unit / c.R, unit % c.R, 0} : split_hc(c, unit);
@@ -86,14 +89,23 @@ hipError_t launch_topk_select(const CacheView& c, const void* scores, int kind, 
     const int units = c.L * c.R * (shared ? 1 : c.H);
     if (units == 0) return hipSuccess;
     const size_t lds = (size_t)stride * sizeof(uint32_t);
+    const bool wide = stride >= kWideFrom;
+    const void* fn = wide ? (const void*)topk_select_kernel<1024>
+                          : (const void*)topk_select_kernel<256>;
     if (lds > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(topk_select_kernel, dim3(units), dim3(kThreads), lds, s, c,
-                       static_cast<const uint32_t*>(scores), kind == BKV_SCORE_F32 ? 1 : 0,
-                       stride, shared ? score_heads : 1, shared, budget, keep, ck, status);
+    const auto* sc = static_cast<const uint32_t*>(scores);
+    const int is_f32 = kind == BKV_SCORE_F32 ? 1 : 0;
+    const int heads = shared ? score_heads : 1;
+    if (wide)
+        hipLaunchKernelGGL(topk_select_kernel<1024>, dim3(units), dim3(1024), lds, s, c, sc,
+                           is_f32, stride, heads, shared, budget, keep, ck, status);
+    else
+        hipLaunchKernelGGL(topk_select_kernel<256>, dim3(units), dim3(256), lds, s, c, sc, is_f32,
+                           stride, heads, shared, budget, keep, ck, status);
     return hipGetLastError();
 }
 
