@@ -198,6 +198,18 @@ PROFILE_CMDS = {
                  "--count-cap 0"),
     "summary": "python bench.py --summarize-profiles <prof-dir> <pmc-dir>",
 }
+# instruction-issue counters, two runs (at most 8 SQ counters per run)
+SQ_COUNTERS = {
+    "SQ1": ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_SALU",
+            "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_INST_ANY"),
+    "SQ2": ("SQ_INSTS_VMEM", "SQ_INSTS_SMEM", "SQ_INST_CYCLES_VMEM", "SQ_ACTIVE_INST_LDS",
+            "SQ_ACTIVE_INST_SCA", "SQ_WAIT_ANY", "SQ_INSTS_BRANCH", "SQ_ACTIVE_INST_ANY"),
+}
+for _run, _cs in SQ_COUNTERS.items():
+    PROFILE_CMDS["pmc_" + _run.lower()] = (
+        f"cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {' '.join(_cs)} -f csv -d <pmc-dir>/{_run} "
+        f"-o {_run} -- python3 <repo>/bench.py --steps 2 --warmup 0 --no-cpu-baseline "
+        "--no-shared --no-pages --no-side --no-random --no-separate --count-cap 0")
 
 
 def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
@@ -321,6 +333,47 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
             lines.append(f"| {k} | {u:.1f} | {flop:.3e} | {tf:.1f} | "
                          f"{100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f} |")
         with open(os.path.join(out, f"{workload}_mfma_counters.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    # instruction issue (optional fourth and fifth counter runs)
+    sq = {}
+    for run in SQ_COUNTERS:
+        for path in glob.glob(os.path.join(pmc_dir, run, "*counter_collection.csv")):
+            for r in csv.DictReader(open(path)):
+                k = kid(r["Kernel_Name"])
+                if k:
+                    d = sq.setdefault(k, {}).setdefault(r["Counter_Name"], {})
+                    key = r.get("Dispatch_Id") or r.get("Correlation_Id") or len(d)
+                    d[key] = d.get(key, 0.0) + float(r["Counter_Value"])
+    if sq:
+        def m(k, c):
+            v = sq[k].get(c)
+            return statistics.mean(v.values()) if v else float("nan")
+        lines = [f"# Instruction issue per launch, workload {workload}", "",
+                 "rocprofv3 SQ counters, mean over the dispatches in the profiled passes (the "
+                 "per-head beacon pass, maintenance then the fused kernel, and the decode attention "
+                 "the benchmark runs after it). Instructions "
+                 "are per wave. The shares divide each wave's cycles executing any instruction, "
+                 "VALU or scalar instructions, and waiting, by its lifetime (SQ_WAVE_CYCLES; the "
+                 "same units). With w waves resident per SIMD, a SIMD's issue is busy about w "
+                 "times the per-wave share.", "", "Commands:", "",
+                 *["    " + PROFILE_CMDS["pmc_" + run.lower()] for run in SQ_COUNTERS],
+                 "    " + PROFILE_CMDS["summary"], "",
+                 "| kernel | waves | VALU | SALU | LDS | VMEM | branch | any-issue share | "
+                 "VALU share | scalar share | wait share |",
+                 "|---|---|---|---|---|---|---|---|---|---|---|"]
+        for k in KERNEL_SOURCES:
+            if k not in sq:
+                continue
+            w = m(k, "SQ_WAVES")
+            life = m(k, "SQ_WAVE_CYCLES")
+            lines.append(
+                f"| {k} | {w:.0f} | {m(k, 'SQ_INSTS_VALU') / w:.0f} | "
+                f"{m(k, 'SQ_INSTS_SALU') / w:.0f} | {m(k, 'SQ_INSTS_LDS') / w:.0f} | "
+                f"{m(k, 'SQ_INSTS_VMEM') / w:.0f} | {m(k, 'SQ_INSTS_BRANCH') / w:.0f} | "
+                f"{m(k, 'SQ_ACTIVE_INST_ANY') / life:.2f} | "
+                f"{m(k, 'SQ_ACTIVE_INST_VALU') / life:.2f} | "
+                f"{m(k, 'SQ_ACTIVE_INST_SCA') / life:.2f} | {m(k, 'SQ_WAIT_ANY') / life:.2f} |")
+        with open(os.path.join(out, f"{workload}_issue_counters.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
     print(f"wrote {workload}_kernel_trace.md, {workload}_hbm_counters.md and traffic.json "
           f"in {out}")

@@ -95,6 +95,22 @@ def fake_profiles(tmp_path):
                 (5, SCORE, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 300.0),
                 (6, SCORE, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 400.0),
                 (5, SCORE, "MfmaUtil", 30.0), (6, SCORE, "MfmaUtil", 40.0)])
+    # issue counters: two runs, per-dispatch rows summed, then averaged over dispatches
+    _write_csv(str(pmc / "SQ1" / "SQ1_counter_collection.csv"), cc,
+               [(5, SCORE, "SQ_WAVES", 40.0), (5, SCORE, "SQ_WAVES", 60.0),
+                (6, SCORE, "SQ_WAVES", 100.0),
+                (5, SCORE, "SQ_WAVE_CYCLES", 1000.0), (6, SCORE, "SQ_WAVE_CYCLES", 3000.0),
+                (5, SCORE, "SQ_INSTS_VALU", 5000.0), (6, SCORE, "SQ_INSTS_VALU", 7000.0),
+                (5, SCORE, "SQ_INSTS_SALU", 2000.0), (6, SCORE, "SQ_INSTS_SALU", 2000.0),
+                (5, SCORE, "SQ_INSTS_LDS", 300.0), (6, SCORE, "SQ_INSTS_LDS", 100.0),
+                (5, SCORE, "SQ_ACTIVE_INST_VALU", 600.0), (6, SCORE, "SQ_ACTIVE_INST_VALU", 600.0),
+                (5, SCORE, "SQ_WAIT_INST_ANY", 1.0), (6, SCORE, "SQ_WAIT_INST_ANY", 1.0)])
+    _write_csv(str(pmc / "SQ2" / "SQ2_counter_collection.csv"), cc,
+               [(5, SCORE, "SQ_INSTS_VMEM", 100.0), (6, SCORE, "SQ_INSTS_VMEM", 300.0),
+                (5, SCORE, "SQ_INSTS_BRANCH", 50.0), (6, SCORE, "SQ_INSTS_BRANCH", 150.0),
+                (5, SCORE, "SQ_ACTIVE_INST_ANY", 1000.0), (6, SCORE, "SQ_ACTIVE_INST_ANY", 1000.0),
+                (5, SCORE, "SQ_ACTIVE_INST_SCA", 200.0), (6, SCORE, "SQ_ACTIVE_INST_SCA", 200.0),
+                (5, SCORE, "SQ_WAIT_ANY", 500.0), (6, SCORE, "SQ_WAIT_ANY", 300.0)])
     out = tmp_path / "out"
     bench.summarize_profiles(str(prof), str(pmc), "fake", out=str(out))
     return out
@@ -138,6 +154,17 @@ def test_summary_mfma(fake_profiles):
     assert cells[0] == "35.0"
     assert float(cells[1]) == pytest.approx(400 * 512)
     assert float(cells[2]) == pytest.approx(round(400 * 512 / 2e-3 / 1e12, 1))
+
+
+def test_summary_issue(fake_profiles):
+    text = (fake_profiles / "fake_issue_counters.md").read_text()
+    row = next(r for r in text.splitlines() if r.startswith("| beacon_score"))
+    cells = [c.strip() for c in row.split("|")[2:12]]
+    # 100 waves, 2000 wave-cycles per dispatch on average; instructions per wave
+    assert cells[:6] == ["100", "60", "20", "2", "2", "1"]
+    # shares of the wave lifetime: any 1000/2000, VALU 600/2000, scalar 200/2000, wait 400/2000
+    assert cells[6:] == ["0.50", "0.30", "0.10", "0.20"]
+    assert bench.PROFILE_CMDS["pmc_sq1"] in text and bench.PROFILE_CMDS["pmc_sq2"] in text
 
 
 def test_profile_commands_run_committed_files_only():
