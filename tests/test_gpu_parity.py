@@ -207,6 +207,8 @@ def test_select_one_shot_32k_candidates():
 @pytest.mark.parametrize("K,prewarm,G,T,cap", [
     (5, False, 4, 16, 0), (64, True, 4, 64, 0), (128, True, 4, 64, 0), (256, True, 8, 64, 0),
     (64, False, 1, 256, 0), (40, True, 2, 33, 0),
+    # a final chunk of one step; every step of a K = 256 set filling empty rows
+    (64, True, 1, 33, 0), (256, False, 8, 5, 0),
     # capped counts (moving average once a row is full)
     (128, True, 4, 64, 16), (64, True, 4, 64, 8), (5, False, 4, 16, 1), (40, True, 2, 33, 3)])
 def test_beacon_update_teacher_forced(K, prewarm, G, T, cap):
