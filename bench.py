@@ -157,14 +157,26 @@ def cpu_baseline(wl, budget_s):
     }
 
 
-def stored_traffic(kernel):
+DEFAULT_WORKLOAD = "serving_r128"
+
+
+def traffic_file(workload, out=None):
+    """Per-kernel counter bytes of a workload: profiles/traffic.json for the
+    default workload, profiles/<workload>_traffic.json for the others."""
+    name = "traffic.json" if workload == DEFAULT_WORKLOAD else f"{workload}_traffic.json"
+    return os.path.join(out or os.path.join(ROOT, "profiles"), name)
+
+
+def stored_traffic(kernel, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    taken on the current kernel source and on this workload (else None)."""
+    path = traffic_file(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
+    if t.get("_calibration", {}).get("workload") != workload:
+        return None
     e = t.get(kernel)
     if not e or e.get("source_sha") != kernel_source_hash(kernel):
         return None
@@ -212,11 +224,79 @@ for _run, _cs in SQ_COUNTERS.items():
         "--no-shared --no-pages --no-side --no-random --no-separate --count-cap 0")
 
 
+def summarize_hbm(paths, workload, out, kid):
+    """profiles/<workload>_hbm_counters.md and the workload's traffic file from
+    the FETCH_SIZE and WRITE_SIZE runs, scaled by the 4 GiB copy's readings."""
+    import csv
+    import statistics
+
+    counters = {}
+    for c, found in paths.items():
+        path = found[0]
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != c:
+                continue
+            name = r["Kernel_Name"]
+            k = "copy" if COPY_SYMBOL in name else kid(name)
+            if k:
+                per.setdefault(k, []).append(float(r["Counter_Value"]))
+        counters[c] = per
+    # the 4 GiB device copy: the largest copyBuffer dispatches
+    copy_bytes = 1 << 32
+    big = max(counters["WRITE_SIZE"]["copy"])
+    n_big = sum(1 for v in counters["WRITE_SIZE"]["copy"] if v >= 0.99 * big)
+    fetch_copy = sorted(counters["FETCH_SIZE"]["copy"])[-n_big:]
+    write_copy = sorted(counters["WRITE_SIZE"]["copy"])[-n_big:]
+    f_read = copy_bytes / (statistics.mean(fetch_copy) * 1024)
+    f_write = copy_bytes / (statistics.mean(write_copy) * 1024)
+    traffic = {"_calibration": {
+        "copy_bytes_read": copy_bytes, "copy_bytes_written": copy_bytes,
+        "copy_fetch_kib": statistics.mean(fetch_copy), "copy_write_kib": statistics.mean(write_copy),
+        "read_factor": f_read, "write_factor": f_write, "workload": workload,
+        "commands": [profile_cmd("pmc", workload, c="FETCH_SIZE"),
+                     profile_cmd("pmc", workload, c="WRITE_SIZE"), profile_cmd("summary", workload)]}}
+    lines = [f"# HBM traffic per launch, workload {workload}", "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over each kernel's dispatches in the "
+             "profiled passes) from two rocprofv3 counter runs, each scaled by what the same counter reads "
+             f"for a plain 4 GiB device copy: read factor {f_read:.4f}, write factor "
+             f"{f_write:.4f}.", "", "Commands:", "",
+             "    " + profile_cmd("pmc", workload, c="FETCH_SIZE"),
+             "    " + profile_cmd("pmc", workload, c="WRITE_SIZE"),
+             "    " + profile_cmd("summary", workload), "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | written GB | total GB | "
+             "source hash |", "|---|---|---|---|---|---|---|"]
+    for k in KERNEL_SOURCES:
+        if k not in counters["FETCH_SIZE"] or k not in counters["WRITE_SIZE"]:
+            continue
+        fk = statistics.mean(counters["FETCH_SIZE"][k])
+        wk = statistics.mean(counters["WRITE_SIZE"][k])
+        rb, wb = fk * 1024 * f_read, wk * 1024 * f_write
+        sha = kernel_source_hash(k)
+        traffic[k] = {"fetch_kib": fk, "write_kib": wk, "bytes_read": rb, "bytes_written": wb,
+                      "bytes_per_launch": rb + wb, "source_sha": sha}
+        lines.append(f"| {k} | {fk:.0f} | {wk:.0f} | {rb / 1e9:.2f} | {wb / 1e9:.2f} | "
+                     f"{(rb + wb) / 1e9:.2f} | {sha} |")
+    with open(os.path.join(out, f"{workload}_hbm_counters.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(traffic_file(workload, out), "w") as f:
+        json.dump(traffic, f, indent=1)
+
+
+def profile_cmd(key, workload, **fmt):
+    """The command that made a profile summary, for this workload."""
+    cmd = PROFILE_CMDS[key].format(**fmt) if fmt else PROFILE_CMDS[key]
+    if workload != DEFAULT_WORKLOAD:
+        cmd = cmd.replace("bench.py --", f"bench.py --workload {workload} --")
+    return cmd
+
+
 def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
     """Write the committed summaries from rocprofv3 output: per-kernel
     durations (kernel trace), HBM bytes per launch from FETCH_SIZE and
     WRITE_SIZE, each scaled by what the counter reads for the 4 GiB device
-    copy the benchmark also runs, and profiles/traffic.json for the roofline."""
+    copy the benchmark also runs, and the workload's traffic file for the
+    roofline; the counter runs are optional."""
     import csv
     import glob
     import statistics
@@ -240,7 +320,7 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
              "shared-position passes (beacon fused, beacon with separate kernels, random), then "
              "as many page-retention passes of each selector (maintenance and scoring also run "
              "in the page-retention beacon passes).", "",
-             "Command:", "", "    " + PROFILE_CMDS["trace"], "",
+             "Command:", "", "    " + profile_cmd("trace", workload), "",
              "| kernel | launches | mean ms | min ms | max ms |", "|---|---|---|---|---|"]
     for k in KERNEL_SOURCES:
         if k in dur:
@@ -250,57 +330,11 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
     with open(os.path.join(out, f"{workload}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
-    counters = {}
-    for c in ("FETCH_SIZE", "WRITE_SIZE"):
-        path = glob.glob(os.path.join(pmc_dir, c, "*counter_collection.csv"))[0]
-        per = {}
-        for r in csv.DictReader(open(path)):
-            if r["Counter_Name"] != c:
-                continue
-            name = r["Kernel_Name"]
-            k = "copy" if COPY_SYMBOL in name else kid(name)
-            if k:
-                per.setdefault(k, []).append(float(r["Counter_Value"]))
-        counters[c] = per
-    # the 4 GiB device copy: the largest copyBuffer dispatches
-    copy_bytes = 1 << 32
-    big = max(counters["WRITE_SIZE"]["copy"])
-    n_big = sum(1 for v in counters["WRITE_SIZE"]["copy"] if v >= 0.99 * big)
-    fetch_copy = sorted(counters["FETCH_SIZE"]["copy"])[-n_big:]
-    write_copy = sorted(counters["WRITE_SIZE"]["copy"])[-n_big:]
-    f_read = copy_bytes / (statistics.mean(fetch_copy) * 1024)
-    f_write = copy_bytes / (statistics.mean(write_copy) * 1024)
-    traffic = {"_calibration": {
-        "copy_bytes_read": copy_bytes, "copy_bytes_written": copy_bytes,
-        "copy_fetch_kib": statistics.mean(fetch_copy), "copy_write_kib": statistics.mean(write_copy),
-        "read_factor": f_read, "write_factor": f_write, "workload": workload,
-        "commands": [PROFILE_CMDS["pmc"].format(c="FETCH_SIZE"),
-                     PROFILE_CMDS["pmc"].format(c="WRITE_SIZE"), PROFILE_CMDS["summary"]]}}
-    lines = [f"# HBM traffic per launch, workload {workload}", "",
-             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over each kernel's dispatches in the "
-             "profiled passes) from two rocprofv3 counter runs, each scaled by what the same counter reads "
-             f"for a plain 4 GiB device copy: read factor {f_read:.4f}, write factor "
-             f"{f_write:.4f}.", "", "Commands:", "",
-             "    " + PROFILE_CMDS["pmc"].format(c="FETCH_SIZE"),
-             "    " + PROFILE_CMDS["pmc"].format(c="WRITE_SIZE"),
-             "    " + PROFILE_CMDS["summary"], "",
-             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | written GB | total GB | "
-             "source hash |", "|---|---|---|---|---|---|---|"]
-    for k in KERNEL_SOURCES:
-        if k not in counters["FETCH_SIZE"] or k not in counters["WRITE_SIZE"]:
-            continue
-        fk = statistics.mean(counters["FETCH_SIZE"][k])
-        wk = statistics.mean(counters["WRITE_SIZE"][k])
-        rb, wb = fk * 1024 * f_read, wk * 1024 * f_write
-        sha = kernel_source_hash(k)
-        traffic[k] = {"fetch_kib": fk, "write_kib": wk, "bytes_read": rb, "bytes_written": wb,
-                      "bytes_per_launch": rb + wb, "source_sha": sha}
-        lines.append(f"| {k} | {fk:.0f} | {wk:.0f} | {rb / 1e9:.2f} | {wb / 1e9:.2f} | "
-                     f"{(rb + wb) / 1e9:.2f} | {sha} |")
-    with open(os.path.join(out, f"{workload}_hbm_counters.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
-    with open(os.path.join(out, "traffic.json"), "w") as f:
-        json.dump(traffic, f, indent=1)
+    # HBM bytes (optional: both counter runs)
+    hbm = {c: glob.glob(os.path.join(pmc_dir, c, "*counter_collection.csv"))
+           for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    if all(hbm.values()):
+        summarize_hbm(hbm, workload, out, kid)
 
     # MFMA utilisation (optional third counter run)
     mfma = glob.glob(os.path.join(pmc_dir, "MFMA", "*counter_collection.csv"))
@@ -319,7 +353,7 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
                  "operations (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 = flop), mean over the "
                  "dispatches in the profiled passes; TFLOP/s uses the kernel-trace mean duration. "
                  f"Dense bf16 peak {MFMA_BF16_PEAK_TFLOPS:.0f} TFLOP/s.", "", "Command:", "",
-                 "    " + PROFILE_CMDS["pmc_mfma"], "",
+                 "    " + profile_cmd("pmc_mfma", workload), "",
                  "| kernel | MfmaUtil % | bf16 MFMA flop per launch | TFLOP/s | % of peak |",
                  "|---|---|---|---|---|"]
         for k in KERNEL_SOURCES:
@@ -356,8 +390,8 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
                  "VALU or scalar instructions, and waiting, by its lifetime (SQ_WAVE_CYCLES; the "
                  "same units). With w waves resident per SIMD, a SIMD's issue is busy about w "
                  "times the per-wave share.", "", "Commands:", "",
-                 *["    " + PROFILE_CMDS["pmc_" + run.lower()] for run in SQ_COUNTERS],
-                 "    " + PROFILE_CMDS["summary"], "",
+                 *["    " + profile_cmd("pmc_" + run.lower(), workload) for run in SQ_COUNTERS],
+                 "    " + profile_cmd("summary", workload), "",
                  "| kernel | waves | VALU | SALU | LDS | VMEM | branch | any-issue share | "
                  "VALU share | scalar share | wait share |",
                  "|---|---|---|---|---|---|---|---|---|---|---|"]
@@ -375,8 +409,7 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
                 f"{m(k, 'SQ_ACTIVE_INST_SCA') / life:.2f} | {m(k, 'SQ_WAIT_ANY') / life:.2f} |")
         with open(os.path.join(out, f"{workload}_issue_counters.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
-    print(f"wrote {workload}_kernel_trace.md, {workload}_hbm_counters.md and traffic.json "
-          f"in {out}")
+    print(f"wrote the {workload} summaries in {out}")
 
 
 def side_pass(torch, bk, synth, wl, steps, warmup, dev, selector="beacon"):
@@ -469,7 +502,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="serving_r128")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-random", action="store_true", help="skip the random-selector A/B")
     ap.add_argument("--no-side", action="store_true",
@@ -611,7 +644,7 @@ def main():
         gbps = nbytes / (ms_ * 1e-3) / 1e9
         e = {"ms": round(ms_, 4), "algorithmic_bytes": int(nbytes), "gbps": round(gbps, 1),
              "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
-        tb = stored_traffic(n)
+        tb = stored_traffic(n, wl.name)
         if tb:
             e["traffic_gbps"] = round(tb / (ms_ * 1e-3) / 1e9, 1)
         return e
@@ -629,7 +662,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4)}
     roof["kernel"] = dom
-    roof["traffic"] = stored_traffic(dom)
+    roof["traffic"] = stored_traffic(dom, wl.name)
 
     # the same pass with score, select and compact as three kernels: the
     # per-step breakdown (and what the fused kernel saves)

@@ -125,11 +125,12 @@ def test_summary_durations(fake_profiles):
     # the fused kernel is told apart from the scoring kernel it shares a source with
     assert rows["beacon_evict"] == ["1", "7.000", "7.000", "7.000"]
     assert set(rows) == {"beacon_score", "kv_compact", "beacon_evict"}  # others not listed
-    assert bench.PROFILE_CMDS["trace"] in text
+    assert bench.profile_cmd("trace", "fake") in text
+    assert "bench.py --workload fake --steps" in text
 
 
 def test_summary_traffic_calibration(fake_profiles):
-    t = json.loads((fake_profiles / "traffic.json").read_text())
+    t = json.loads((fake_profiles / "fake_traffic.json").read_text())
     cal = t["_calibration"]
     assert cal["read_factor"] == pytest.approx(0.8)
     assert cal["write_factor"] == pytest.approx(2.0)
@@ -164,7 +165,26 @@ def test_summary_issue(fake_profiles):
     assert cells[:6] == ["100", "60", "20", "2", "2", "1"]
     # shares of the wave lifetime: any 1000/2000, VALU 600/2000, scalar 200/2000, wait 400/2000
     assert cells[6:] == ["0.50", "0.30", "0.10", "0.20"]
-    assert bench.PROFILE_CMDS["pmc_sq1"] in text and bench.PROFILE_CMDS["pmc_sq2"] in text
+    assert bench.profile_cmd("pmc_sq1", "fake") in text
+    assert bench.profile_cmd("pmc_sq2", "fake") in text
+
+
+def test_stored_traffic_belongs_to_its_workload(tmp_path, monkeypatch):
+    path = tmp_path / "t.json"
+    monkeypatch.setattr(bench, "traffic_file", lambda workload, out=None: str(path))
+    sha = bench.kernel_source_hash("beacon_evict")
+    path.write_text(json.dumps({"_calibration": {"workload": "a"},
+                                "beacon_evict": {"bytes_per_launch": 5.0, "source_sha": sha}}))
+    assert bench.stored_traffic("beacon_evict", "a") == 5.0
+    assert bench.stored_traffic("beacon_evict", "b") is None      # another workload's bytes
+    path.write_text(json.dumps({"_calibration": {"workload": "a"},
+                                "beacon_evict": {"bytes_per_launch": 5.0, "source_sha": "x"}}))
+    assert bench.stored_traffic("beacon_evict", "a") is None      # taken on other source
+
+
+def test_traffic_file_names():
+    assert bench.traffic_file(bench.DEFAULT_WORKLOAD).endswith("profiles/traffic.json")
+    assert bench.traffic_file("a").endswith("profiles/a_traffic.json")
 
 
 def test_profile_commands_run_committed_files_only():
