@@ -138,9 +138,10 @@ def cpu_baseline(wl, budget_s):
         Nh = np.array([N[(hc // H) % R] for hc in hcs], np.int32)
         Ph = np.array([P[(hc // H) % R] for hc in hcs], np.int32)
         t1 = time.perf_counter()
-        oracle.evict_batch(q[sl], b[sl], c[sl], keys, vals, Nh, Ph, wl.budget, wl.window,
-                           wl.bonus)
+        nb, nc, _, _, _ = oracle.evict_batch(q[sl], b[sl], c[sl], keys, vals, Nh, Ph, wl.budget,
+                                             wl.window, wl.bonus)
         elapsed += time.perf_counter() - t1
+        b[sl], c[sl] = nb, nc
         done += sl.stop - sl.start
     per_hc = elapsed / done
     pass_s = per_hc * wl.n_head_caches

@@ -151,9 +151,19 @@ def _check(code: int, where: str):
         raise BkvError(code, where)
 
 
-def _status(status: Optional[torch.Tensor], device):
+def _for_stream(t: torch.Tensor, stream) -> torch.Tensor:
+    """A tensor this module created on the current stream and hands to kernels
+    on `stream`: its initialisation is ordered before `stream`'s later work, and
+    the caching allocator does not reuse its memory until that work is done."""
+    if stream is not None and stream != torch.cuda.current_stream():
+        stream.wait_stream(torch.cuda.current_stream())
+        t.record_stream(stream)
+    return t
+
+
+def _status(status: Optional[torch.Tensor], device, stream=None):
     if status is None:
-        return torch.zeros(1, dtype=torch.int32, device=device), True
+        return _for_stream(torch.zeros(1, dtype=torch.int32, device=device), stream), True
     _need(status, "status", torch.int32)
     return status, False
 
@@ -271,7 +281,7 @@ def bkv_beacon_score(cache: PagedCache, beacons, counts, scores, window=64, bonu
         raise ValueError("scores must be [HC, stride]")
     if lse is not None:
         _need(lse, "lse", torch.float32, (HC, K))
-    st, own = _status(status, cache.device)
+    st, own = _status(status, cache.device, stream)
     c = cache.struct()
     code = _lib.bkv_beacon_score(ctypes.byref(c), _ptr(beacons), _ptr(counts), K, int(window),
                                  float(bonus), _ptr(scores), scores.shape[1], _ptr(lse), _ptr(st),
@@ -300,7 +310,7 @@ def bkv_random_score(cache: PagedCache, seed, request_ids, pass_idx, scores,
     _need(scores, "scores", torch.int32)
     if scores.dim() != 2 or scores.shape[0] != rows:
         raise ValueError(f"scores must be [{rows}, stride]")
-    st, own = _status(status, cache.device)
+    st, own = _status(status, cache.device, stream)
     c = cache.struct()
     code = _lib.bkv_random_score(ctypes.byref(c), int(seed) & (2**64 - 1), _ptr(request_ids),
                                  _ptr(pass_idx), layout, _ptr(scores),
@@ -328,7 +338,7 @@ def bkv_topk_select(cache: PagedCache, scores, budget, keep, status=None, check=
     if scores.dim() != 2 or scores.shape[0] != HC:
         raise ValueError("scores must be [HC, stride]")
     _need(keep, "keep", torch.int32, (HC, budget))
-    st, own = _status(status, cache.device)
+    st, own = _status(status, cache.device, stream)
     c = cache.struct()
     code = _lib.bkv_topk_select(ctypes.byref(c), _ptr(scores), kind, scores.shape[1], int(budget),
                                 _ptr(keep), _ptr(st), _stream(stream))
@@ -352,7 +362,7 @@ def bkv_topk_select_shared(cache: PagedCache, scores, budget, keep, status=None,
         raise ValueError("scores must be [n_layers * n_requests * S, stride]")
     S = scores.shape[0] // LR
     _need(keep, "keep", torch.int32, (LR, budget))
-    st, own = _status(status, cache.device)
+    st, own = _status(status, cache.device, stream)
     c = cache.struct()
     code = _lib.bkv_topk_select_shared(ctypes.byref(c), _ptr(scores), kind, scores.shape[1], S,
                                        int(budget), _ptr(keep), _ptr(st), _stream(stream))
@@ -375,7 +385,7 @@ def bkv_kv_compact(cache: PagedCache, keep, budget, pos_ids=None, status=None, c
         if pos_ids.dim() != 2 or pos_ids.shape[0] != HC:
             raise ValueError("pos_ids must be [HC, stride]")
         pos_stride = pos_ids.shape[1]
-    st, own = _status(status, cache.device)
+    st, own = _status(status, cache.device, stream)
     c = cache.struct()
     code = _lib.bkv_kv_compact(ctypes.byref(c), _ptr(keep), int(budget), int(bool(keep_shared)),
                                _ptr(pos_ids), pos_stride, _ptr(st), _stream(stream))
@@ -403,7 +413,7 @@ def bkv_page_retain(cache: PagedCache, scores, budget, keep_pages, block_table_o
     _need(block_table_out, "block_table_out", torch.int32, (R, cache.max_blocks))
     _need(seq_len_out, "seq_len_out", torch.int32, (R,))
     _need(freed_blocks, "freed_blocks", torch.int32, (R, cache.max_blocks))
-    st, own = _status(status, cache.device)
+    st, own = _status(status, cache.device, stream)
     c = cache.struct()
     code = _lib.bkv_page_retain(ctypes.byref(c), _ptr(scores), kind, scores.shape[1], int(rows),
                                 int(budget), _ptr(keep_pages), _ptr(block_table_out),
@@ -425,7 +435,7 @@ def bkv_decode_attention(cache: PagedCache, queries, out, scale=None, status=Non
     G = queries.shape[1]
     _need(out, "out", torch.float32, (HC, G, HEAD_DIM))
     sc = HEAD_DIM ** -0.5 if scale is None else float(scale)
-    st, own = _status(status, cache.device)
+    st, own = _status(status, cache.device, stream)
     c = cache.struct()
     code = _lib.bkv_decode_attention(ctypes.byref(c), _ptr(queries), G, sc, _ptr(out), _ptr(st),
                                      _stream(stream))
@@ -544,10 +554,10 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
         a.n_timing_events = len(handles)
     need = bkv_workspace_size(cache, a)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=cache.device)
+        workspace = _for_stream(torch.empty(need, dtype=torch.uint8, device=cache.device), stream)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8)
-    st, own = _status(status, cache.device)
+    st, own = _status(status, cache.device, stream)
     c = cache.struct()
     code = _lib.bkv_evict_pass(ctypes.byref(c), ctypes.byref(a), _ptr(workspace),
                                0 if workspace is None else workspace.numel(), _ptr(st),

@@ -80,6 +80,16 @@ size_t keep_cols(const bkv_pass_args* a) {
     return a->page_retention ? (size_t)(a->budget / kBlock) : (size_t)a->budget;
 }
 
+// Row compaction runs scoring (or the draws), selection and compaction as
+// one kernel when its LDS holds the candidates and keep list: per head for
+// either selector, or shared positions for the beacon selector.  The fused
+// kernels keep the keep list on chip (written out only to keep_out).
+bool fused_pass(const bkv_pass_args* a, int stride) {
+    return !a->page_retention && !a->separate_steps &&
+           (!a->shared_positions || a->selector == BKV_SELECT_BEACON) &&
+           (int64_t)stride + a->budget <= kFusedMaxEntries;
+}
+
 int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     const int max_slots = v.max_blocks * kBlock;
     const int stride = a->score_stride > 0 ? a->score_stride : max_slots;
@@ -96,7 +106,7 @@ int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
         L->scores_off = off;
         off = round_up(off + score_rows(v, a) * (size_t)stride * 4, 256);
     }
-    if (!a->keep_out) {
+    if (!a->keep_out && !fused_pass(a, stride)) {
         L->keep_off = off;
         off = round_up(off + keep_rows(v, a) * keep_cols(a) * 4, 256);
     }
@@ -335,8 +345,7 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
     // row compaction: one kernel for score, select and compact when its LDS
     // holds the candidates and keep list (per head for either selector, or
     // shared positions for the beacon selector)
-    const bool fused = !pages && !a->separate_steps && (!shared || beacon) &&
-                       (int64_t)L.stride + a->budget <= kFusedMaxEntries;
+    const bool fused = fused_pass(a, L.stride);
     if (fused && beacon) {
         he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
                                   a->assign, a->count_cap, &v, all, status, s);

@@ -283,12 +283,17 @@ def num_threads() -> int:
     return int(lib().oracle_num_threads())
 
 
-def evict_batch(q, beacons, counts, keys, vals, N, P, B, W=64, bonus=1.0):
+def evict_batch(q, beacons, counts, keys, vals, N, P, B, W=64, bonus=1.0, strict=True):
     """Beacon eviction pass over H independent dense head-caches (OpenMP).
 
     q[H][T][G][d] bf16 bits, beacons[H][K][d] f32, counts[H][K] i32,
     keys/vals[H][Nmax][d] bf16 bits, N/P[H] i32.  Returns
-    (beacons', counts', keep[H][B], kout[H][B][d], vout[H][B][d]).
+    (beacons', counts', keep[H][B], kout[H][B][d], vout[H][B][d]); keep rows
+    are -1 past the kept count and kout/vout rows past it stay zero.  A
+    head-cache whose prompt exceeds the budget is refused: its keep row stays
+    -1 and nothing is compacted (its beacons are still updated).  strict=True
+    raises on any refusal; strict=False appends the number of refusals to the
+    returned tuple.
     """
     q = _c(q, np.uint16)
     H, T, G, d = q.shape
@@ -306,6 +311,8 @@ def evict_batch(q, beacons, counts, keys, vals, N, P, B, W=64, bonus=1.0):
     fails = lib().oracle_evict_batch(H, T, G, d, K, int(B), int(W), float(bonus), Nmax,
                                      _ptr(n), _ptr(p), _ptr(q), _ptr(b), _ptr(c), _ptr(k),
                                      _ptr(v), _ptr(keep), _ptr(ko), _ptr(vo))
-    if fails:
-        raise ValueError(f"{fails} head-caches refused (prompt exceeds budget)")
-    return b, c, keep, ko, vo
+    if strict:
+        if fails:
+            raise ValueError(f"{fails} head-caches refused (prompt exceeds budget)")
+        return b, c, keep, ko, vo
+    return b, c, keep, ko, vo, int(fails)

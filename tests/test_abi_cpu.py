@@ -199,13 +199,26 @@ def test_workspace_and_pass_validation():
     n = ctypes.c_size_t(0)
     assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
     HC = 2 * 3 * 8
-    assert n.value >= HC * 160 * 4 + HC * 64 * 4
+    # per-head random pass: the fused kernel keeps the keep lists on chip
+    assert HC * 160 * 4 <= n.value < HC * 160 * 4 + 256
+    a.separate_steps = 1          # three kernels: the keep lists go through the workspace
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
+    assert HC * 160 * 4 + HC * 64 * 4 <= n.value < HC * 160 * 4 + HC * 64 * 4 + 512
+    a.separate_steps = 0
+    a.budget = 15872 - 160 + 1    # past the fused kernel's LDS: keep lists in the workspace
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value >= HC * 160 * 4 + HC * a.budget * 4
+    a.budget = 64
     a.shared_positions = 1        # random + shared: one score row and one keep row per (layer, request)
     assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
     assert HC // 8 * (160 + 64) * 4 <= n.value < HC * 64 * 4
-    a.selector = bk.BKV_SELECT_BEACON   # beacon + shared: per-head scores, shared keep rows
+    a.selector = bk.BKV_SELECT_BEACON   # beacon + shared (fused): per-head scores only
+    assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
+    assert HC * 160 * 4 <= n.value < HC * 160 * 4 + 256
+    a.separate_steps = 1               # separate kernels: plus the shared keep rows
     assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == 0
     assert HC * 160 * 4 + HC // 8 * 64 * 4 <= n.value < HC * 160 * 4 + HC * 64 * 4
+    a.separate_steps = 0
     a.shared_positions = 2
     assert bk._lib.bkv_workspace_size(ctypes.byref(c), ctypes.byref(a), ctypes.byref(n)) == \
         bk.BKV_ERR_INVALID

@@ -585,6 +585,47 @@ def test_compaction_is_numpy_gather():
     assert oracle.kv_compact(rows, np.zeros(0, np.int32)).shape == (0, 128)
 
 
+def test_evict_batch_is_the_per_head_steps_composed():
+    """The whole-pass oracle (the CPU baseline's timed routine) equals the
+    pinned per-head steps called one head-cache at a time: update, score,
+    select, compact, bit for bit, with its own strides over a padded batch."""
+    H, T, G, d, K, B, W, bonus = 9, 5, 3, 128, 40, 48, 8, 1.0
+    Nmax = 83
+    N = np.array([80, 70, 49, 48, 33, 64, 77, 56, 83], np.int32)
+    P = np.array([10, 0, 20, 5, 33, 50, 47, 3, 12], np.int32)   # head 5: P > B, refused
+    rng = np.random.default_rng(2024)
+    q = bf16_bits(rng.normal(size=(H, T, G, d)))
+    keys = bf16_bits(rng.normal(size=(H, Nmax, d)) * rng.uniform(0.5, 2, (H, 1, d)))
+    vals = bf16_bits(rng.normal(size=(H, Nmax, d)))
+    beacons = rng.normal(size=(H, K, d)).astype(np.float32)
+    counts = rng.integers(1, 9, (H, K)).astype(np.int32)
+    counts[1, [3, 17, 39]] = 0          # rows still to be filled (MacQueen)
+    counts[4] = 0                       # a fresh beacon set: every step fills
+    beacons[counts == 0] = 0.0
+    b2, c2, keep, ko, vo, fails = oracle.evict_batch(q, beacons, counts, keys, vals, N, P, B,
+                                                     W, bonus, strict=False)
+    assert fails == 1
+    for h in range(H):
+        rb, rc, _ = oracle.beacon_update(q[h], beacons[h], counts[h])
+        assert np.array_equal(b2[h].view(np.int32), rb.view(np.int32)), h
+        assert np.array_equal(c2[h], rc), h
+        n, p = int(N[h]), int(P[h])
+        sc, _ = oracle.beacon_score(keys[h, :n], rb, rc, p, W, bonus)
+        if p > B:
+            with pytest.raises(ValueError):
+                oracle.topk_select(sc, n, p, B)
+            assert np.all(keep[h] == -1) and not ko[h].any() and not vo[h].any(), h
+            continue
+        rk = oracle.topk_select(sc, n, p, B)
+        nk = len(rk)
+        assert np.array_equal(keep[h, :nk], rk) and np.all(keep[h, nk:] == -1), h
+        assert np.array_equal(ko[h, :nk], oracle.kv_compact(keys[h, :n], rk)), h
+        assert np.array_equal(vo[h, :nk], oracle.kv_compact(vals[h, :n], rk)), h
+        assert not ko[h, nk:].any() and not vo[h, nk:].any(), h
+    with pytest.raises(ValueError):
+        oracle.evict_batch(q, beacons, counts, keys, vals, N, P, B, W, bonus)
+
+
 def test_gather_paged_reads_block_table():
     pool = RNG.integers(0, 2**16, (10, 2, 16, 4), dtype=np.uint16)
     table = np.array([7, 2, 9], np.int32)
