@@ -27,9 +27,6 @@ if ROOT not in sys.path:
 METRIC = "KV eviction passes/sec and achieved HBM GB/s (score+select+compact), % of peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E peak, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, vendor figure
-# fp32 FMA on the vector ALUs without packed forms: 256 CU x 4 SIMD x 16 lanes
-# x 2 flop x 2.4 GHz (packed fp32 forms are not used by this library)
-VALU_FP32_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 
 
 def log(*a):
@@ -67,27 +64,43 @@ KERNEL_SOURCES = {
 
 
 def algorithmic_bytes(wl, N, P, moved_rows, hc_per_req):
-    """Bytes each kernel must move at least once per pass.
+    """Bytes each kernel must move at least once per pass: the roofline basis.
 
+    For scoring and the fused pass these are the per-head-cache bytes of the
+    pass's definition: every key read once (N*d*2), the fp32 beacons (K*d*4)
+    and every moved row's K and V read and written (4*M*d*2); scores and keep
+    lists that stay on chip, block-table reads and re-reads of keys from the
+    caches are not counted (they are in extra_bytes).
     update : queries T*G*256 + beacons read+write 2*K*512 + counts 2*K*4
-    score  : keys N*256 + beacons K*512 + counts K*4 + block table ceil(N/16)*4
-             + scores written (N-P)*4
-    select : scores read (N-P)*4 + keep list written B*4
-    compact: moved rows 4*M*256 (K and V read and written) + keep list B*4
-    evict  : the fused score+select+compact kernel: the score bytes, the keep
-             list written B*4 and the moved rows 4*M*256 (the scores it reads
-             back and the keep list it keeps in LDS are not counted again)
+    score  : keys N*256 + beacons K*512
+    select : scores read (N-P)*4 + keep list written B*4 (its own input and
+             output: a separate kernel cannot keep them on chip)
+    compact: moved rows 4*M*256
+    evict  : the fused score+select+compact kernel: keys N*256 + beacons
+             K*512 + moved rows 4*M*256
     """
     T, G, K, B = wl.steps, wl.group, wl.n_beacons, wl.budget
     upd = sc = sel = 0
     for n, p in zip(N, P):
         upd += hc_per_req * (T * G * 256 + 2 * K * 512 + 2 * K * 4)
-        sc += hc_per_req * (n * 256 + K * 512 + K * 4 + -(-n // 16) * 4 + (n - p) * 4)
+        sc += hc_per_req * (n * 256 + K * 512)
         sel += hc_per_req * ((n - p) * 4 + B * 4)
+    moves = 4 * moved_rows * 256
+    return {"beacon_update": upd, "beacon_score": sc, "topk_select": sel, "kv_compact": moves,
+            "beacon_evict": sc + moves}
+
+
+def extra_bytes(wl, N, P, hc_per_req):
+    """Bytes the kernels also move that the roofline basis leaves out:
+    score  : counts K*4 + block table ceil(N/16)*4 + scores written (N-P)*4
+    compact: keep lists read B*4
+    evict  : the score extras + the keep list written B*4 (when the caller
+             asks for it, as the benchmark does)."""
+    K, B = wl.n_beacons, wl.budget
+    sc = sum(hc_per_req * (K * 4 + -(-n // 16) * 4 + (n - p) * 4) for n, p in zip(N, P))
     keep_lists = len(N) * hc_per_req * B * 4
-    cmp_ = 4 * moved_rows * 256 + keep_lists
-    return {"beacon_update": upd, "beacon_score": sc, "topk_select": sel, "kv_compact": cmp_,
-            "beacon_evict": sc + keep_lists + 4 * moved_rows * 256}
+    return {"beacon_update": 0, "beacon_score": sc, "topk_select": 0, "kv_compact": keep_lists,
+            "beacon_evict": sc + keep_lists}
 
 
 def cpu_model():
@@ -168,20 +181,26 @@ def traffic_file(workload, out=None):
     return os.path.join(out or os.path.join(ROOT, "profiles"), name)
 
 
-def stored_traffic(kernel, workload):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source and on this workload (else None)."""
+def stored_counters(kernel, workload):
+    """Per-launch figures from committed rocprofv3 counter runs (HBM bytes,
+    bf16 MFMA flop, instruction-issue shares), if they were taken on the
+    current kernel source and on this workload (else {})."""
     path = traffic_file(workload)
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         t = json.load(f)
-    if t.get("_calibration", {}).get("workload") != workload:
-        return None
+    if t.get("_workload", t.get("_calibration", {}).get("workload")) != workload:
+        return {}
     e = t.get(kernel)
     if not e or e.get("source_sha") != kernel_source_hash(kernel):
-        return None
-    return e.get("bytes_per_launch")
+        return {}
+    return e
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter runs, or None."""
+    return stored_counters(kernel, workload).get("bytes_per_launch")
 
 
 # kernel symbol fragment -> kernel id
@@ -251,7 +270,7 @@ def summarize_hbm(paths, workload, out, kid):
     write_copy = sorted(counters["WRITE_SIZE"]["copy"])[-n_big:]
     f_read = copy_bytes / (statistics.mean(fetch_copy) * 1024)
     f_write = copy_bytes / (statistics.mean(write_copy) * 1024)
-    traffic = {"_calibration": {
+    traffic = {"_workload": workload, "_calibration": {
         "copy_bytes_read": copy_bytes, "copy_bytes_written": copy_bytes,
         "copy_fetch_kib": statistics.mean(fetch_copy), "copy_write_kib": statistics.mean(write_copy),
         "read_factor": f_read, "write_factor": f_write, "workload": workload,
@@ -280,8 +299,7 @@ def summarize_hbm(paths, workload, out, kid):
                      f"{(rb + wb) / 1e9:.2f} | {sha} |")
     with open(os.path.join(out, f"{workload}_hbm_counters.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    with open(traffic_file(workload, out), "w") as f:
-        json.dump(traffic, f, indent=1)
+    return traffic
 
 
 def profile_cmd(key, workload, **fmt):
@@ -334,8 +352,12 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
     # HBM bytes (optional: both counter runs)
     hbm = {c: glob.glob(os.path.join(pmc_dir, c, "*counter_collection.csv"))
            for c in ("FETCH_SIZE", "WRITE_SIZE")}
+    counters = {"_workload": workload}
     if all(hbm.values()):
-        summarize_hbm(hbm, workload, out, kid)
+        counters = summarize_hbm(hbm, workload, out, kid)
+
+    def entry(k):
+        return counters.setdefault(k, {"source_sha": kernel_source_hash(k)})
 
     # MFMA utilisation (optional third counter run)
     mfma = glob.glob(os.path.join(pmc_dir, "MFMA", "*counter_collection.csv"))
@@ -367,6 +389,8 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
             tf = flop / (statistics.mean(dur[k]) * 1e-3) / 1e12 if k in dur and mops else float("nan")
             lines.append(f"| {k} | {u:.1f} | {flop:.3e} | {tf:.1f} | "
                          f"{100 * tf / MFMA_BF16_PEAK_TFLOPS:.1f} |")
+            if mops:
+                entry(k).update({"mfma_flop_per_launch": flop, "mfma_util_pct": u})
         with open(os.path.join(out, f"{workload}_mfma_counters.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
     # instruction issue (optional fourth and fifth counter runs)
@@ -408,8 +432,15 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
                 f"{m(k, 'SQ_ACTIVE_INST_ANY') / life:.2f} | "
                 f"{m(k, 'SQ_ACTIVE_INST_VALU') / life:.2f} | "
                 f"{m(k, 'SQ_ACTIVE_INST_SCA') / life:.2f} | {m(k, 'SQ_WAIT_ANY') / life:.2f} |")
+            entry(k).update({"issue_share": m(k, "SQ_ACTIVE_INST_ANY") / life,
+                             "valu_share": m(k, "SQ_ACTIVE_INST_VALU") / life,
+                             "wait_share": m(k, "SQ_WAIT_ANY") / life,
+                             "valu_insts_per_wave": m(k, "SQ_INSTS_VALU") / w})
         with open(os.path.join(out, f"{workload}_issue_counters.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
+    if len(counters) > 1:
+        with open(traffic_file(workload, out), "w") as f:
+            json.dump(counters, f, indent=1)
     print(f"wrote the {workload} summaries in {out}")
 
 
@@ -490,11 +521,13 @@ def side_line(wl, ms, kms, N, P, M, selector):
         e.update({"fused_algorithmic_bytes": int(nbytes), "fused_gbps": round(gbps, 1),
                   "fused_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)})
     elif selector == "random" and "random_evict" in kms:
-        nbytes = 4 * M * 256 + hc_per_req * sum((n - p) * 4 + wl.budget * 4
-                                                for n, p in zip(N, P))
+        # the random pass reads no key and no beacon: only the moved rows count
+        nbytes = 4 * M * 256
         gbps = nbytes / (kms["random_evict"] * 1e-3) / 1e9
         e.update({"fused_algorithmic_bytes": int(nbytes), "fused_gbps": round(gbps, 1),
-                  "fused_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)})
+                  "fused_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                  "fused_extra_bytes": int(hc_per_req * sum((n - p) * 4 + wl.budget * 4
+                                                            for n, p in zip(N, P)))})
     return e
 
 
@@ -641,29 +674,38 @@ def main():
     score_flops = 2.0 * wl.n_beacons * 128 * hc_per_req * sum(n + (n - p) for n, p in zip(N, P))
     update_flops = 2.0 * wl.steps * wl.group * wl.n_beacons * 128 * HC
 
+    xbytes = extra_bytes(wl, N, P, hc_per_req)
+
     def kernel_entry(n, ms_, nbytes):
         gbps = nbytes / (ms_ * 1e-3) / 1e9
         e = {"ms": round(ms_, 4), "algorithmic_bytes": int(nbytes), "gbps": round(gbps, 1),
              "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
-        tb = stored_traffic(n, wl.name)
-        if tb:
-            e["traffic_gbps"] = round(tb / (ms_ * 1e-3) / 1e9, 1)
+        if xbytes.get(n):
+            e["extra_bytes"] = int(xbytes[n])
+        sc_ = stored_counters(n, wl.name)
+        if sc_.get("bytes_per_launch"):
+            e["traffic_gbps"] = round(sc_["bytes_per_launch"] / (ms_ * 1e-3) / 1e9, 1)
+        if sc_.get("mfma_flop_per_launch"):
+            tf = sc_["mfma_flop_per_launch"] / (ms_ * 1e-3) / 1e12
+            e["mfma_tflops"] = round(tf, 1)
+            e["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+        if sc_.get("issue_share") is not None:
+            e["issue_share_per_wave"] = round(sc_["issue_share"], 3)
         return e
 
     kernels = {n: kernel_entry(n, kms[n], abytes[n]) for n in names}
-    kernels["beacon_update"]["valu_tflops"] = round(update_flops / (kms["beacon_update"] * 1e-3) / 1e12, 2)
+    # the cosine dots the maintenance chain needs (its MFMA split forms each
+    # product exactly, so it executes more MFMA flop than this; see mfma_tflops)
+    kernels["beacon_update"]["cosine_dot_flop"] = int(update_flops)
 
+    # the dominant (slowest) kernel against the HBM peak, on the roofline
+    # basis bytes of one launch (the fused kernel: keys once, beacons, moved rows)
     dom = max(names, key=lambda n: kms[n])
-    if dom == "beacon_update":
-        ach = update_flops / (kms[dom] * 1e-3) / 1e12
-        roof = {"bound": "alu", "achieved": round(ach, 2), "peak": round(VALU_FP32_PEAK_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(ach / VALU_FP32_PEAK_TFLOPS, 4)}
-    else:
-        ach = abytes[dom] / (kms[dom] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBPS, 4)}
-    roof["kernel"] = dom
-    roof["traffic"] = stored_traffic(dom, wl.name)
+    ach = abytes[dom] / (kms[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(dom, wl.name),
+            "kernel": dom, "bytes_per_launch": int(abytes[dom]), "ms_per_launch": round(kms[dom], 4),
+            "moved_rows_per_launch": int(M)}
 
     # the same pass with score, select and compact as three kernels: the
     # per-step breakdown (and what the fused kernel saves)
@@ -785,7 +827,7 @@ def main():
 
         # the pass's default: draws, selection and compaction in one kernel
         rpass, _, rM, rlist = random_passes(False, 1000)
-        rbytes = 4 * rM * 256 + HC * (stride * 4 + B * 4)
+        rbytes = 4 * rM * 256            # no key or beacon reads: the moved rows only
         sp, sk, sM, slist = random_passes(True, 1000)
         result["random_selector"] = {
             "passes_per_s": round(1000.0 / rpass, 3), "ms": round(rpass, 4),
@@ -796,8 +838,9 @@ def main():
             "separate_steps": {"passes_per_s": round(1000.0 / sp, 3), "ms": round(sp, 4),
                                "kernel_ms": sk, "moved_rows_per_pass": int(sM),
                                "same_moved_rows_as_fused": slist == rlist},
-            "note": "algorithmic bytes: the draws written, the keep lists written and the "
-                    "moved rows (K and V read and written)"}
+            "extra_bytes": int(HC * (stride * 4 + B * 4)),
+            "note": "algorithmic bytes: the moved rows (K and V read and written); the draws "
+                    "and keep lists written are the extra bytes"}
 
     # shared positions: one selection per (layer, request) for all its heads
     if not args.no_shared:

@@ -194,15 +194,35 @@ def layer_kv(wl: Workload, layer: int, table: torch.Tensor, prompt_len: torch.Te
     return kb, v
 
 
-def layer_queries(wl: Workload, layer: int, prompt_len: torch.Tensor, device="cpu"):
-    """bf16 decode queries [R, H, T, G, d] of one layer."""
+def _query_draws(wl: Workload, layer: int, device="cpu"):
+    """The random draws behind one layer's queries: noise z [R, H, T, G, d],
+    uniform u [R, H, T, G] (which kind of query) and cluster m [R, H, T, G]."""
     R, H, T, G, d, C = (wl.n_requests, wl.n_kv_heads, wl.steps, wl.group, wl.head_dim,
                         wl.n_clusters)
-    _, centres = layer_params(wl, layer, device)
     g = _gen(device, wl.seed, 23, layer)
     z = torch.randn(R, H, T, G, d, generator=g, device=device)
     u = torch.rand(R, H, T, G, generator=g, device=device)
     m = torch.randint(0, C, (R, H, T, G), generator=g, device=device)
+    return z, u, m
+
+
+def query_clusters(wl: Workload, layer: int) -> torch.Tensor:
+    """int64 [R, H, T, G]: the cluster each decode query of one layer aims at
+    (the span planted on that cluster's centre), or -1 for a plain N(0, I)
+    query.  Revisiting queries aim at cluster 0."""
+    _, u, m = _query_draws(wl, layer, "cpu")
+    is_centre = (u >= wl.p_revisit) & (u < wl.p_revisit + wl.p_centre)
+    out = torch.where(is_centre, m, torch.full_like(m, -1))
+    if wl.p_revisit > 0:
+        out = torch.where(u < wl.p_revisit, torch.zeros_like(m), out)
+    return out
+
+
+def layer_queries(wl: Workload, layer: int, prompt_len: torch.Tensor, device="cpu"):
+    """bf16 decode queries [R, H, T, G, d] of one layer."""
+    H, d = wl.n_kv_heads, wl.head_dim
+    _, centres = layer_params(wl, layer, device)
+    z, u, m = _query_draws(wl, layer, device)
     cen = centres[torch.arange(H, device=device).view(1, H, 1, 1), m]   # [R,H,T,G,d]
     is_centre = (u >= wl.p_revisit) & (u < wl.p_revisit + wl.p_centre)
     q = torch.where(is_centre.unsqueeze(-1), cen + wl.noise_std * z, z)

@@ -21,30 +21,37 @@ def test_algorithmic_bytes_by_hand():
     # T = 64 steps x G = 4 query heads, K = 128 beacons, B = 2048, 8 heads
     wl = synth.WORKLOADS["serving_r128"]
     b = bench.algorithmic_bytes(wl, [2112], [1024], moved_rows=100, hc_per_req=8)
+    x = bench.extra_bytes(wl, [2112], [1024], hc_per_req=8)
     # maintenance: 64*4 bf16 queries (65536) + beacons in and out (131072)
     # + counts in and out (1024), per head-cache
-    assert b["beacon_update"] == 8 * 197632
-    # scoring: 2112 keys (540672) + beacons (65536) + counts (512)
-    # + 132 block-table entries (528) + 1088 scores written (4352)
-    assert b["beacon_score"] == 8 * 611600
+    assert b["beacon_update"] == 8 * 197632 and x["beacon_update"] == 0
+    # scoring: 2112 keys read once (540672) + fp32 beacons (65536)
+    assert b["beacon_score"] == 8 * 606208
+    # ... and beside it counts (512) + 132 block-table entries (528) + 1088
+    # scores written (4352)
+    assert x["beacon_score"] == 8 * 5392
     # selection: 1088 scores read (4352) + 2048 keep entries (8192)
     assert b["topk_select"] == 8 * 12544
-    # compaction: 100 moved rows, K and V each read and written (102400)
-    # + the keep lists (8 x 8192)
-    assert b["kv_compact"] == 102400 + 65536
-    # the fused kernel: the scoring bytes, the keep lists written and the
-    # moved rows (its score read-back and LDS keep list are not counted)
-    assert b["beacon_evict"] == 8 * 611600 + 65536 + 102400
+    # compaction: 100 moved rows, K and V each read and written (102400);
+    # the keep lists it reads (8 x 8192) are extra
+    assert b["kv_compact"] == 102400 and x["kv_compact"] == 65536
+    # the fused kernel: keys once, beacons, moved rows (the survey's
+    # N*d*2 + K*d*4 + 4*M*d*2 per head-cache)
+    assert b["beacon_evict"] == 8 * (2112 * 128 * 2 + 128 * 128 * 4) + 4 * 100 * 128 * 2
+    assert x["beacon_evict"] == 8 * 5392 + 65536
 
 
 def test_algorithmic_bytes_scale_with_the_cache():
     wl = synth.WORKLOADS["serving_r128"]
     a = bench.algorithmic_bytes(wl, [2112], [1024], 0, 1)
     b = bench.algorithmic_bytes(wl, [2112 + 16], [1024], 0, 1)
+    xa = bench.extra_bytes(wl, [2112], [1024], 1)
+    xb = bench.extra_bytes(wl, [2112 + 16], [1024], 1)
     # maintenance does not see the cache
     assert a["beacon_update"] == b["beacon_update"]
-    # sixteen more slots: one more page, 16 keys and 16 scores
-    assert b["beacon_score"] - a["beacon_score"] == 16 * 256 + 4 + 16 * 4
+    # sixteen more slots: 16 keys; one more page and 16 more scores are extra
+    assert b["beacon_score"] - a["beacon_score"] == 16 * 256
+    assert xb["beacon_score"] - xa["beacon_score"] == 4 + 16 * 4
     assert b["topk_select"] - a["topk_select"] == 16 * 4
     # two requests cost twice one
     two = bench.algorithmic_bytes(wl, [2112, 2112], [1024, 1024], 0, 1)
@@ -142,7 +149,11 @@ def test_summary_traffic_calibration(fake_profiles):
     assert s["source_sha"] == bench.kernel_source_hash("beacon_score")
     c = t["kv_compact"]
     assert c["bytes_per_launch"] == pytest.approx(4000 * KIB * 0.8 + 2000 * KIB * 2.0)
-    assert set(t) == {"_calibration", "beacon_score", "kv_compact"}
+    assert set(t) == {"_workload", "_calibration", "beacon_score", "kv_compact"}
+    assert t["_workload"] == "fake"
+    # the MFMA and issue runs add their per-launch figures to the same entries
+    assert s["mfma_flop_per_launch"] == pytest.approx(400 * 512)
+    assert s["issue_share"] == pytest.approx(0.5) and s["wait_share"] == pytest.approx(0.2)
     md = (fake_profiles / "fake_hbm_counters.md").read_text()
     assert "read factor 0.8000, write factor 2.0000" in md
 
@@ -180,6 +191,10 @@ def test_stored_traffic_belongs_to_its_workload(tmp_path, monkeypatch):
     path.write_text(json.dumps({"_calibration": {"workload": "a"},
                                 "beacon_evict": {"bytes_per_launch": 5.0, "source_sha": "x"}}))
     assert bench.stored_traffic("beacon_evict", "a") is None      # taken on other source
+    path.write_text(json.dumps({"_workload": "a", "beacon_evict": {
+        "bytes_per_launch": 5.0, "mfma_flop_per_launch": 7.0, "source_sha": sha}}))
+    assert bench.stored_counters("beacon_evict", "a")["mfma_flop_per_launch"] == 7.0
+    assert bench.stored_counters("beacon_evict", "b") == {}
 
 
 def test_traffic_file_names():
