@@ -24,13 +24,16 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
-BKV_ABI_VERSION = 6
+BKV_ABI_VERSION = 7
 # bkv_evict_pass fuses score, select and compact (row compaction with per-head
 # selection, or shared positions for the beacon selector) when score_stride +
 # budget is at most this
 FUSED_MAX_ENTRIES = 15872
+# bytes of the scratch array bkv_evict_pass_noalloc holds on each GPU
+NOALLOC_SCRATCH_BYTES = 268435456
 BKV_OK, BKV_ERR_NULL, BKV_ERR_INVALID, BKV_ERR_BUDGET, BKV_ERR_UNSUPPORTED = 0, 1, 2, 3, 4
 BKV_ERR_WORKSPACE, BKV_ERR_HIP, BKV_ERR_LENGTH, BKV_ERR_BLOCK_TABLE = 5, 6, 7, 8
+BKV_ERR_SCRATCH = 9
 BKV_SCORE_F32, BKV_SCORE_U32 = 0, 1
 BKV_SELECT_BEACON, BKV_SELECT_RANDOM = 0, 1
 BKV_ROWS_PER_HEAD, BKV_ROWS_PER_LAYER_REQUEST, BKV_ROWS_PER_REQUEST = 0, 1, 2
@@ -97,10 +100,14 @@ _lib.bkv_workspace_size.restype = _i32
 _lib.bkv_evict_pass.argtypes = [ctypes.POINTER(bkv_cache), ctypes.POINTER(bkv_pass_args), _P, _sz,
                                 _P, _P]
 _lib.bkv_evict_pass.restype = _i32
+_lib.bkv_evict_pass_noalloc.argtypes = [ctypes.POINTER(bkv_cache), ctypes.POINTER(bkv_pass_args),
+                                        _P, _P]
+_lib.bkv_evict_pass_noalloc.restype = _i32
 
 EXPORTS = ("bkv_abi_version", "bkv_status_string", "bkv_beacon_update", "bkv_beacon_score",
            "bkv_random_score", "bkv_topk_select", "bkv_topk_select_shared", "bkv_kv_compact",
-           "bkv_page_retain", "bkv_decode_attention", "bkv_workspace_size", "bkv_evict_pass")
+           "bkv_page_retain", "bkv_decode_attention", "bkv_workspace_size", "bkv_evict_pass",
+           "bkv_evict_pass_noalloc")
 
 
 class BkvError(RuntimeError):
@@ -511,6 +518,22 @@ def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, wi
     return a
 
 
+def _timing_args(a: bkv_pass_args, timing_events, stream):
+    """Puts the HIP handles of torch timing events into the pass arguments;
+    returns the handle array, which must outlive the call."""
+    if timing_events is None:
+        return None
+    handles = []
+    for e in timing_events:
+        if e.cuda_event == 0:            # torch creates the HIP event lazily
+            e.record(stream or torch.cuda.current_stream())
+        handles.append(e.cuda_event)
+    ev_arr = (ctypes.c_void_p * len(handles))(*handles)
+    a.timing_events = ctypes.cast(ev_arr, ctypes.c_void_p)
+    a.n_timing_events = len(handles)
+    return ev_arr
+
+
 def bkv_workspace_size(cache: PagedCache, args: bkv_pass_args) -> int:
     n = _sz(0)
     c = cache.struct()
@@ -542,16 +565,7 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
     a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
                    seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride,
                    count_cap, shared_positions, page_retention, separate_steps)
-    ev_arr = None
-    if timing_events is not None:
-        handles = []
-        for e in timing_events:
-            if e.cuda_event == 0:            # torch creates the HIP event lazily
-                e.record(stream or torch.cuda.current_stream())
-            handles.append(e.cuda_event)
-        ev_arr = (ctypes.c_void_p * len(handles))(*handles)
-        a.timing_events = ctypes.cast(ev_arr, ctypes.c_void_p)
-        a.n_timing_events = len(handles)
+    ev_arr = _timing_args(a, timing_events, stream)  # noqa: F841 (kept alive for the call)
     need = bkv_workspace_size(cache, a)
     if workspace is None and need:
         workspace = _for_stream(torch.empty(need, dtype=torch.uint8, device=cache.device), stream)
@@ -566,3 +580,27 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
     if own and check:
         check_status(st, "bkv_evict_pass", stream)
     return st
+
+
+def bkv_evict_pass_noalloc(cache: PagedCache, selector, budget, *, queries=None, beacons=None,
+                           counts=None, window=64, bonus=1.0, assign=None, lse=None, seed=0,
+                           request_ids=None, pass_idx=None, pos_ids=None, scores_out=None,
+                           keep_out=None, score_stride=0, status=None, stream=None,
+                           timing_events=None, count_cap=0, shared_positions=False,
+                           page_retention=None, separate_steps=False):
+    """bkv_evict_pass for callers that cannot allocate device memory: the
+    score and keep buffers it is not given live in the library's per-GPU
+    scratch array (NOALLOC_SCRATCH_BYTES; larger passes raise BKV_ERR_SCRATCH).
+    Nothing is allocated here either: `status` (int32 [1], caller-zeroed) is
+    optional and is not checked (call check_status to see device-detected
+    errors).  Calls whose work overlaps on one GPU share the scratch and race."""
+    a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
+                   seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride,
+                   count_cap, shared_positions, page_retention, separate_steps)
+    ev_arr = _timing_args(a, timing_events, stream)  # noqa: F841 (kept alive for the call)
+    if status is not None:
+        _need(status, "status", torch.int32)
+    c = cache.struct()
+    code = _lib.bkv_evict_pass_noalloc(ctypes.byref(c), ctypes.byref(a), _ptr(status),
+                                       _stream(stream))
+    _check(code, "bkv_evict_pass_noalloc")

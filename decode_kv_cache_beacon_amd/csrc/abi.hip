@@ -1,12 +1,23 @@
 // abi.hip -- extern "C" entry points of libbeaconkv.so: synchronous argument
 // validation (nothing is enqueued on failure), then kernel launches on the
-// caller's stream.  No allocation, no global state.
+// caller's stream.  No allocation; the one piece of global state is the
+// scratch array of bkv_evict_pass_noalloc and its per-device addresses.
 
 #include <limits.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "bkv_internal.h"
 
 using namespace bkv;
+
+// Scratch of bkv_evict_pass_noalloc (the score and keep buffers a pass is not
+// given).  Each GPU the library's code is loaded on holds its own copy, at its
+// own address, until the process ends.  In host code the name below is a
+// host-side stand-in, not a device address: host code only ever uses the
+// address hipGetSymbolAddress returns for the device (scratch_address below).
+static __device__ __align__(256) uint8_t scratch[BKV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -114,6 +125,152 @@ int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     return BKV_OK;
 }
 
+// The pass after the cache, the selector and the buffer layout have been
+// checked and `ws` holds L.total bytes: validates the remaining arguments,
+// then launches on the stream (nothing is enqueued on a failed check).
+int32_t run_pass(const CacheView& v, const PassLayout& L, const bkv_pass_args* a, uint8_t* ws,
+                 int32_t* status, bkv_stream_t stream) {
+    if (status && !aligned(status, 4)) return BKV_ERR_INVALID;
+    if (a->pos_ids && (a->pos_stride < v.max_blocks * kBlock || !aligned(a->pos_ids, 4)))
+        return BKV_ERR_INVALID;
+    if ((a->scores_out && !aligned(a->scores_out, 4)) || (a->keep_out && !aligned(a->keep_out, 4)))
+        return BKV_ERR_INVALID;
+    const bool beacon = a->selector == BKV_SELECT_BEACON;
+    const int shared = a->shared_positions;
+    const bool pages = a->page_retention;
+    if (pages) {
+        if (!a->block_table_out || !a->seq_len_out || !a->freed_blocks) return BKV_ERR_NULL;
+        if (a->pos_ids || !aligned(a->block_table_out, 4) || !aligned(a->seq_len_out, 4) ||
+            !aligned(a->freed_blocks, 4))
+            return BKV_ERR_INVALID;
+    }
+    if (beacon) {
+        if (!a->queries || !a->beacons || !a->counts) return BKV_ERR_NULL;
+        if (a->n_beacons < 1 || a->n_beacons > BKV_MAX_BEACONS || a->T < 1 || a->G < 1 ||
+            a->count_cap < 0 ||
+            a->window < 0 || (int64_t)a->T * a->G > INT_MAX / kHeadDim)
+            return BKV_ERR_INVALID;
+        if (!aligned(a->queries, 16) || !aligned(a->beacons, 16) || !aligned(a->counts, 4) ||
+            (a->assign && !aligned(a->assign, 4)) || (a->lse && !aligned(a->lse, 4)))
+            return BKV_ERR_INVALID;
+    } else {
+        if (!a->request_ids || !a->pass_idx) return BKV_ERR_NULL;
+        if (!aligned(a->request_ids, 8) || !aligned(a->pass_idx, 4)) return BKV_ERR_INVALID;
+    }
+
+    void* sc = a->scores_out ? a->scores_out : ws + L.scores_off;
+    int32_t* keep = a->keep_out ? a->keep_out : reinterpret_cast<int32_t*>(ws + L.keep_off);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // every kernel applies every check, so a failing request is skipped by all steps
+    const Check all{a->budget, L.stride, 1, pages ? 1 : 0};
+    const int HC = (int)head_caches(v);
+    const int n_marks = (beacon ? 5 : 4) - (pages ? 1 : 0);
+    const bool timed = a->timing_events && a->n_timing_events >= n_marks;
+    if (timed)
+        for (int i = 0; i < n_marks; ++i)
+            if (!a->timing_events[i]) return BKV_ERR_NULL;
+    int mark_i = 0;
+    auto mark = [&]() -> hipError_t {
+        return timed ? hipEventRecord(static_cast<hipEvent_t>(a->timing_events[mark_i++]), s)
+                     : hipSuccess;
+    };
+    hipError_t he = mark();
+    if (he != hipSuccess) return BKV_ERR_HIP;
+    // row compaction: one kernel for score, select and compact when its LDS
+    // holds the candidates and keep list (per head for either selector, or
+    // shared positions for the beacon selector)
+    const bool fused = fused_pass(a, L.stride);
+    if (fused && beacon) {
+        he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
+                                  a->assign, a->count_cap, &v, all, status, s);
+        if (he == hipSuccess) he = mark();
+        if (he == hipSuccess)
+            he = (shared ? launch_beacon_evict_shared : launch_beacon_evict)(
+                v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
+                static_cast<float*>(sc), L.stride, a->lse, a->budget, a->keep_out, a->pos_ids,
+                a->pos_stride, all, status, s);
+        for (int i = 0; i < 3 && he == hipSuccess; ++i) he = mark();
+        return hip_status(he);
+    }
+    if (fused) {
+        he = launch_random_evict(v, a->seed, a->request_ids, a->pass_idx, static_cast<uint32_t*>(sc),
+                                 L.stride, a->budget, a->keep_out, a->pos_ids, a->pos_stride, all,
+                                 status, s);
+        for (int i = 0; i < 3 && he == hipSuccess; ++i) he = mark();
+        return hip_status(he);
+    }
+    if (beacon) {
+        he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
+                                  a->assign, a->count_cap, &v, all, status, s);
+        if (he == hipSuccess) he = mark();
+        if (he == hipSuccess)
+            he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
+                                     static_cast<float*>(sc), L.stride, a->lse, all, status, s);
+        if (he == hipSuccess) he = mark();
+        if (he == hipSuccess && pages)
+            he = launch_page_retain(v, sc, BKV_SCORE_F32, L.stride, BKV_ROWS_PER_HEAD, a->budget,
+                                    keep, a->block_table_out, a->seq_len_out, a->freed_blocks,
+                                    all, status, s);
+        else if (he == hipSuccess)  // shared: the largest of the H per-head scores
+            he = launch_topk_select(v, sc, BKV_SCORE_F32, L.stride, v.H, shared, a->budget, keep,
+                                    all, status, s);
+    } else {
+        he = launch_random_score(v, a->seed, a->request_ids, a->pass_idx, random_rows(a),
+                                 static_cast<uint32_t*>(sc), L.stride, all, status, s);
+        if (he == hipSuccess) he = mark();
+        if (he == hipSuccess && pages)
+            he = launch_page_retain(v, sc, BKV_SCORE_U32, L.stride, BKV_ROWS_PER_REQUEST,
+                                    a->budget, keep, a->block_table_out, a->seq_len_out,
+                                    a->freed_blocks, all, status, s);
+        else if (he == hipSuccess)  // shared: one draw row per (layer, request)
+            he = launch_topk_select(v, sc, BKV_SCORE_U32, L.stride, 1, shared, a->budget, keep,
+                                    all, status, s);
+    }
+    if (he == hipSuccess) he = mark();
+    if (he == hipSuccess && !pages) {
+        he = launch_kv_compact(v, keep, a->budget, shared, a->pos_ids, a->pos_stride, all, status,
+                               s);
+        if (he == hipSuccess) he = mark();
+    }
+    return hip_status(he);
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the GPU that runs `stream` (the null stream:
+// the current device).  It is looked up once per device, with that device
+// current, and kept; later calls read the kept address.
+int32_t scratch_address(bkv_stream_t stream, uint8_t** out) {
+    int dev = -1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (s) {
+        if (hipStreamGetDevice(s, &dev) != hipSuccess) return BKV_ERR_HIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return BKV_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return BKV_ERR_HIP;
+    uint8_t* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            int cur = -1;
+            if (hipGetDevice(&cur) != hipSuccess) return BKV_ERR_HIP;
+            if (cur != dev && hipSetDevice(dev) != hipSuccess) return BKV_ERR_HIP;
+            void* q = nullptr;
+            const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+            if (cur != dev) (void)hipSetDevice(cur);
+            if (e != hipSuccess || !q) return BKV_ERR_HIP;
+            p = static_cast<uint8_t*>(q);
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return BKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -131,6 +288,9 @@ const char* bkv_status_string(int32_t code) {
         case BKV_ERR_HIP: return "HIP launch error";
         case BKV_ERR_LENGTH: return "seq_len / prompt_len out of range";
         case BKV_ERR_BLOCK_TABLE: return "block id outside the pool";
+        case BKV_ERR_SCRATCH:
+            return "the pass needs more scratch than bkv_evict_pass_noalloc holds "
+                   "(BKV_NOALLOC_SCRATCH_BYTES); use bkv_evict_pass with a workspace";
         default: return "unknown status code";
     }
 }
@@ -295,110 +455,29 @@ int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* a, void* wor
     if (e) return e;
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return BKV_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 256)) return BKV_ERR_INVALID;
-    if (status && !aligned(status, 4)) return BKV_ERR_INVALID;
-    if (a->pos_ids && (a->pos_stride < v.max_blocks * kBlock || !aligned(a->pos_ids, 4)))
-        return BKV_ERR_INVALID;
-    if ((a->scores_out && !aligned(a->scores_out, 4)) || (a->keep_out && !aligned(a->keep_out, 4)))
-        return BKV_ERR_INVALID;
-    const bool beacon = a->selector == BKV_SELECT_BEACON;
-    const int shared = a->shared_positions;
-    const bool pages = a->page_retention;
-    if (pages) {
-        if (!a->block_table_out || !a->seq_len_out || !a->freed_blocks) return BKV_ERR_NULL;
-        if (a->pos_ids || !aligned(a->block_table_out, 4) || !aligned(a->seq_len_out, 4) ||
-            !aligned(a->freed_blocks, 4))
-            return BKV_ERR_INVALID;
-    }
-    if (beacon) {
-        if (!a->queries || !a->beacons || !a->counts) return BKV_ERR_NULL;
-        if (a->n_beacons < 1 || a->n_beacons > BKV_MAX_BEACONS || a->T < 1 || a->G < 1 ||
-            a->count_cap < 0 ||
-            a->window < 0 || (int64_t)a->T * a->G > INT_MAX / kHeadDim)
-            return BKV_ERR_INVALID;
-        if (!aligned(a->queries, 16) || !aligned(a->beacons, 16) || !aligned(a->counts, 4) ||
-            (a->assign && !aligned(a->assign, 4)) || (a->lse && !aligned(a->lse, 4)))
-            return BKV_ERR_INVALID;
-    } else {
-        if (!a->request_ids || !a->pass_idx) return BKV_ERR_NULL;
-        if (!aligned(a->request_ids, 8) || !aligned(a->pass_idx, 4)) return BKV_ERR_INVALID;
-    }
+    return run_pass(v, L, a, static_cast<uint8_t*>(workspace), status, stream);
+}
 
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    void* sc = a->scores_out ? a->scores_out : ws + L.scores_off;
-    int32_t* keep = a->keep_out ? a->keep_out : reinterpret_cast<int32_t*>(ws + L.keep_off);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    // every kernel applies every check, so a failing request is skipped by all steps
-    const Check all{a->budget, L.stride, 1, pages ? 1 : 0};
-    const int HC = (int)head_caches(v);
-    const int n_marks = (beacon ? 5 : 4) - (pages ? 1 : 0);
-    const bool timed = a->timing_events && a->n_timing_events >= n_marks;
-    if (timed)
-        for (int i = 0; i < n_marks; ++i)
-            if (!a->timing_events[i]) return BKV_ERR_NULL;
-    int mark_i = 0;
-    auto mark = [&]() -> hipError_t {
-        return timed ? hipEventRecord(static_cast<hipEvent_t>(a->timing_events[mark_i++]), s)
-                     : hipSuccess;
-    };
-    hipError_t he = mark();
-    if (he != hipSuccess) return BKV_ERR_HIP;
-    // row compaction: one kernel for score, select and compact when its LDS
-    // holds the candidates and keep list (per head for either selector, or
-    // shared positions for the beacon selector)
-    const bool fused = fused_pass(a, L.stride);
-    if (fused && beacon) {
-        he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
-                                  a->assign, a->count_cap, &v, all, status, s);
-        if (he == hipSuccess) he = mark();
-        if (he == hipSuccess)
-            he = (shared ? launch_beacon_evict_shared : launch_beacon_evict)(
-                v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
-                static_cast<float*>(sc), L.stride, a->lse, a->budget, a->keep_out, a->pos_ids,
-                a->pos_stride, all, status, s);
-        for (int i = 0; i < 3 && he == hipSuccess; ++i) he = mark();
-        return hip_status(he);
+int32_t bkv_evict_pass_noalloc(const bkv_cache* cache, const bkv_pass_args* a, int32_t* status,
+                               bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!a) return BKV_ERR_NULL;
+    if (a->selector != BKV_SELECT_BEACON && a->selector != BKV_SELECT_RANDOM)
+        return BKV_ERR_INVALID;
+    PassLayout L;
+    e = pass_layout(v, a, &L);
+    if (e) return e;
+    if (L.total > (size_t)BKV_NOALLOC_SCRATCH_BYTES) return BKV_ERR_SCRATCH;
+    uint8_t* ws = nullptr;
+    if (L.total > 0) {
+        e = scratch_address(stream, &ws);
+        if (e) return e;
     }
-    if (fused) {
-        he = launch_random_evict(v, a->seed, a->request_ids, a->pass_idx, static_cast<uint32_t*>(sc),
-                                 L.stride, a->budget, a->keep_out, a->pos_ids, a->pos_stride, all,
-                                 status, s);
-        for (int i = 0; i < 3 && he == hipSuccess; ++i) he = mark();
-        return hip_status(he);
-    }
-    if (beacon) {
-        he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
-                                  a->assign, a->count_cap, &v, all, status, s);
-        if (he == hipSuccess) he = mark();
-        if (he == hipSuccess)
-            he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
-                                     static_cast<float*>(sc), L.stride, a->lse, all, status, s);
-        if (he == hipSuccess) he = mark();
-        if (he == hipSuccess && pages)
-            he = launch_page_retain(v, sc, BKV_SCORE_F32, L.stride, BKV_ROWS_PER_HEAD, a->budget,
-                                    keep, a->block_table_out, a->seq_len_out, a->freed_blocks,
-                                    all, status, s);
-        else if (he == hipSuccess)  // shared: the largest of the H per-head scores
-            he = launch_topk_select(v, sc, BKV_SCORE_F32, L.stride, v.H, shared, a->budget, keep,
-                                    all, status, s);
-    } else {
-        he = launch_random_score(v, a->seed, a->request_ids, a->pass_idx, random_rows(a),
-                                 static_cast<uint32_t*>(sc), L.stride, all, status, s);
-        if (he == hipSuccess) he = mark();
-        if (he == hipSuccess && pages)
-            he = launch_page_retain(v, sc, BKV_SCORE_U32, L.stride, BKV_ROWS_PER_REQUEST,
-                                    a->budget, keep, a->block_table_out, a->seq_len_out,
-                                    a->freed_blocks, all, status, s);
-        else if (he == hipSuccess)  // shared: one draw row per (layer, request)
-            he = launch_topk_select(v, sc, BKV_SCORE_U32, L.stride, 1, shared, a->budget, keep,
-                                    all, status, s);
-    }
-    if (he == hipSuccess) he = mark();
-    if (he == hipSuccess && !pages) {
-        he = launch_kv_compact(v, keep, a->budget, shared, a->pos_ids, a->pos_stride, all, status,
-                               s);
-        if (he == hipSuccess) he = mark();
-    }
-    return hip_status(he);
+    // every byte a kernel of the pass reads from the scratch was written
+    // earlier in the same pass, so nothing in it needs to start at zero
+    return run_pass(v, L, a, ws, status, stream);
 }
 
 }  // extern "C"

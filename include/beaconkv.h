@@ -10,7 +10,9 @@
  * ---------------------------------------
  *  - All array pointers are DEVICE pointers owned by the caller (for example
  *    the storage of torch tensors).  The library never allocates or frees
- *    memory and keeps no global or static state; calls are reentrant.
+ *    memory.  Its one piece of global state is the scratch array of
+ *    bkv_evict_pass_noalloc (one copy per GPU); every other call is
+ *    reentrant.
  *  - Work is enqueued asynchronously on the caller's HIP stream (`stream`,
  *    a hipStream_t; NULL means the legacy default stream).  Outputs are valid
  *    once that stream has been synchronised.
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 6
+#define BKV_ABI_VERSION 7
 
 typedef void* bkv_stream_t; /* hipStream_t */
 
@@ -76,6 +78,8 @@ enum {
     BKV_ERR_HIP = 6,         /* a HIP launch failed (hipGetLastError) */
     BKV_ERR_LENGTH = 7,      /* (device) seq_len / prompt_len out of range */
     BKV_ERR_BLOCK_TABLE = 8, /* (device) a block id outside [0, num_blocks) */
+    BKV_ERR_SCRATCH = 9,     /* bkv_evict_pass_noalloc: the pass needs more than
+                                BKV_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 enum { BKV_SCORE_F32 = 0, BKV_SCORE_U32 = 1 };           /* score buffer element type */
@@ -91,6 +95,9 @@ enum { BKV_ROWS_PER_HEAD = 0, BKV_ROWS_PER_LAYER_REQUEST = 1, BKV_ROWS_PER_REQUE
  * selection and compaction (the candidate keys and keep list of a head-cache
  * then fit in the scoring kernel's LDS). */
 #define BKV_FUSED_MAX_ENTRIES 15872
+/* Bytes of the scratch array bkv_evict_pass_noalloc holds on each GPU
+ * (256 MiB). */
+#define BKV_NOALLOC_SCRATCH_BYTES 268435456
 
 /* A paged bf16 KV cache (vLLM-style pools, one K and one V pool per layer).
  * Layer pool l holds bf16 [num_blocks][n_kv_heads][block_size][head_dim];
@@ -348,6 +355,25 @@ int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, si
  * *status. */
 int32_t bkv_evict_pass(const bkv_cache* cache, const bkv_pass_args* args, void* workspace,
                        size_t workspace_bytes, int32_t* status, bkv_stream_t stream);
+
+/* bkv_evict_pass without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of bkv_evict_pass; the buffers bkv_workspace_size counts (the score and
+ * keep buffers the pass is not given) live in a scratch array of
+ * BKV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on,
+ * from the loading of its code on that GPU until the process ends.  The call
+ * allocates and frees nothing.  Returns BKV_ERR_SCRATCH, with nothing
+ * enqueued, when bkv_workspace_size exceeds BKV_NOALLOC_SCRATCH_BYTES (the
+ * 128-request, 36-layer, B = 2048 serving pass needs 160 MB).  The array's
+ * address on the stream's GPU is looked up on the first call on that GPU
+ * (BKV_ERR_HIP if that fails).  All calls on one GPU share its array, which
+ * keeps the last call's contents (nothing in it needs to start at zero): two
+ * calls whose work overlaps on one GPU -- on different streams, or enqueued
+ * from different host threads without ordering -- race, and their results
+ * are undefined. */
+int32_t bkv_evict_pass_noalloc(const bkv_cache* cache, const bkv_pass_args* args,
+                               int32_t* status, bkv_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     lib = ctypes.CDLL(bk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -33,11 +33,12 @@ def test_binding_constants_match_the_header():
     assert int(macros["BKV_ABI_VERSION"]) == bk.BKV_ABI_VERSION
     assert int(macros["BKV_FUSED_MAX_ENTRIES"]) == bk.FUSED_MAX_ENTRIES
     assert int(macros["BKV_MAX_BEACONS"]) == bk.BKV_MAX_BEACONS
+    assert int(macros["BKV_NOALLOC_SCRATCH_BYTES"]) == bk.NOALLOC_SCRATCH_BYTES
 
 
 def test_version_and_status_strings():
-    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 6
-    for code in range(0, 9):
+    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 7
+    for code in range(0, 10):
         s = bk.bkv_status_string(code)
         assert s and s != "unknown status code"
     assert bk.bkv_status_string(99) == "unknown status code"
@@ -254,6 +255,36 @@ def test_workspace_and_pass_validation():
     assert ev(ctypes.byref(c), ctypes.byref(a), FAKE, big, None, None) == bk.BKV_ERR_INVALID
     a.budget = 64
     assert ev(ctypes.byref(c), ctypes.byref(a), FAKE + 16, big, None, None) == bk.BKV_ERR_INVALID
+
+
+def test_noalloc_pass_validation():
+    """The allocation-free pass validates like bkv_evict_pass and refuses a
+    pass whose buffers exceed its scratch before any HIP call."""
+    ev = bk._lib.bkv_evict_pass_noalloc
+    a = bk.bkv_pass_args()
+    a.selector, a.budget = bk.BKV_SELECT_RANDOM, 64
+    a.request_ids = a.pass_idx = FAKE
+    assert ev(None, ctypes.byref(a), None, None) == bk.BKV_ERR_NULL
+    assert ev(ctypes.byref(_cache()), None, None, None) == bk.BKV_ERR_NULL
+    assert ev(ctypes.byref(_cache(head_dim=64)), ctypes.byref(a), None, None) == \
+        bk.BKV_ERR_UNSUPPORTED
+    a.selector = 5
+    assert ev(ctypes.byref(_cache()), ctypes.byref(a), None, None) == bk.BKV_ERR_INVALID
+    a.selector = bk.BKV_SELECT_RANDOM
+    # 64 layers x 512 requests x 8 heads x 2048 candidates x 4 B = 2 GiB > 256 MiB
+    big = _cache(n_layers=64, n_requests=512, n_kv_heads=8, max_blocks=128)
+    n = ctypes.c_size_t(0)
+    assert bk._lib.bkv_workspace_size(ctypes.byref(big), ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value > bk.NOALLOC_SCRATCH_BYTES
+    assert ev(ctypes.byref(big), ctypes.byref(a), None, None) == bk.BKV_ERR_SCRATCH
+    # given its own score and keep buffers the same pass needs no scratch; the
+    # remaining checks still run before anything is enqueued
+    a.scores_out, a.keep_out = FAKE, FAKE
+    assert bk._lib.bkv_workspace_size(ctypes.byref(big), ctypes.byref(a), ctypes.byref(n)) == 0
+    assert n.value == 0
+    a.pass_idx = None
+    assert ev(ctypes.byref(big), ctypes.byref(a), None, None) == bk.BKV_ERR_NULL
+    assert "scratch" in bk.bkv_status_string(bk.BKV_ERR_SCRATCH)
 
 
 def test_binding_rejects_host_tensors():

@@ -1,0 +1,112 @@
+"""bkv_evict_pass_noalloc (the pass for callers that cannot allocate) against
+bkv_evict_pass with a workspace: the same kernels on the same inputs, so every
+output must match byte for byte -- beacons, counts, assignments, the K/V pools,
+position ids, and with page retention the block table, lengths and released
+blocks.  Two calls in a row for every pass kind, the second on a smaller
+cache, so the second call runs over the scratch the first one left behind."""
+import numpy as np
+import pytest
+import torch
+
+from decode_kv_cache_beacon_amd import synth
+from tests.gpu_util import device_cache
+
+pytestmark = pytest.mark.gpu
+
+bk = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    global bk
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from decode_kv_cache_beacon_amd import beaconkv
+    bk = beaconkv
+    torch.cuda.init()
+    yield
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+# (layers, requests, heads, N per request, P per request): the second call is smaller
+# (the second request of the first shape keeps 22 of its 24 pages as forced
+# prompt and tail pages; the second request of the second shape fits the budget)
+SHAPES = [(2, 3, 2, [576, 541, 400], [200, 333, 100]),
+          (1, 2, 2, [560, 330], [120, 64])]
+MODES = ["beacon", "beacon_separate", "random", "random_shared", "beacon_pages"]
+
+
+class Run:
+    """One copy of a cache and its beacon state, and the outputs of one pass."""
+
+    def __init__(self, batch, N, P):
+        self.cache = device_cache(batch, N, P)
+        HC, S = self.cache.n_head_caches, self.cache.max_slots
+        self.b = batch.beacons.cuda()
+        self.c = batch.counts.cuda()
+        self.assign = torch.full((HC, batch.queries.shape[1] * batch.queries.shape[2]), -1,
+                                 dtype=torch.int32).cuda()
+        self.pos = torch.arange(S, dtype=torch.int32).repeat(HC, 1).cuda()
+        R = self.cache.n_requests
+        self.bt = self.cache.block_table.clone()
+        self.seq = self.cache.seq_len.clone()
+        self.freed = torch.full((R, self.cache.max_blocks), -5, dtype=torch.int32).cuda()
+        self.st = torch.zeros(1, dtype=torch.int32).cuda()
+
+    def outputs(self):
+        torch.cuda.synchronize()
+        out = [self.b, self.c, self.assign, self.pos, self.bt, self.seq, self.freed, self.st]
+        out += list(self.cache.k_pools) + list(self.cache.v_pools)
+        return [(t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy().copy()
+                for t in out]
+
+
+def run_pass(fn, run, mode, q, B, rid, pss, extra):
+    beacon = mode.startswith("beacon")
+    kw = dict(status=run.st, **extra)
+    if mode == "beacon_pages":
+        kw["page_retention"] = (run.bt, run.seq, run.freed)
+    else:
+        kw["pos_ids"] = run.pos
+    if beacon:
+        fn(run.cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=run.b, counts=run.c,
+           assign=run.assign, separate_steps=mode == "beacon_separate", **kw)
+    else:
+        fn(run.cache, bk.BKV_SELECT_RANDOM, B, seed=11, request_ids=rid, pass_idx=pss,
+           shared_positions=mode == "random_shared", **kw)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_noalloc_pass_matches_the_workspace_pass(mode):
+    B = 384
+    for call, (L, R, H, N, P) in enumerate(SHAPES):
+        say("noalloc", mode, "call", call, "L R H", L, R, H, "N", N, "P", P)
+        wl = synth.WORKLOADS["serving_r128"].with_(n_layers=L, n_requests=R, n_kv_heads=H,
+                                                  budget=B, prompt_len=max(P),
+                                                  seq_len=max(N), seed=100 + call)
+        batch = synth.make_batch(wl)
+        q = batch.queries.cuda()
+        rid = torch.arange(3, 3 + R, dtype=torch.int64).cuda()
+        pss = torch.full((R,), 2 + call, dtype=torch.int32).cuda()
+        ref, mine = Run(batch, N, P), Run(batch, N, P)
+        run_pass(bk.bkv_evict_pass, ref, mode, q, B, rid, pss, dict(check=False))
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_stats().get("allocation.all.allocated", 0)
+        run_pass(bk.bkv_evict_pass_noalloc, mine, mode, q, B, rid, pss, {})
+        after = torch.cuda.memory_stats().get("allocation.all.allocated", 0)
+        assert after == before, "the allocation-free pass allocated through torch"
+        r_out, m_out = ref.outputs(), mine.outputs()
+        assert int(r_out[7][0]) == 0 and int(m_out[7][0]) == 0, (r_out[7], m_out[7])
+        names = ["beacons", "counts", "assign", "pos_ids", "block_table", "seq_len", "freed",
+                 "status"] + [f"k{layer}" for layer in range(L)] + [f"v{layer}" for layer in range(L)]
+        for name, x, y in zip(names, r_out, m_out):
+            assert x.shape == y.shape and np.array_equal(x.view(np.uint8), y.view(np.uint8)), \
+                (mode, call, name)
+        if mode == "beacon_pages":
+            assert not np.array_equal(r_out[4], batch.block_table.numpy()), "no page moved"
+        else:
+            assert not np.array_equal(r_out[8].view(np.uint16), synth.bits(batch.k_pools[0])), \
+                "no row moved"
