@@ -62,14 +62,11 @@ __device__ __forceinline__ bool any_thread(bool p) {
     else return __syncthreads_or(p) != 0;
 }
 
-// Validates request r.  Every thread of the block (kWaveOnly: of the wave)
-// must call it; the result is uniform.  Errors are OR-ed into *status by
-// thread (lane) 0.
-template <bool kWaveOnly = false>
-__device__ inline bool request_ok(const CacheView& c, int layer, int r, const Check& ck,
-                                  int32_t* status) {
-    const int tid = kWaveOnly ? (int)(threadIdx.x % kWave) : (int)threadIdx.x;
-    const int nthreads = kWaveOnly ? kWave : (int)blockDim.x;
+// Checks of request r by `nthreads` cooperating threads (this one is `tid`);
+// `any` ORs a predicate over them.  Errors are OR-ed into *status by tid 0.
+template <class Any>
+__device__ inline bool request_ok_impl(const CacheView& c, int layer, int r, const Check& ck,
+                                       int32_t* status, int tid, int nthreads, Any any) {
     const int N = c.seq_len[r];
     const int P = c.prompt_len[r];
     int err = 0;
@@ -89,7 +86,7 @@ __device__ inline bool request_ok(const CacheView& c, int layer, int r, const Ch
         bool mis = false;
         for (int l = tid; l < c.L; l += nthreads)
             mis |= ((c.k_pools[l] | c.v_pools[l]) & 15u) != 0;
-        if (any_thread<kWaveOnly>(mis)) err |= 1 << BKV_ERR_INVALID;
+        if (any(mis)) err |= 1 << BKV_ERR_INVALID;
     }
     if (ck.blocks) {
         if (((c.k_pools[layer] | c.v_pools[layer]) & 15u) != 0) err |= 1 << BKV_ERR_INVALID;
@@ -100,10 +97,35 @@ __device__ inline bool request_ok(const CacheView& c, int layer, int r, const Ch
             bad |= (b < 0) || ((int64_t)b >= c.num_blocks);
         }
     }
-    bad = any_thread<kWaveOnly>(bad);
+    bad = any(bad);
     if (bad) err |= 1 << BKV_ERR_BLOCK_TABLE;
     if (err && tid == 0) raise_status(status, err);
     return err == 0;
+}
+
+// Validates request r.  Every thread of the block (kWaveOnly: of the wave)
+// must call it; the result is uniform.  Errors are OR-ed into *status by
+// thread (lane) 0.
+template <bool kWaveOnly = false>
+__device__ inline bool request_ok(const CacheView& c, int layer, int r, const Check& ck,
+                                  int32_t* status) {
+    const int tid = kWaveOnly ? (int)(threadIdx.x % kWave) : (int)threadIdx.x;
+    const int nthreads = kWaveOnly ? kWave : (int)blockDim.x;
+    return request_ok_impl(c, layer, r, ck, status, tid, nthreads,
+                           [](bool p) { return any_thread<kWaveOnly>(p); });
+}
+
+// The same for groups of G consecutive lanes of one wave (G = 32 or 64), each
+// group checking its own request r: every lane of the wave must call it, and
+// the result is uniform within each group.
+template <int G>
+__device__ inline bool request_ok_lanes(const CacheView& c, int layer, int r, const Check& ck,
+                                        int32_t* status) {
+    const int lane = (int)(threadIdx.x % kWave);
+    const unsigned long long gmask =
+        G >= kWave ? ~0ull : (((1ull << G) - 1ull) << (lane / G * G));
+    return request_ok_impl(c, layer, r, ck, status, lane % G, G,
+                           [gmask](bool p) { return (__ballot(p) & gmask) != 0ull; });
 }
 
 // Address of the bf16 row of (block, head, row-in-block) in a layer pool.

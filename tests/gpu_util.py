@@ -6,8 +6,9 @@ copies for the oracle, and implement the comparison rules:
   * float scores: |gpu - oracle| <= 1e-3 |oracle| + 1e-30;
   * beacon selection: a slot may differ from the oracle's choice only if its
     oracle score is within 1e-3 (relative) of the oracle's boundary score;
-  * beacon assignment (teacher-forced): the GPU's row must be a cosine argmax
-    to within ASSIGN_TOL, and the replayed state must match bit for bit.
+  * beacon assignment (teacher-forced): the GPU's row must be the oracle's
+    cosine argmax to within ASSIGN_TOL (fp64 rounding), and the replayed state
+    must match bit for bit.
 """
 import numpy as np
 import torch
@@ -17,16 +18,17 @@ from decode_kv_cache_beacon_amd import synth
 
 SCORE_RTOL = 1e-3
 SCORE_ATOL = 1e-30
-# Error budget of the GPU's cosine (relative to ||x|| ||b||, u = 2^-24), worst case:
-#   chunk-start dot: fp32 accumulation of 128 exact products (three bf16
-#   planes of the fp32 beacon) ..................................... ~130 u
-#   norm: fp32 sum of 128 squares + rsqrt ............................ ~35 u
-#   up to 31 running-mean advances of the dot inside a chunk, each one
-#   fp32 fma+mul plus the rounding of the real fp32 row update ...... ~155 u
-#   the same for the norm ............................................ ~155 u
-# total ~475 u = 2.8e-5 per cosine; the chosen row is then within 2 x 2.8e-5
-# of the best cosine.
-ASSIGN_TOL = 6e-5
+# Beacon assignment: the GPU picks a row whose cosine lies within a rigorous
+# bound of the best, and re-ranks every such near tie in fp64 from the actual
+# fp32 rows; the oracle ranks in fp64 too.  Each side's cosine is a sum of 128
+# exact products (bf16 x fp32 fits a double) with at most 127 roundings,
+# norms alike, then a square root and a divide: within about 3e-14 of the
+# exact cosine.  Two rows can therefore be ranked differently only when their
+# cosines lie within about 6e-14, so every pick is the oracle's argmax to
+# within 1e-12; picks with a positive gap at all (INEXACT_LIMIT) need such a
+# near tie, which the seeded inputs do not contain.
+ASSIGN_TOL = 1e-12
+INEXACT_LIMIT = 0
 # Decode attention, |gpu - oracle| <= ATT_TOL * max |v| of the head-cache: the
 # fp32 logit (128 exact bf16 products, fp32 sums) is off by at most ~128 u |q||k|
 # scale, at most ~3e-4 in log units for these inputs; a weight p = exp(s - m)

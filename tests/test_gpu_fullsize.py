@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from decode_kv_cache_beacon_amd import synth
-from tests.gpu_util import (ASSIGN_TOL, ATT_TOL, bf16_values, check_scores, check_selection,
+from tests.gpu_util import (ASSIGN_TOL, ATT_TOL, INEXACT_LIMIT, bf16_values, check_scores, check_selection,
                             keep_rows)
 
 pytestmark = pytest.mark.gpu
@@ -100,7 +100,7 @@ def _full_size_beacon_pass(wl, n_sample, sample_seed, attention):
         x = before[hc]
         say("full size head-cache", hc, "layer", layer, "request", r, "head", h)
         ob, oc, gap = oracle.beacon_update_forced(x["q"], x["b"], x["c"], a[hc].numpy())
-        assert gap.max() <= ASSIGN_TOL, hc
+        assert gap.max() <= ASSIGN_TOL and int((gap > 0).sum()) <= INEXACT_LIMIT, (hc, gap.max())
         assert np.array_equal(ob.view(np.int32), batch.beacons[hc].cpu().numpy().view(np.int32))
         assert np.array_equal(oc, batch.counts[hc].cpu().numpy())
         os_, _ = oracle.beacon_score(x["keys"], ob, oc, p, W, wl.bonus)
@@ -403,6 +403,6 @@ def test_full_size_capped_maintenance():
         say("full size capped head-cache", hc)
         q, b0, c0 = before[hc]
         ob, oc, gap = oracle.beacon_update_forced(q, b0, c0, assign[hc].cpu().numpy(), cap=cap)
-        assert gap.max() <= ASSIGN_TOL, hc
+        assert gap.max() <= ASSIGN_TOL and int((gap > 0).sum()) <= INEXACT_LIMIT, (hc, gap.max())
         assert np.array_equal(ob.view(np.int32), batch.beacons[hc].cpu().numpy().view(np.int32))
         assert np.array_equal(oc, batch.counts[hc].cpu().numpy()), hc
