@@ -220,7 +220,7 @@ COPY_SYMBOL = "__amd_rocclr_copyBuffer"
 PROFILE_CMDS = {
     "trace": ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -f csv -d <prof-dir> "
               "-o bench -- python3 <repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline "
-              "--no-side --count-cap 0"),
+              "--no-side --count-cap 0 > <trace-run-log>"),
     "pmc": ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {c} -f csv -d <pmc-dir>/{c} -o {c} -- "
             "python3 <repo>/bench.py --steps 2 --warmup 0 --no-cpu-baseline "
             "--no-shared --no-pages --no-side --count-cap 0"),
@@ -228,7 +228,7 @@ PROFILE_CMDS = {
                  "-f csv -d <pmc-dir>/MFMA -o MFMA -- python3 <repo>/bench.py --steps 2 "
                  "--warmup 0 --no-cpu-baseline --no-shared --no-pages --no-side "
                  "--count-cap 0"),
-    "summary": "python bench.py --summarize-profiles <prof-dir> <pmc-dir>",
+    "summary": "python bench.py --summarize-profiles <prof-dir> <pmc-dir> <trace-run-log>",
 }
 # instruction-issue counters, two runs (at most 8 SQ counters per run)
 SQ_COUNTERS = {
@@ -310,7 +310,7 @@ def profile_cmd(key, workload, **fmt):
     return cmd
 
 
-def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
+def summarize_profiles(prof_dir, pmc_dir, workload, out=None, bench_log=None):
     """Write the committed summaries from rocprofv3 output: per-kernel
     durations (kernel trace), HBM bytes per launch from FETCH_SIZE and
     WRITE_SIZE, each scaled by what the counter reads for the 4 GiB device
@@ -346,6 +346,28 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None):
             d = dur[k]
             lines.append(f"| {k} | {len(d)} | {statistics.mean(d):.3f} | {min(d):.3f} | "
                          f"{max(d):.3f} |")
+    # the roofline fraction of the profiled run, recomputed from the trace: the
+    # dominant kernel's algorithmic bytes per launch (the run's own line, whose
+    # moved-row count is that run's) over the trace's mean duration
+    line = None
+    if bench_log and os.path.exists(bench_log):
+        for raw in open(bench_log):
+            raw = raw.strip()
+            if raw.startswith("{") and '"roofline"' in raw:
+                line = json.loads(raw)
+    if line and line["roofline"].get("kernel") in dur:
+        rf = line["roofline"]
+        k = rf["kernel"]
+        tmean = statistics.mean(dur[k])
+        tfrac = rf["bytes_per_launch"] / (tmean * 1e-3) / 1e9 / HBM_PEAK_GBPS
+        lines += ["", "Roofline of the profiled run, from this trace:", "",
+                  f"- dominant kernel `{k}`: {rf['bytes_per_launch']:,} algorithmic bytes per launch "
+                  f"(keys read once, beacons, {rf.get('moved_rows_per_launch', 0):,} moved rows "
+                  f"read and written: the run's own moved-row count)",
+                  f"- trace mean {tmean:.4f} ms -> {rf['bytes_per_launch'] / (tmean * 1e-3) / 1e9:.1f} "
+                  f"GB/s = {tfrac:.4f} of the {HBM_PEAK_GBPS:.0f} GB/s peak",
+                  f"- the run's own line (HIP events around its timed passes): "
+                  f"{rf['ms_per_launch']:.4f} ms, frac {rf['frac']:.4f}"]
     with open(os.path.join(out, f"{workload}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -552,11 +574,15 @@ def main():
                     help="also time the maintenance kernel with this count cap (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 4 GiB device copy (for counter calibration)")
-    ap.add_argument("--summarize-profiles", nargs=2, metavar=("PROF_DIR", "PMC_DIR"),
-                    help="write profiles/ summaries from rocprofv3 output and exit")
+    ap.add_argument("--summarize-profiles", nargs="+", metavar="DIR",
+                    help="PROF_DIR PMC_DIR [TRACE_RUN_LOG]: write profiles/ summaries from "
+                         "rocprofv3 output (and the traced run's bench line) and exit")
     args = ap.parse_args()
     if args.summarize_profiles:
-        summarize_profiles(*args.summarize_profiles, args.workload)
+        sp = args.summarize_profiles
+        if len(sp) not in (2, 3):
+            ap.error("--summarize-profiles takes PROF_DIR PMC_DIR [TRACE_RUN_LOG]")
+        summarize_profiles(sp[0], sp[1], args.workload, bench_log=sp[2] if len(sp) == 3 else None)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -1027,6 +1053,15 @@ def main():
             "note": f"one layer of the 64-layer shape: {ohc} head-caches, N = 32768 "
                     f"({oP[0]} prompt), K = {owl.n_beacons}, B = {owl.budget}, "
                     f"G = {owl.group}; scoring flops count both logit passes"}
+        # the Qwen3-4B-like dense batch (36 layers, 16 requests, K = 64): one pass
+        # streams every layer's keys in layer-major order (about 5 GB, far more
+        # than the 256 MB memory-side cache), so each layer is read cold
+        q4 = synth.WORKLOADS["qwen3_4b_r16"]
+        result["qwen3_4b_r16"] = side_line(q4, *side_pass(torch, bk, synth, q4, 8, 2, dev),
+                                           "beacon")
+        result["qwen3_4b_r16"]["note"] = ("36 layers, 16 requests, 8 KV heads, G = 4, K = 64, "
+                                          "B = 2048, P = 1024, N = 2112, dense: maintenance, "
+                                          "then the fused kernel")
         # the 64-layer K = 256 batch at the three budgets, steady state N = B + 64
         c4 = {}
         for Bx in (1024, 2048, 4096):
