@@ -360,10 +360,12 @@ def summarize_profiles(prof_dir, pmc_dir, workload, out=None, bench_log=None):
         k = rf["kernel"]
         tmean = statistics.mean(dur[k])
         tfrac = rf["bytes_per_launch"] / (tmean * 1e-3) / 1e9 / HBM_PEAK_GBPS
+        what = {"beacon_update": "queries read once, beacons and counts read and written",
+                "beacon_evict": (f"keys read once, beacons, {rf.get('moved_rows_per_launch', 0):,} "
+                                 "moved rows read and written: the run's own moved-row count")}
         lines += ["", "Roofline of the profiled run, from this trace:", "",
                   f"- dominant kernel `{k}`: {rf['bytes_per_launch']:,} algorithmic bytes per launch "
-                  f"(keys read once, beacons, {rf.get('moved_rows_per_launch', 0):,} moved rows "
-                  f"read and written: the run's own moved-row count)",
+                  f"({what.get(k, 'its own inputs and outputs, each moved once')})",
                   f"- trace mean {tmean:.4f} ms -> {rf['bytes_per_launch'] / (tmean * 1e-3) / 1e9:.1f} "
                   f"GB/s = {tfrac:.4f} of the {HBM_PEAK_GBPS:.0f} GB/s peak",
                   f"- the run's own line (HIP events around its timed passes): "
