@@ -32,8 +32,11 @@ int32_t check_cache(const bkv_cache* cache, CacheView* v) {
     if (cache->n_layers < 1 || cache->n_requests < 1 || cache->n_kv_heads < 1 ||
         cache->max_blocks < 1 || cache->num_blocks < 1)
         return BKV_ERR_INVALID;
-    const int64_t hc = (int64_t)cache->n_layers * cache->n_requests * cache->n_kv_heads;
-    if (hc > INT_MAX || (int64_t)cache->max_blocks * kBlock > kMaxSlots ||
+    // L * R fits int64 for any int32 operands; it is bounded before the third
+    // factor so that L * R * H cannot overflow either
+    const int64_t lr = (int64_t)cache->n_layers * cache->n_requests;
+    if (lr > INT_MAX || lr * cache->n_kv_heads > INT_MAX ||
+        (int64_t)cache->max_blocks * kBlock > kMaxSlots ||
         cache->num_blocks > INT_MAX)
         return BKV_ERR_INVALID;
     if (!aligned(cache->k_pools, 8) || !aligned(cache->v_pools, 8) ||

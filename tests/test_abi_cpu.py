@@ -111,6 +111,11 @@ def test_cache_validation():
     assert _score(_cache(num_blocks=0)) == bk.BKV_ERR_INVALID
     assert _score(_cache(seq_len=FAKE + 2)) == bk.BKV_ERR_INVALID
     assert _score(_cache(n_layers=2**16, n_requests=2**12, n_kv_heads=8)) == bk.BKV_ERR_INVALID
+    # a head-cache count whose product overflows 64 bits is refused, not wrapped
+    m = 2**31 - 1
+    assert _score(_cache(n_layers=m, n_requests=m, n_kv_heads=m)) == bk.BKV_ERR_INVALID
+    assert _score(_cache(n_layers=2**21, n_requests=2**21, n_kv_heads=2**21)) == \
+        bk.BKV_ERR_INVALID
     assert bk._lib.bkv_beacon_score(None, FAKE, FAKE, 8, 64, 1.0, FAKE, 16, None, None,
                                     None) == bk.BKV_ERR_NULL
 
