@@ -253,11 +253,15 @@ def _near_tie_rows(b, c, rng):
 @pytest.mark.parametrize("case,K,G,T,cap", [
     ("near_ties", 64, 4, 64, 0), ("near_ties", 128, 4, 64, 0), ("near_ties", 256, 8, 32, 0),
     ("near_ties", 40, 2, 33, 3), ("zero_queries", 64, 4, 16, 0), ("opposed", 5, 4, 16, 0),
-    ("opposed", 128, 2, 32, 0), ("cap_one", 64, 4, 16, 1)])
+    ("opposed", 128, 2, 32, 0), ("cap_one", 64, 4, 16, 1), ("extreme_norms", 128, 4, 64, 0),
+    ("extreme_norms", 256, 2, 48, 0), ("garbage_unfilled", 64, 4, 32, 0),
+    ("garbage_unfilled", 128, 2, 48, 2)])
 def test_beacon_update_teacher_forced_adversarial(case, K, G, T, cap):
-    """Near ties, exact ties, zero queries and queries opposed to every beacon
+    """Near ties, exact ties, zero queries, queries opposed to every beacon
     (all cosines negative, where the chain's error bound does not hold and its
-    rows are re-ranked exactly): every pick must still be the oracle's argmax."""
+    rows are re-ranked exactly), row and query norms far outside the bound's
+    range (2^+-35 and beyond), and never-filled rows holding NaN and infinity:
+    every pick must still be the oracle's argmax."""
     say("update adversarial", case, K, G, T, "cap", cap)
     wl = small(n_layers=1, n_requests=2, n_kv_heads=2, n_beacons=K, group=G, steps=T,
                prewarm=True, budget=512, prompt_len=200, seq_len=576)
@@ -276,6 +280,21 @@ def test_beacon_update_teacher_forced_adversarial(case, K, G, T, cap):
     elif case in ("opposed", "cap_one"):
         # every query points away from the mean of the beacons
         qv = -b.mean(1, keepdim=True)[:, :, None, :].expand_as(qv) * 3 + 0.1 * qv
+    elif case == "extreme_norms":
+        # rows and queries scaled far above and below the covered norm range
+        b[:, 0::3] *= 2.0 ** 35
+        b[:, 1::5] *= 2.0 ** -40
+        flat = qv.reshape(qv.shape[0], -1, 128)
+        flat[:, 0::4] *= 2.0 ** 36
+        flat[:, 1::7] *= 2.0 ** -38
+        qv = flat.reshape(qv.shape)
+    elif case == "garbage_unfilled":
+        # never-filled rows whose stored values are NaN and infinity: the fill
+        # replaces them, and nothing may read them before
+        dead = torch.from_numpy(rng.choice(K, size=K // 6, replace=False))
+        c[:, dead] = 0
+        b[:, dead] = float("nan")
+        b[:, dead[::2], ::3] = float("inf")
     q = qv.to(torch.bfloat16)
     HC = q.shape[0]
     qd, bd, cd = q.cuda(), b.cuda(), c.cuda()
