@@ -247,7 +247,10 @@ __device__ __forceinline__ bool score_head(
     int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
     Check ck, int32_t* status, const int hc) {
     constexpr int kGroups = NG, kQ = NQ, kWaves = NG * NQ;
-    constexpr int kRingTiles = kQ * kRingIters;
+    // the streaming ring; the fused kernels reuse it for the selection, which
+    // needs 64 KiB, so a one-phase layout allocates more than it streams
+    constexpr int kRingTiles =
+        (kMode != kScoreOnly && kQ * kRingIters < 8) ? 8 : kQ * kRingIters;
     static_assert(kMode == kScoreOnly ||
                       kRingTiles * kTileBytes >= kFuseKeyOff + 4 * kFusedMaxEntries,
                   "the ring cannot hold the fused selection");
@@ -715,7 +718,15 @@ void launch_cfg(const CacheView& c, const float* beacons, const int32_t* counts,
 //   K <= 64 : 2 groups x 2 phases, 32 rows per wave (4 waves per workgroup)
 //   K <= 128: 2 groups x 2 phases, 64 rows per wave; every tile is read
 //             from LDS by two waves (four 32-row waves took 5% longer)
-//   K <= 256: 4 groups x 2 phases, 64 rows per wave
+//   K <= 256: 8 groups x 1 phase, 32 rows per wave (8 waves of 112
+//             registers: two workgroups per CU, where 4 groups x 2 phases of
+//             64-row waves, with 199 registers, allowed one; 8.25 against
+//             9.07 ms for the 64-layer B = 2048 fused pass).  Every tile is
+//             read from LDS by all 8 waves.  With shared positions the
+//             kernel's extra state does not fit 128 registers, so it runs
+//             the same layout (the layout fixes the summation order, and the
+//             fused kernels must reproduce the separate ones) with more
+//             registers, one workgroup per CU.
 template <int kMode>
 hipError_t launch_any(const CacheView& c, const float* beacons, const int32_t* counts, int K,
                       int window, float bonus, float* scores, int stride, float* lse, int B,
@@ -726,13 +737,24 @@ hipError_t launch_any(const CacheView& c, const float* beacons, const int32_t* c
     // K <= 128, four tile phases instead of two keep twice the key tiles in
     // flight in the CU's one workgroup (the ring takes 128 KiB; one workgroup
     // per CU fits).  The fused kernel of one 4096-key head-cache at K = 64
-    // took 100 us instead of 146.  At K = 256 the wider layout was no faster.
+    // took 100 us instead of 146.  At K = 256 the 4 x 2 layout of 64-row
+    // waves serves such launches (1.44 against 2.00 ms for the 32k layer's
+    // scoring: the one-phase layout reads every tile 8 times and gains
+    // nothing without a second workgroup on the CU).  The layout fixes the
+    // order of the log-sum-exp sums, so it is chosen from the head-cache
+    // count for every kernel, the shared-position ones included: a fused pass
+    // then reproduces its separate kernels bit for bit.
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 0;
-    const long units = kMode == kEvictShared ? (long)c.L * c.R : (long)c.L * c.R * c.H;
-    if (units <= cus && K <= 128) {
+    const long units = (long)c.L * c.R * c.H;
+    if (units <= cus && K > 128) {
+        launch_cfg<4, 2, 2, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
+                                      keep_out, pos_ids, pos_stride, ck, status, s);
+        return hipGetLastError();
+    }
+    if (units <= cus) {
         if (K <= 64)
             launch_cfg<2, 4, 1, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse,
                                           B, keep_out, pos_ids, pos_stride, ck, status, s);
@@ -747,8 +769,11 @@ hipError_t launch_any(const CacheView& c, const float* beacons, const int32_t* c
     else if (K <= 128)
         launch_cfg<2, 2, 2, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
                                       keep_out, pos_ids, pos_stride, ck, status, s);
+    else if (kMode == kEvictShared)  // the same layout (hence the same scores), more registers
+        launch_cfg<8, 1, 1, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
+                                      keep_out, pos_ids, pos_stride, ck, status, s);
     else
-        launch_cfg<4, 2, 2, 2, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
+        launch_cfg<8, 1, 1, 4, kMode>(c, beacons, counts, K, window, bonus, scores, stride, lse, B,
                                       keep_out, pos_ids, pos_stride, ck, status, s);
     return hipGetLastError();
 }
