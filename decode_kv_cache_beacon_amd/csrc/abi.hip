@@ -5,6 +5,7 @@
 
 #include <limits.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -64,7 +65,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct PassLayout {
     int stride;
-    size_t scores_off, keep_off, total;
+    int parts;  // beacon scoring: workgroups per head-cache (1: unsplit)
+    size_t scores_off, keep_off, part_off, total;
 };
 
 // Row layout of the random selector's draws in a pass: per head-cache, per
@@ -104,6 +106,20 @@ bool fused_pass(const bkv_pass_args* a, int stride) {
            (int64_t)stride + a->budget <= kFusedMaxEntries;
 }
 
+// Workgroups per head-cache of a pass's beacon scoring.  A pass that no fused
+// kernel can run (more candidates and keep entries than its LDS holds) and
+// that has no more head-caches than the GPU has CUs (256) splits each
+// head-cache's keys over up to eight workgroups (about 1024 in all).  Every
+// pass a fused kernel could run scores unsplit, so that its separate steps
+// reproduce it bit for bit.
+int score_parts(const CacheView& v, const bkv_pass_args* a, int stride) {
+    if (a->selector != BKV_SELECT_BEACON) return 1;
+    if ((int64_t)stride + a->budget <= kFusedMaxEntries) return 1;
+    const int64_t hc = head_caches(v);
+    if (hc == 0 || hc > 256) return 1;
+    return (int)std::min<int64_t>(8, std::max<int64_t>(1, 1024 / hc));
+}
+
 int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     const int max_slots = v.max_blocks * kBlock;
     const int stride = a->score_stride > 0 ? a->score_stride : max_slots;
@@ -115,7 +131,8 @@ int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
         return BKV_ERR_INVALID;
     size_t off = 0;
     L->stride = stride;
-    L->scores_off = L->keep_off = 0;
+    L->parts = score_parts(v, a, stride);
+    L->scores_off = L->keep_off = L->part_off = 0;
     if (!a->scores_out) {
         L->scores_off = off;
         off = round_up(off + score_rows(v, a) * (size_t)stride * 4, 256);
@@ -123,6 +140,10 @@ int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     if (!a->keep_out && !fused_pass(a, stride)) {
         L->keep_off = off;
         off = round_up(off + keep_rows(v, a) * keep_cols(a) * 4, 256);
+    }
+    if (L->parts > 1) {  // the parts' log-sum-exps
+        L->part_off = off;
+        off = round_up(off + (size_t)head_caches(v) * L->parts * BKV_MAX_BEACONS * 4, 256);
     }
     L->total = off;
     return BKV_OK;
@@ -206,7 +227,12 @@ int32_t run_pass(const CacheView& v, const PassLayout& L, const bkv_pass_args* a
         he = launch_beacon_update(HC, a->T, a->G, a->n_beacons, a->queries, a->beacons, a->counts,
                                   a->assign, a->count_cap, &v, all, status, s);
         if (he == hipSuccess) he = mark();
-        if (he == hipSuccess)
+        if (he == hipSuccess && L.parts > 1)
+            he = launch_beacon_score_split(v, a->beacons, a->counts, a->n_beacons, a->window,
+                                           a->bonus, static_cast<float*>(sc), L.stride, a->lse,
+                                           reinterpret_cast<float*>(ws + L.part_off), L.parts,
+                                           all, status, s);
+        else if (he == hipSuccess)
             he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
                                      static_cast<float*>(sc), L.stride, a->lse, all, status, s);
         if (he == hipSuccess) he = mark();

@@ -234,7 +234,13 @@ __device__ void select_compact(const CacheView& c, int layer, int head0, int n, 
 // What the score body does after scoring: nothing, the per-head selection
 // and compaction, or (shared positions) the selection and compaction of the
 // (layer, request) once its last head is scored.
-enum { kScoreOnly = 0, kEvictHead = 1, kEvictShared = 2 };
+// kSplitLse / kSplitScore: a head-cache's keys split over `nparts` workgroups
+// in two launches -- each part reduces its share of the key tiles to a
+// log-sum-exp per row (kSplitLse, written to part_lse), then each part merges
+// the partials and scores its share of the candidate tiles (kSplitScore).
+enum { kScoreOnly = 0, kEvictHead = 1, kEvictShared = 2, kSplitLse = 3, kSplitScore = 4 };
+// row stride of the per-part log-sum-exp partials (log2 units)
+constexpr int kPartRow = BKV_MAX_BEACONS;
 
 // The body of the kernels below, for head-cache hc: NG row groups of NQ waves
 // (NQ tile phases), MBW 32-row blocks per wave; kMode as above (budget B,
@@ -245,13 +251,15 @@ __device__ __forceinline__ bool score_head(
     CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
     int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
     int B, int32_t* __restrict__ keep_out, int32_t* __restrict__ pos_ids, int pos_stride,
-    Check ck, int32_t* status, const int hc) {
+    Check ck, int32_t* status, const int hc, const int part = 0, const int nparts = 1,
+    float* __restrict__ part_lse = nullptr) {
     constexpr int kGroups = NG, kQ = NQ, kWaves = NG * NQ;
+    constexpr bool kScoreLike = kMode == kScoreOnly || kMode == kSplitLse || kMode == kSplitScore;
     // the streaming ring; the fused kernels reuse it for the selection, which
     // needs 64 KiB, so a one-phase layout allocates more than it streams
     constexpr int kRingTiles =
-        (kMode != kScoreOnly && kQ * kRingIters < 8) ? 8 : kQ * kRingIters;
-    static_assert(kMode == kScoreOnly ||
+        (!kScoreLike && kQ * kRingIters < 8) ? 8 : kQ * kRingIters;
+    static_assert(kScoreLike ||
                       kRingTiles * kTileBytes >= kFuseKeyOff + 4 * kFusedMaxEntries,
                   "the ring cannot hold the fused selection");
     static_assert(kWaves <= 16, "fused scan slots");
@@ -293,12 +301,17 @@ __device__ __forceinline__ bool score_head(
 
     // the keep-list row: per head-cache, or per (layer, request) when shared
     int32_t* keep_row = nullptr;
-    if (kMode != kScoreOnly && keep_out)
+    if (!kScoreLike && keep_out)
         keep_row = keep_out + (size_t)(kMode == kEvictShared ? hc / c.H : hc) * B;
     const bool last_head = x.head == c.H - 1;
     if (N == 0) {  // empty cache: nothing to score, every live lse is log(0)
+        if constexpr (kMode == kSplitLse) {
+            for (int j = tid; j < K; j += blockDim.x)
+                part_lse[((size_t)hc * nparts + part) * kPartRow + j] = -INFINITY;
+            return true;
+        }
         for (int j = tid; j < K; j += blockDim.x)
-            if (lse_out)
+            if (lse_out && part == 0)
                 lse_out[(size_t)hc * K + j] = s_live[j] ? -INFINITY : __int_as_float(0x7fc00000);
         if (kMode == kEvictHead || (kMode == kEvictShared && last_head))
             for (int i = tid; i < B; i += blockDim.x)
@@ -306,18 +319,40 @@ __device__ __forceinline__ bool score_head(
         return true;
     }
 
-    const uint64_t kpool = c.k_pools[x.layer];
+    // a scalar load: a vector one would still count as outstanding inside the
+    // ring loop below and make the loaders wait for their ring loads there
+    const uint64_t kpool =
+        *(const __attribute__((address_space(4))) uint64_t*)(c.k_pools + x.layer);
     const int ntiles = (N + kTileKeys - 1) / kTileKeys;
-    const int iters = (ntiles + kQ - 1) / kQ;  // phase-1 iterations (all keys)
     // Phase 2 scores only the candidates [P, N): its tiles start at the one
     // holding slot P.
     const int t2 = P / kTileKeys;
     const int ntiles2 = ntiles - t2;
-    const int iters2 = (ntiles2 + kQ - 1) / kQ;
-    const int G = iters + iters2;               // the stream: phase 1, then phase 2
+    // this workgroup's tiles: phase 1 over [p1a, p1a + p1n), phase 2 over
+    // [p2a, p2a + p2n) (a split part takes its share of one of them)
+    int p1a = 0, p1n = ntiles, p2a = t2, p2n = ntiles2;
+    if constexpr (kMode == kSplitLse) {
+        p1a = ntiles * part / nparts;
+        p1n = ntiles * (part + 1) / nparts - p1a;
+        p2n = 0;
+    }
+    if constexpr (kMode == kSplitScore) {
+        const int a = ntiles2 * part / nparts;
+        p1n = 0;
+        p2a = t2 + a;
+        p2n = ntiles2 * (part + 1) / nparts - a;
+    }
+    if (kMode == kSplitLse && p1n == 0) {  // no keys in this part: log(0)
+        for (int j = tid; j < K; j += blockDim.x)
+            part_lse[((size_t)hc * nparts + part) * kPartRow + j] = -INFINITY;
+        return true;
+    }
+    const int iters = (p1n + kQ - 1) / kQ;   // phase-1 iterations
+    const int iters2 = (p2n + kQ - 1) / kQ;  // phase-2 iterations
+    const int G = iters + iters2;            // the stream: phase 1, then phase 2
     // last iteration of a phase in which this wave's phase q has a tile (-1 if none)
-    const int jlast = (q < ntiles) ? (ntiles - 1 - q) / kQ : -1;
-    const int jlast2 = (q < ntiles2) ? (ntiles2 - 1 - q) / kQ : -1;
+    const int jlast = (q < p1n) ? (p1n - 1 - q) / kQ : -1;
+    const int jlast2 = (q < p2n) ? (p2n - 1 - q) / kQ : -1;
 
     // DMA of key tile t into ring slot `slot` (issued by a group-1 wave).  Lane
     // l of instruction i fills LDS bytes [1024 i + 16 l, +16) of the slot: row
@@ -348,7 +383,7 @@ __device__ __forceinline__ bool score_head(
     // one tile per iteration, so a wave's outstanding loads are always whole
     // iterations.
     auto slot_of = [&](int g) { return (g % kRingIters) * kQ + q; };
-    auto tile_of = [&](int g) { return g < iters ? kQ * g + q : t2 + kQ * (g - iters) + q; };
+    auto tile_of = [&](int g) { return g < iters ? p1a + kQ * g + q : p2a + kQ * (g - iters) + q; };
     // this lane's key column from a ring slot: the B fragment of k-step s is
     // global chunk 2s + hh of row `col`
     auto read_tile = [&](Tile& t, int slot) {
@@ -369,14 +404,20 @@ __device__ __forceinline__ bool score_head(
     };
 
     // A fragments: beacon row 32*(mb0+m) + col, bf16 (RNE) of the fp32 state.
-    // Dead rows load row 0 (present whenever the block is) and are zeroed.
-    // The loads of the first blocks (both of two, one of four) go out before
-    // the first ring tiles, so that waiting for them does not also wait for
-    // the tiles.
+    // Dead rows, and the rows of blocks past K, load row 0 (always present)
+    // and are zeroed.  The loads of the first blocks (both of two, one of four)
+    // go out before the first ring tiles and are converted on every path: the
+    // compiler, which does not see the ring loads, would otherwise count them
+    // as outstanding inside the ring loop and make the loaders wait there for
+    // their own ring loads.
     bf16x8_t A[MBW][8];
+    auto row_live = [&](int m) {
+        const int j = 32 * (mb0 + m) + col;
+        return mb0 + m < MB && s_live[j < BKV_MAX_BEACONS ? j : 0];
+    };
     auto load_block = [&](int m, float4 (&r)[8][2]) {
         const int j = 32 * (mb0 + m) + col;
-        const float* br = beacons + ((size_t)hc * K + (s_live[j] ? j : 0)) * kHeadDim + 8 * hh;
+        const float* br = beacons + ((size_t)hc * K + (row_live(m) ? j : 0)) * kHeadDim + 8 * hh;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             r[s][0] = *reinterpret_cast<const float4*>(br + 16 * s);
@@ -384,7 +425,7 @@ __device__ __forceinline__ bool score_head(
         }
     };
     auto convert_block = [&](int m, const float4 (&r)[8][2]) {
-        const uint32_t keep = s_live[32 * (mb0 + m) + col] ? 0xffffffffu : 0u;
+        const uint32_t keep = row_live(m) ? 0xffffffffu : 0u;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const float4 lo = r[s][0], hi = r[s][1];
@@ -399,20 +440,17 @@ __device__ __forceinline__ bool score_head(
     constexpr int kPre = MBW <= 2 ? MBW : 1;
     float4 raw[kPre][8][2];
 #pragma unroll
-    for (int m = 0; m < kPre; ++m)
-        if (mb0 + m < MB) load_block(m, raw[m]);
+    for (int m = 0; m < kPre; ++m) load_block(m, raw[m]);
     if (loader)  // the first ring tiles are in flight while the beacons are prepared
         for (int g = 0; g < kDepth && g < G; ++g) issue_tile(tile_of(g), slot_of(g));
 #pragma unroll
     for (int m = 0; m < MBW; ++m) {
-        if (mb0 + m < MB) {
-            if (m < kPre) {
-                convert_block(m, raw[m < kPre ? m : 0]);
-            } else {
-                float4 r[8][2];
-                load_block(m, r);
-                convert_block(m, r);
-            }
+        if (m < kPre) {
+            convert_block(m, raw[m < kPre ? m : 0]);
+        } else if (mb0 + m < MB) {
+            float4 r[8][2];
+            load_block(m, r);
+            convert_block(m, r);
         } else {
 #pragma unroll
             for (int s = 0; s < 8; ++s) A[m][s] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
@@ -442,7 +480,7 @@ __device__ __forceinline__ bool score_head(
     for (int it = 0; it < iters; ++it) {
         begin_iter(it);  // stream iteration g = it
         if (!computes || it > jlast) continue;
-        const int tt = kQ * it + q;
+        const int tt = p1a + kQ * it + q;
         const int n = kTileKeys * tt + col;
         Tile t;
         read_tile(t, slot_of(it));
@@ -477,116 +515,137 @@ __device__ __forceinline__ bool score_head(
             }
         }
     }
-    // lanes -> waves -> rows.  The first phase-2 tiles are in flight, so the
-    // exchange uses ring barriers (LDS only) rather than fenced ones.
-#pragma unroll
-    for (int m = 0; m < MBW; ++m) {
-        if (mb0 + m >= MB) continue;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float v = half_sum(sum[m][i]);
-            if (col == kHalfLead) s_part[w][32 * m + acc_row(i, hh)] = v;
-        }
-    }
-    if (lane == 0) s_M[w] = (jlast >= 0 && computes) ? Mw : -INFINITY;
-    ring_barrier();
-    // row j belongs to group g = (j / 32) / MBW, at local row lj of its waves
-    for (int j = tid; j < Kp; j += blockDim.x) {
-        const int g = (j / 32) / MBW;
-        const int lj = j - 32 * MBW * g;
-        float Mg = -INFINITY;
-        for (int k2 = 0; k2 < kQ; ++k2) Mg = fmaxf(Mg, s_M[g * kQ + k2]);
-        float total = 0.f;
-        for (int k2 = 0; k2 < kQ; ++k2) {
-            const float Mk = s_M[g * kQ + k2];
-            if (Mk != -INFINITY) total += s_part[g * kQ + k2][lj] * exp2f(Mk - Mg);
-        }
-        const bool lv = s_live[j];
-        const bool ok = total >= 0x1p-100f && total < INFINITY;
-        if (lv && !ok) s_rescue = 1;
-        s_lse2[j] = lv ? Mg + log2f(total) : INFINITY;
-    }
-    ring_barrier();
-
-    if (s_rescue) {
-        // Exact fallback with direct loads: per-row maximum over all keys
-        // first, then the sums against it (every term <= 1, the maximum == 1).
-#pragma unroll
-        for (int m = 0; m < MBW; ++m)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sum[m][i] = -INFINITY;
-        if (computes) {
-            for (int tt = q; tt < ntiles; tt += kQ) {
-                Tile t;
-                const int n = kTileKeys * tt + col;
-                load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
-#pragma unroll
-                for (int m = 0; m < MBW; ++m) {
-                    if (mb0 + m >= MB) continue;
-                    const f32x16_t acc = logits(A[m], t, zero);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (n < N) sum[m][i] = fmaxf(sum[m][i], acc[i]);
-                }
+    if constexpr (kMode == kSplitScore) {
+        // the parts' log-sum-exps, merged: lse = m + log2(sum 2^(lse_s - m))
+        const float* pl = part_lse + (size_t)hc * nparts * kPartRow;
+        for (int j = tid; j < Kp; j += blockDim.x) {
+            float m = -INFINITY, total = 0.f;
+            if (j < K) {
+                for (int p2 = 0; p2 < nparts; ++p2) m = fmaxf(m, pl[p2 * kPartRow + j]);
+                if (m != -INFINITY)
+                    for (int p2 = 0; p2 < nparts; ++p2) total += exp2f(pl[p2 * kPartRow + j] - m);
             }
+            s_lse2[j] = s_live[j] ? (m == -INFINITY ? -INFINITY : m + log2f(total)) : INFINITY;
         }
-#pragma unroll
+        ring_barrier();
+    } else {
+        // lanes -> waves -> rows.  The first phase-2 tiles are in flight, so the
+        // exchange uses ring barriers (LDS only) rather than fenced ones.
+    #pragma unroll
         for (int m = 0; m < MBW; ++m) {
             if (mb0 + m >= MB) continue;
-#pragma unroll
+    #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float v = half_max(sum[m][i]);
+                const float v = half_sum(sum[m][i]);
                 if (col == kHalfLead) s_part[w][32 * m + acc_row(i, hh)] = v;
             }
         }
-        __syncthreads();
+        if (lane == 0) s_M[w] = (jlast >= 0 && computes) ? Mw : -INFINITY;
+        ring_barrier();
+        // row j belongs to group g = (j / 32) / MBW, at local row lj of its waves
         for (int j = tid; j < Kp; j += blockDim.x) {
             const int g = (j / 32) / MBW;
             const int lj = j - 32 * MBW * g;
-            float R = -INFINITY;
-            for (int k2 = 0; k2 < kQ; ++k2) R = fmaxf(R, s_part[g * kQ + k2][lj]);
-            s_ref[j] = R * kCs;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int m = 0; m < MBW; ++m) {
-            if (mb0 + m >= MB) continue;
-            float ref[16], acc_sum[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                ref[i] = s_ref[32 * (mb0 + m) + acc_row(i, hh)];
-                acc_sum[i] = 0.f;
-            }
-            for (int tt = q; tt < ntiles; tt += kQ) {
-                Tile t;
-                const int n = kTileKeys * tt + col;
-                load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
-                const f32x16_t acc = logits(A[m], t, zero);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -ref[i]));
-                    acc_sum[i] += (n < N) ? e : 0.f;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float v = half_sum(acc_sum[i]);
-                if (col == kHalfLead) s_part[w][32 * m + acc_row(i, hh)] = v;
-            }
-        }
-        __syncthreads();
-        for (int j = tid; j < Kp; j += blockDim.x) {
-            const int g = (j / 32) / MBW;
-            const int lj = j - 32 * MBW * g;
+            float Mg = -INFINITY;
+            for (int k2 = 0; k2 < kQ; ++k2) Mg = fmaxf(Mg, s_M[g * kQ + k2]);
             float total = 0.f;
-            for (int k2 = 0; k2 < kQ; ++k2) total += s_part[g * kQ + k2][lj];
-            s_lse2[j] = s_live[j] ? s_ref[j] + log2f(total) : INFINITY;
+            for (int k2 = 0; k2 < kQ; ++k2) {
+                const float Mk = s_M[g * kQ + k2];
+                if (Mk != -INFINITY) total += s_part[g * kQ + k2][lj] * exp2f(Mk - Mg);
+            }
+            const bool lv = s_live[j];
+            const bool ok = total >= 0x1p-100f && total < INFINITY;
+            if (lv && !ok) s_rescue = 1;
+            s_lse2[j] = lv ? Mg + log2f(total) : INFINITY;
         }
-        __syncthreads();
-    }
+        ring_barrier();
 
+        if (s_rescue) {
+            // Exact fallback with direct loads: per-row maximum over all keys
+            // first, then the sums against it (every term <= 1, the maximum == 1).
+    #pragma unroll
+            for (int m = 0; m < MBW; ++m)
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) sum[m][i] = -INFINITY;
+            if (computes) {
+                for (int tt = p1a + q; tt < p1a + p1n; tt += kQ) {
+                    Tile t;
+                    const int n = kTileKeys * tt + col;
+                    load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
+    #pragma unroll
+                    for (int m = 0; m < MBW; ++m) {
+                        if (mb0 + m >= MB) continue;
+                        const f32x16_t acc = logits(A[m], t, zero);
+    #pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            if (n < N) sum[m][i] = fmaxf(sum[m][i], acc[i]);
+                    }
+                }
+            }
+    #pragma unroll
+            for (int m = 0; m < MBW; ++m) {
+                if (mb0 + m >= MB) continue;
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float v = half_max(sum[m][i]);
+                    if (col == kHalfLead) s_part[w][32 * m + acc_row(i, hh)] = v;
+                }
+            }
+            __syncthreads();
+            for (int j = tid; j < Kp; j += blockDim.x) {
+                const int g = (j / 32) / MBW;
+                const int lj = j - 32 * MBW * g;
+                float R = -INFINITY;
+                for (int k2 = 0; k2 < kQ; ++k2) R = fmaxf(R, s_part[g * kQ + k2][lj]);
+                s_ref[j] = R * kCs;
+            }
+            __syncthreads();
+    #pragma unroll
+            for (int m = 0; m < MBW; ++m) {
+                if (mb0 + m >= MB) continue;
+                float ref[16], acc_sum[16];
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    ref[i] = s_ref[32 * (mb0 + m) + acc_row(i, hh)];
+                    acc_sum[i] = 0.f;
+                }
+                for (int tt = p1a + q; tt < p1a + p1n; tt += kQ) {
+                    Tile t;
+                    const int n = kTileKeys * tt + col;
+                    load_key(t, kpool, s_bt, c.H, x.head, n, N, hh);
+                    const f32x16_t acc = logits(A[m], t, zero);
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], kCs, -ref[i]));
+                        acc_sum[i] += (n < N) ? e : 0.f;
+                    }
+                }
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float v = half_sum(acc_sum[i]);
+                    if (col == kHalfLead) s_part[w][32 * m + acc_row(i, hh)] = v;
+                }
+            }
+            __syncthreads();
+            for (int j = tid; j < Kp; j += blockDim.x) {
+                const int g = (j / 32) / MBW;
+                const int lj = j - 32 * MBW * g;
+                float total = 0.f;
+                for (int k2 = 0; k2 < kQ; ++k2) total += s_part[g * kQ + k2][lj];
+                s_lse2[j] = s_live[j] ? s_ref[j] + log2f(total) : INFINITY;
+            }
+            __syncthreads();
+        }
+    }
+    if constexpr (kMode == kSplitLse) {
+        for (int j = tid; j < K; j += blockDim.x)
+            part_lse[((size_t)hc * nparts + part) * kPartRow + j] = s_live[j] ? s_lse2[j] : INFINITY;
+        // the ring loads issued past this part's phase 1 (none: the stream
+        // ends with it) have all landed before the loaders' last hand-over
+        return true;
+    }
     // written by group 0, which issues no ring loads
-    if (lse_out && group == 0) {
+    if (lse_out && group == 0 && part == 0) {
         for (int j = tid; j < K; j += kQ * kWave)
             lse_out[(size_t)hc * K + j] = s_live[j] ? s_lse2[j] * kLn2 : __int_as_float(0x7fc00000);
     }
@@ -604,7 +663,7 @@ __device__ __forceinline__ bool score_head(
     // The other groups' partial maxima of tile j pass through s_pmax[j % 3];
     // group 0 finishes tile j once they have crossed a barrier.
     auto finalize = [&](int j, float mx) {
-        const int n = kTileKeys * (t2 + kQ * j + q) + col;
+        const int n = kTileKeys * (p2a + kQ * j + q) + col;
         if (j <= jlast2 && hh == 0 && n >= P && n < N) {
 #pragma unroll
             for (int g = 0; g < kGroups - 1; ++g) mx = fmaxf(mx, s_pmax[j % 3][g][q][col]);
@@ -692,6 +751,43 @@ __global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_evict_shared_kern
                                                    pos_stride, ck, status, blockIdx.x * c.H + h))
             return;
     }
+}
+
+// A head-cache's keys split over `nparts` workgroups (workgroup b takes part
+// b % nparts of head-cache b / nparts): the partial log-sum-exps of each
+// part's key tiles ...
+template <int NG, int NQ, int MBW, int WPE>
+__global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_lse_split_kernel(
+    CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
+    float* __restrict__ part_lse, int nparts, Check ck, int32_t* status) {
+    score_head<NG, NQ, MBW, kSplitLse>(c, beacons, counts, K, 0, 0.f, nullptr, 0, nullptr, 0,
+                                       nullptr, nullptr, 0, ck, status, blockIdx.x / nparts,
+                                       blockIdx.x % nparts, nparts, part_lse);
+}
+
+// ... then, after they are merged, each part's share of the candidate scores.
+template <int NG, int NQ, int MBW, int WPE>
+__global__ __launch_bounds__(NG * NQ * kWave, WPE) void beacon_score_split_kernel(
+    CacheView c, const float* __restrict__ beacons, const int32_t* __restrict__ counts, int K,
+    int window, float bonus, float* __restrict__ scores, int stride, float* __restrict__ lse_out,
+    float* __restrict__ part_lse, int nparts, Check ck, int32_t* status) {
+    score_head<NG, NQ, MBW, kSplitScore>(c, beacons, counts, K, window, bonus, scores, stride,
+                                         lse_out, 0, nullptr, nullptr, 0, ck, status,
+                                         blockIdx.x / nparts, blockIdx.x % nparts, nparts,
+                                         part_lse);
+}
+
+template <int NG, int NQ, int MBW, int WPE>
+void launch_split_cfg(const CacheView& c, const float* beacons, const int32_t* counts, int K,
+                      int window, float bonus, float* scores, int stride, float* lse,
+                      float* part_lse, int nparts, Check ck, int32_t* status, hipStream_t s) {
+    const unsigned grid = (unsigned)(c.L * c.R * c.H) * (unsigned)nparts;
+    hipLaunchKernelGGL((beacon_lse_split_kernel<NG, NQ, MBW, WPE>), dim3(grid),
+                       dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, part_lse, nparts, ck,
+                       status);
+    hipLaunchKernelGGL((beacon_score_split_kernel<NG, NQ, MBW, WPE>), dim3(grid),
+                       dim3(NG * NQ * kWave), 0, s, c, beacons, counts, K, window, bonus, scores,
+                       stride, lse, part_lse, nparts, ck, status);
 }
 
 template <int NG, int NQ, int MBW, int WPE, int kMode>
@@ -785,6 +881,25 @@ hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const i
                                float* lse, Check ck, int32_t* status, hipStream_t s) {
     return launch_any<kScoreOnly>(c, beacons, counts, K, window, bonus, scores, stride, lse, 0,
                                   nullptr, nullptr, 0, ck, status, s);
+}
+
+hipError_t launch_beacon_score_split(const CacheView& c, const float* beacons,
+                                     const int32_t* counts, int K, int window, float bonus,
+                                     float* scores, int stride, float* lse, float* part_lse,
+                                     int nparts, Check ck, int32_t* status, hipStream_t s) {
+    if (c.L * c.R * c.H == 0) return hipSuccess;
+    // the workgroups of every part fill the chip, so the layouts of wide
+    // launches serve (at K = 256, two workgroups per CU)
+    if (K <= 64)
+        launch_split_cfg<2, 2, 1, 2>(c, beacons, counts, K, window, bonus, scores, stride, lse,
+                                     part_lse, nparts, ck, status, s);
+    else if (K <= 128)
+        launch_split_cfg<2, 2, 2, 2>(c, beacons, counts, K, window, bonus, scores, stride, lse,
+                                     part_lse, nparts, ck, status, s);
+    else
+        launch_split_cfg<8, 1, 1, 4>(c, beacons, counts, K, window, bonus, scores, stride, lse,
+                                     part_lse, nparts, ck, status, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_beacon_evict(const CacheView& c, const float* beacons, const int32_t* counts,

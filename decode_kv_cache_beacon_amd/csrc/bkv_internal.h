@@ -173,6 +173,15 @@ hipError_t launch_beacon_update(int HC, int T, int G, int K, const uint16_t* q, 
 hipError_t launch_beacon_score(const CacheView& c, const float* beacons, const int32_t* counts,
                                int K, int window, float bonus, float* scores, int stride,
                                float* lse, Check ck, int32_t* status, hipStream_t s);
+// The same scores with every head-cache's keys split over `nparts` workgroups
+// (two launches: partial log-sum-exps into part_lse, [HC][nparts][256]
+// floats, then the merge and each part's share of the scores).  Their last
+// bits differ from the unsplit kernel's (another summation order); the pass
+// uses it only where no fused kernel could run.
+hipError_t launch_beacon_score_split(const CacheView& c, const float* beacons,
+                                     const int32_t* counts, int K, int window, float bonus,
+                                     float* scores, int stride, float* lse, float* part_lse,
+                                     int nparts, Check ck, int32_t* status, hipStream_t s);
 // Scoring, top-B selection and compaction of every head-cache in one kernel
 // (per-head selection).  `scores` is still written (the selection reads it
 // back); keep_out and pos_ids are nullable.  Requires stride + budget <=

@@ -341,8 +341,9 @@ typedef struct bkv_pass_args {
 } bkv_pass_args;
 
 /* Bytes of workspace bkv_evict_pass needs for these arguments (the score and
- * keep buffers it is not given).  The workspace is a caller-owned device
- * buffer aligned to 256 bytes. */
+ * keep buffers it is not given, and the partial log-sum-exps of a split
+ * beacon scoring, below).  The workspace is a caller-owned device buffer
+ * aligned to 256 bytes. */
 int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, size_t* bytes);
 
 /* Runs, on `stream`: (beacon) maintenance -> beacon scoring -> selection ->
@@ -350,6 +351,11 @@ int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, si
  * page_retention, bkv_page_retain takes the place of the last two.  Scoring,
  * selection and compaction run as one fused kernel where separate_steps
  * allows it (see there); the results are those of the separate kernels.
+ * A beacon pass that no fused kernel could run (score_stride + budget >
+ * BKV_FUSED_MAX_ENTRIES) with at most 256 head-caches splits each
+ * head-cache's keys over several workgroups to fill the GPU: its scores and
+ * lse then match bkv_beacon_score's to within fp32 rounding (another
+ * summation order), not bit for bit.
  * A request that fails a device check (lengths, block ids, budget) is left
  * entirely untouched -- beacons, counts, cache and pos_ids -- and flagged in
  * *status. */

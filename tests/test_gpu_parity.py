@@ -396,12 +396,15 @@ def test_beacon_score_one_shot_long():
 
 
 # ------------------------------------------------------------------ whole pass
-def _pass_case(wl, N, P, B, selector, seed=17, shared=False, separate=False):
+def _pass_case(wl, N, P, B, selector, seed=17, shared=False, separate=False, mutate=None):
     """One bkv_evict_pass against the oracle.  shared=True: one selection per
     (layer, request) for all its heads (beacon: merged per-head scores;
     random: one draw row with the head field 0).  separate=True: score,
-    select and compact as three kernels instead of the fused one."""
+    select and compact as three kernels instead of the fused one.  The beacon
+    selector's lse output is checked too."""
     batch = synth.make_batch(wl)
+    if mutate:
+        mutate(batch)
     cache = device_cache(batch, N, P)
     k_in, v_in = host_pools(cache)
     bt = batch.block_table.numpy()
@@ -415,9 +418,11 @@ def _pass_case(wl, N, P, B, selector, seed=17, shared=False, separate=False):
         T, G = q.shape[1], q.shape[2]
         assign = torch.zeros((HC, T * G), dtype=torch.int32).cuda()
         sc = torch.zeros((HC, S)).cuda()
+        lse = torch.zeros((HC, b.shape[1])).cuda()
         bk.bkv_evict_pass(cache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
                           window=64, bonus=1.0, assign=assign, pos_ids=pos_dev, scores_out=sc,
-                          keep_out=keep, shared_positions=shared, separate_steps=separate)
+                          keep_out=keep, shared_positions=shared, separate_steps=separate,
+                          lse=lse)
     else:
         rid = torch.arange(100, 100 + cache.n_requests, dtype=torch.int64).cuda()
         pss = torch.full((cache.n_requests,), 4, dtype=torch.int32).cuda()
@@ -447,8 +452,12 @@ def _pass_case(wl, N, P, B, selector, seed=17, shared=False, separate=False):
                     assert gap.max() <= ASSIGN_TOL, hc
                     assert np.array_equal(ob.view(np.int32), b[hc].cpu().numpy().view(np.int32))
                     assert np.array_equal(oc, c[hc].cpu().numpy()), hc
-                    o, _ = oracle.beacon_score(keys[hc], ob, oc, p, 64, 1.0)
+                    o, ol = oracle.beacon_score(keys[hc], ob, oc, p, 64, 1.0)
                     check_scores(scn[hc, :n - p], o, f"pass hc {hc}")
+                    live, ln = oc > 0, lse[hc].cpu().numpy()
+                    assert np.all(np.isnan(ln[~live])), hc
+                    if live.any() and n > 0:
+                        assert np.max(np.abs(ln[live] - ol[live])) <= 1e-3, hc
                     os_.append(o)
                     gs.append(scn[hc, :n - p].astype(np.float64))
                 if shared:
@@ -883,6 +892,37 @@ def test_decode_attention_after_compaction():
 def test_evict_pass_tiny_one_shot():
     say("pass tiny")
     _pass_case(synth.WORKLOADS["tiny"], N=[4096], P=[512], B=1024, selector="beacon")
+
+
+@pytest.mark.parametrize("case", ["k256", "k64-rescue", "k128-sparse", "k256-shared"])
+def test_evict_pass_split_scoring(case):
+    """More candidates and keep entries than a fused kernel holds, and few
+    head-caches: the pass splits each head-cache's keys over several
+    workgroups (partial log-sum-exps, merged, then each part's share of the
+    candidates).  Covered: a request whose candidates span fewer tiles than
+    there are parts, one with no prompt, a logit spread that overflows one
+    part's running sum (its exact fallback), mostly never-filled beacons, and
+    shared positions."""
+    say("pass split", case)
+    N, P, B = [12288, 4200, 9001], [512, 4090, 0], 4096
+    assert max(N) + B > bk.FUSED_MAX_ENTRIES
+    if case.startswith("k256"):
+        wl = small("qwen3_32b_r32", n_layers=1, n_requests=3, n_kv_heads=2, budget=B,
+                   seq_len=max(N), steps=8)
+        _pass_case(wl, N, P, B, selector="beacon", shared=case == "k256-shared")
+    elif case == "k64-rescue":
+        wl = small(n_layers=1, n_requests=3, n_kv_heads=2, n_beacons=64, budget=B,
+                   seq_len=max(N), steps=4)
+
+        def mutate(batch):
+            k = batch.k_pools[0].float()
+            k[batch.block_table[0, 500]] *= 40.0   # a late block of huge keys, request 0
+            batch.k_pools[0] = k.to(torch.bfloat16)
+        _pass_case(wl, N, P, B, selector="beacon", mutate=mutate)
+    else:
+        wl = small(n_layers=1, n_requests=3, n_kv_heads=2, n_beacons=128, budget=B,
+                   seq_len=max(N), steps=2, prewarm=False)
+        _pass_case(wl, N, P, B, selector="beacon")
 
 
 def test_evict_pass_k256_group8():
