@@ -24,7 +24,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ---------------------------------------------------------------- constants
-BKV_ABI_VERSION = 7
+BKV_ABI_VERSION = 8
 # bkv_evict_pass fuses score, select and compact (row compaction with per-head
 # selection, or shared positions for the beacon selector) when score_stride +
 # budget is at most this
@@ -37,6 +37,7 @@ BKV_ERR_SCRATCH = 9
 BKV_SCORE_F32, BKV_SCORE_U32 = 0, 1
 BKV_SELECT_BEACON, BKV_SELECT_RANDOM = 0, 1
 BKV_ROWS_PER_HEAD, BKV_ROWS_PER_LAYER_REQUEST, BKV_ROWS_PER_REQUEST = 0, 1, 2
+BKV_PAGES_OFF, BKV_PAGES_PER_REQUEST, BKV_PAGES_PER_HEAD = 0, 1, 2
 BKV_MAX_BEACONS = 256
 BKV_MAX_CANDIDATES = 32768
 BKV_MAX_QUERY_HEADS = 8
@@ -52,7 +53,7 @@ class bkv_cache(ctypes.Structure):
         ("n_layers", _i32), ("n_requests", _i32), ("n_kv_heads", _i32), ("head_dim", _i32),
         ("block_size", _i32), ("max_blocks", _i32), ("num_blocks", _i64),
         ("k_pools", _P), ("v_pools", _P), ("block_table", _P), ("seq_len", _P),
-        ("prompt_len", _P),
+        ("prompt_len", _P), ("head_block_table", _P), ("head_seq_len", _P),
     ]
 
 
@@ -92,6 +93,9 @@ _lib.bkv_kv_compact.restype = _i32
 _lib.bkv_page_retain.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i32, _i32, _i32, _P, _P, _P,
                                  _P, _P, _P]
 _lib.bkv_page_retain.restype = _i32
+_lib.bkv_page_retain_heads.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _i32, _i32, _P, _P,
+                                       _P, _P, _P, _P]
+_lib.bkv_page_retain_heads.restype = _i32
 _lib.bkv_decode_attention.argtypes = [ctypes.POINTER(bkv_cache), _P, _i32, _f32, _P, _P, _P]
 _lib.bkv_decode_attention.restype = _i32
 _lib.bkv_workspace_size.argtypes = [ctypes.POINTER(bkv_cache), ctypes.POINTER(bkv_pass_args),
@@ -106,7 +110,7 @@ _lib.bkv_evict_pass_noalloc.restype = _i32
 
 EXPORTS = ("bkv_abi_version", "bkv_status_string", "bkv_beacon_update", "bkv_beacon_score",
            "bkv_random_score", "bkv_topk_select", "bkv_topk_select_shared", "bkv_kv_compact",
-           "bkv_page_retain", "bkv_decode_attention", "bkv_workspace_size", "bkv_evict_pass",
+           "bkv_page_retain", "bkv_page_retain_heads", "bkv_decode_attention", "bkv_workspace_size", "bkv_evict_pass",
            "bkv_evict_pass_noalloc")
 
 
@@ -185,12 +189,17 @@ def check_status(status: torch.Tensor, where: str = "eviction pass", stream=None
 
 @dataclasses.dataclass
 class PagedCache:
-    """A paged bf16 KV cache: per-layer pools [num_blocks, H, 16, 128]."""
+    """A paged bf16 KV cache: per-layer pools [num_blocks, H, 16, 128].  With
+    head_block_table int32 [HC, max_blocks] and head_seq_len int32 [HC] (both
+    or neither), every head-cache reads its slots through its own row (what
+    bkv_page_retain_heads writes)."""
     k_pools: list
     v_pools: list
     block_table: torch.Tensor   # int32 [R, max_blocks]
     seq_len: torch.Tensor       # int32 [R]
     prompt_len: torch.Tensor    # int32 [R]
+    head_block_table: Optional[torch.Tensor] = None   # int32 [HC, max_blocks]
+    head_seq_len: Optional[torch.Tensor] = None       # int32 [HC]
     _k_addr: torch.Tensor = None
     _v_addr: torch.Tensor = None
 
@@ -209,6 +218,13 @@ class PagedCache:
             raise ValueError("block_table must be [R, max_blocks]")
         _need(self.seq_len, "seq_len", torch.int32, (R,))
         _need(self.prompt_len, "prompt_len", torch.int32, (R,))
+        if (self.head_block_table is None) != (self.head_seq_len is None):
+            raise ValueError("head_block_table and head_seq_len come together")
+        if self.head_block_table is not None:
+            HC = len(self.k_pools) * R * shape[1]
+            _need(self.head_block_table, "head_block_table", torch.int32,
+                  (HC, self.block_table.shape[1]))
+            _need(self.head_seq_len, "head_seq_len", torch.int32, (HC,))
         dev = self.k_pools[0].device
         self._k_addr = torch.tensor([t.data_ptr() for t in self.k_pools], dtype=torch.int64,
                                     device=dev)
@@ -251,7 +267,10 @@ class PagedCache:
         return bkv_cache(self.n_layers, self.n_requests, self.n_kv_heads, HEAD_DIM, BLOCK_SIZE,
                          self.max_blocks, self.num_blocks, self._k_addr.data_ptr(),
                          self._v_addr.data_ptr(), self.block_table.data_ptr(),
-                         self.seq_len.data_ptr(), self.prompt_len.data_ptr())
+                         self.seq_len.data_ptr(), self.prompt_len.data_ptr(),
+                         None if self.head_block_table is None
+                         else self.head_block_table.data_ptr(),
+                         None if self.head_seq_len is None else self.head_seq_len.data_ptr())
 
 
 # ---------------------------------------------------------------- entry points
@@ -431,6 +450,38 @@ def bkv_page_retain(cache: PagedCache, scores, budget, keep_pages, block_table_o
     return st
 
 
+def bkv_page_retain_heads(cache: PagedCache, scores, budget, keep_pages, head_table_out,
+                          head_seq_len_out, dropped_blocks, status=None, check=True, stream=None):
+    """Whole-page retention per head-cache: each head-cache keeps budget // 16
+    pages chosen from its own score row.
+
+    scores: fp32 beacon scores or int32-stored uint32 draws, [HC, stride].
+    keep_pages int32 [HC, budget // 16]; head_table_out int32 [HC, max_blocks] and
+    head_seq_len_out int32 [HC] (either may be the cache's own per-head tensor:
+    rewritten in place); dropped_blocks int32 [HC, max_blocks].  Reading the cache
+    afterwards: PagedCache(..., head_block_table=head_table_out,
+    head_seq_len=head_seq_len_out)."""
+    HC = cache.n_head_caches
+    kind = _score_kind(scores)
+    _need(scores, "scores", scores.dtype)
+    if scores.dim() != 2 or scores.shape[0] != HC:
+        raise ValueError("scores must be [HC, stride]")
+    _need(keep_pages, "keep_pages", torch.int32, (HC, budget // BLOCK_SIZE))
+    _need(head_table_out, "head_table_out", torch.int32, (HC, cache.max_blocks))
+    _need(head_seq_len_out, "head_seq_len_out", torch.int32, (HC,))
+    _need(dropped_blocks, "dropped_blocks", torch.int32, (HC, cache.max_blocks))
+    st, own = _status(status, cache.device, stream)
+    c = cache.struct()
+    code = _lib.bkv_page_retain_heads(ctypes.byref(c), _ptr(scores), kind, scores.shape[1],
+                                      int(budget), _ptr(keep_pages), _ptr(head_table_out),
+                                      _ptr(head_seq_len_out), _ptr(dropped_blocks), _ptr(st),
+                                      _stream(stream))
+    _check(code, "bkv_page_retain_heads")
+    if own and check:
+        check_status(st, "bkv_page_retain_heads", stream)
+    return st
+
+
 def bkv_decode_attention(cache: PagedCache, queries, out, scale=None, status=None, check=True,
                          stream=None):
     """queries bf16 [HC, G, 128] -> out fp32 [HC, G, 128]: softmax attention of every query
@@ -455,7 +506,7 @@ def bkv_decode_attention(cache: PagedCache, queries, out, scale=None, status=Non
 def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, window, bonus,
                assign, lse, seed, request_ids, pass_idx, pos_ids, scores_out, keep_out,
                score_stride, count_cap=0, shared_positions=False, page_retention=None,
-               separate_steps=False):
+               separate_steps=False, page_heads=False):
     HC, R = cache.n_head_caches, cache.n_requests
     LR = cache.n_layers * R
     a = bkv_pass_args()
@@ -466,10 +517,11 @@ def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, wi
     a.separate_steps = int(bool(separate_steps))
     if page_retention is not None:
         bto, slo, fr = page_retention
-        _need(bto, "block_table_out", torch.int32, (R, cache.max_blocks))
-        _need(slo, "seq_len_out", torch.int32, (R,))
-        _need(fr, "freed_blocks", torch.int32, (R, cache.max_blocks))
-        a.page_retention = 1
+        U = HC if page_heads else R
+        _need(bto, "block_table_out", torch.int32, (U, cache.max_blocks))
+        _need(slo, "seq_len_out", torch.int32, (U,))
+        _need(fr, "freed_blocks", torch.int32, (U, cache.max_blocks))
+        a.page_retention = BKV_PAGES_PER_HEAD if page_heads else BKV_PAGES_PER_REQUEST
         a.block_table_out, a.seq_len_out, a.freed_blocks = bto.data_ptr(), slo.data_ptr(), fr.data_ptr()
     if selector == BKV_SELECT_BEACON:
         _need(queries, "queries", torch.bfloat16)
@@ -502,7 +554,7 @@ def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, wi
     if scores_out is not None:
         want = torch.float32 if selector == BKV_SELECT_BEACON else torch.int32
         rows = HC
-        if selector == BKV_SELECT_RANDOM and page_retention is not None:
+        if selector == BKV_SELECT_RANDOM and page_retention is not None and not page_heads:
             rows = R
         elif selector == BKV_SELECT_RANDOM and shared_positions:
             rows = LR
@@ -510,7 +562,7 @@ def _pass_args(cache: PagedCache, selector, budget, queries, beacons, counts, wi
         a.scores_out = scores_out.data_ptr()
     if keep_out is not None:
         if page_retention is not None:
-            shape = (R, budget // BLOCK_SIZE)
+            shape = (HC if page_heads else R, budget // BLOCK_SIZE)
         else:
             shape = (LR if shared_positions else HC, budget)
         _need(keep_out, "keep_out", torch.int32, shape)
@@ -547,12 +599,14 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
                    request_ids=None, pass_idx=None, pos_ids=None, scores_out=None,
                    keep_out=None, score_stride=0, workspace=None, status=None, check=True,
                    stream=None, timing_events=None, count_cap=0, shared_positions=False,
-                   page_retention=None, separate_steps=False):
+                   page_retention=None, separate_steps=False, page_heads=False):
     """One whole eviction pass (beacon: update -> score -> select -> compact;
     random: score -> select -> compact), every layer/request/head at once.
     shared_positions: one selection per (layer, request) for all its heads.
     page_retention: (block_table_out, seq_len_out, freed_blocks) to keep whole
-    pages per request instead (no rows move; keep_out is then the kept pages).
+    pages per request instead (no rows move; keep_out is then the kept pages);
+    with page_heads=True every head-cache keeps its own pages and the three
+    outputs are per head-cache ([HC, max_blocks], [HC], [HC, max_blocks]).
 
     separate_steps: run score, select and compact as three kernels even where
     a fused kernel applies (row compaction with per-head selection for either
@@ -564,7 +618,7 @@ def bkv_evict_pass(cache: PagedCache, selector, budget, *, queries=None, beacons
     compact, and the other two are empty)."""
     a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
                    seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride,
-                   count_cap, shared_positions, page_retention, separate_steps)
+                   count_cap, shared_positions, page_retention, separate_steps, page_heads)
     ev_arr = _timing_args(a, timing_events, stream)  # noqa: F841 (kept alive for the call)
     need = bkv_workspace_size(cache, a)
     if workspace is None and need:
@@ -587,7 +641,7 @@ def bkv_evict_pass_noalloc(cache: PagedCache, selector, budget, *, queries=None,
                            request_ids=None, pass_idx=None, pos_ids=None, scores_out=None,
                            keep_out=None, score_stride=0, status=None, stream=None,
                            timing_events=None, count_cap=0, shared_positions=False,
-                           page_retention=None, separate_steps=False):
+                           page_retention=None, separate_steps=False, page_heads=False):
     """bkv_evict_pass for callers that cannot allocate device memory: the
     score and keep buffers it is not given live in the library's per-GPU
     scratch array (NOALLOC_SCRATCH_BYTES; larger passes raise BKV_ERR_SCRATCH).
@@ -596,7 +650,7 @@ def bkv_evict_pass_noalloc(cache: PagedCache, selector, budget, *, queries=None,
     errors).  Calls whose work overlaps on one GPU share the scratch and race."""
     a = _pass_args(cache, selector, budget, queries, beacons, counts, window, bonus, assign, lse,
                    seed, request_ids, pass_idx, pos_ids, scores_out, keep_out, score_stride,
-                   count_cap, shared_positions, page_retention, separate_steps)
+                   count_cap, shared_positions, page_retention, separate_steps, page_heads)
     ev_arr = _timing_args(a, timing_events, stream)  # noqa: F841 (kept alive for the call)
     if status is not None:
         _need(status, "status", torch.int32)

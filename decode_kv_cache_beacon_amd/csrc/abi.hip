@@ -44,6 +44,11 @@ int32_t check_cache(const bkv_cache* cache, CacheView* v) {
         !aligned(cache->block_table, 4) || !aligned(cache->seq_len, 4) ||
         !aligned(cache->prompt_len, 4))
         return BKV_ERR_INVALID;
+    // per-head page tables come as a pair
+    if ((cache->head_block_table == nullptr) != (cache->head_seq_len == nullptr))
+        return BKV_ERR_INVALID;
+    if (!aligned(cache->head_block_table, 4) || !aligned(cache->head_seq_len, 4))
+        return BKV_ERR_INVALID;
     v->L = cache->n_layers;
     v->R = cache->n_requests;
     v->H = cache->n_kv_heads;
@@ -54,6 +59,8 @@ int32_t check_cache(const bkv_cache* cache, CacheView* v) {
     v->block_table = cache->block_table;
     v->seq_len = cache->seq_len;
     v->prompt_len = cache->prompt_len;
+    v->head_table = cache->head_block_table;
+    v->head_len = cache->head_seq_len;
     return BKV_OK;
 }
 
@@ -70,11 +77,12 @@ struct PassLayout {
 };
 
 // Row layout of the random selector's draws in a pass: per head-cache, per
-// (layer, request) with shared positions, per request with page retention.
+// (layer, request) with shared positions, per request with page retention
+// (per head-cache with per-head page retention).
 int random_rows(const bkv_pass_args* a) {
-    return a->page_retention     ? BKV_ROWS_PER_REQUEST
-           : a->shared_positions ? BKV_ROWS_PER_LAYER_REQUEST
-                                 : BKV_ROWS_PER_HEAD;
+    return a->page_retention == BKV_PAGES_PER_REQUEST ? BKV_ROWS_PER_REQUEST
+           : a->shared_positions                      ? BKV_ROWS_PER_LAYER_REQUEST
+                                                      : BKV_ROWS_PER_HEAD;
 }
 size_t layout_rows(const CacheView& v, int rows) {
     return rows == BKV_ROWS_PER_REQUEST        ? (size_t)v.R
@@ -88,9 +96,9 @@ size_t score_rows(const CacheView& v, const bkv_pass_args* a) {
                                             : layout_rows(v, BKV_ROWS_PER_HEAD);
 }
 size_t keep_rows(const CacheView& v, const bkv_pass_args* a) {
-    return a->page_retention     ? (size_t)v.R
-           : a->shared_positions ? (size_t)v.L * v.R
-                                 : (size_t)v.L * v.R * v.H;
+    return a->page_retention == BKV_PAGES_PER_REQUEST ? (size_t)v.R
+           : a->shared_positions                      ? (size_t)v.L * v.R
+                                                      : (size_t)v.L * v.R * v.H;
 }
 size_t keep_cols(const bkv_pass_args* a) {
     return a->page_retention ? (size_t)(a->budget / kBlock) : (size_t)a->budget;
@@ -126,8 +134,13 @@ int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     if (stride > BKV_MAX_CANDIDATES) return BKV_ERR_INVALID;
     if (a->budget < 1) return BKV_ERR_INVALID;
     if (a->shared_positions != 0 && a->shared_positions != 1) return BKV_ERR_INVALID;
-    if (a->page_retention != 0 && a->page_retention != 1) return BKV_ERR_INVALID;
+    if (a->page_retention != 0 && a->page_retention != BKV_PAGES_PER_REQUEST &&
+        a->page_retention != BKV_PAGES_PER_HEAD)
+        return BKV_ERR_INVALID;
     if (a->page_retention && (a->budget % kBlock != 0 || a->shared_positions))
+        return BKV_ERR_INVALID;
+    // a cache read through per-head page tables: every selection is per head
+    if (v.head_table && (a->shared_positions || a->page_retention == BKV_PAGES_PER_REQUEST))
         return BKV_ERR_INVALID;
     size_t off = 0;
     L->stride = stride;
@@ -161,7 +174,8 @@ int32_t run_pass(const CacheView& v, const PassLayout& L, const bkv_pass_args* a
         return BKV_ERR_INVALID;
     const bool beacon = a->selector == BKV_SELECT_BEACON;
     const int shared = a->shared_positions;
-    const bool pages = a->page_retention;
+    const bool pages = a->page_retention != 0;
+    const bool head_pages = a->page_retention == BKV_PAGES_PER_HEAD;
     if (pages) {
         if (!a->block_table_out || !a->seq_len_out || !a->freed_blocks) return BKV_ERR_NULL;
         if (a->pos_ids || !aligned(a->block_table_out, 4) || !aligned(a->seq_len_out, 4) ||
@@ -236,7 +250,11 @@ int32_t run_pass(const CacheView& v, const PassLayout& L, const bkv_pass_args* a
             he = launch_beacon_score(v, a->beacons, a->counts, a->n_beacons, a->window, a->bonus,
                                      static_cast<float*>(sc), L.stride, a->lse, all, status, s);
         if (he == hipSuccess) he = mark();
-        if (he == hipSuccess && pages)
+        if (he == hipSuccess && head_pages)
+            he = launch_page_retain_heads(v, sc, BKV_SCORE_F32, L.stride, a->budget, keep,
+                                          a->block_table_out, a->seq_len_out, a->freed_blocks,
+                                          all, status, s);
+        else if (he == hipSuccess && pages)
             he = launch_page_retain(v, sc, BKV_SCORE_F32, L.stride, BKV_ROWS_PER_HEAD, a->budget,
                                     keep, a->block_table_out, a->seq_len_out, a->freed_blocks,
                                     all, status, s);
@@ -247,7 +265,11 @@ int32_t run_pass(const CacheView& v, const PassLayout& L, const bkv_pass_args* a
         he = launch_random_score(v, a->seed, a->request_ids, a->pass_idx, random_rows(a),
                                  static_cast<uint32_t*>(sc), L.stride, all, status, s);
         if (he == hipSuccess) he = mark();
-        if (he == hipSuccess && pages)
+        if (he == hipSuccess && head_pages)
+            he = launch_page_retain_heads(v, sc, BKV_SCORE_U32, L.stride, a->budget, keep,
+                                          a->block_table_out, a->seq_len_out, a->freed_blocks,
+                                          all, status, s);
+        else if (he == hipSuccess && pages)
             he = launch_page_retain(v, sc, BKV_SCORE_U32, L.stride, BKV_ROWS_PER_REQUEST,
                                     a->budget, keep, a->block_table_out, a->seq_len_out,
                                     a->freed_blocks, all, status, s);
@@ -366,6 +388,7 @@ int32_t bkv_random_score(const bkv_cache* cache, uint64_t seed, const uint64_t* 
     if (!request_ids || !pass_idx || !scores) return BKV_ERR_NULL;
     if (score_stride < 1 || rows < BKV_ROWS_PER_HEAD || rows > BKV_ROWS_PER_REQUEST)
         return BKV_ERR_INVALID;
+    if (v.head_table && rows != BKV_ROWS_PER_HEAD) return BKV_ERR_INVALID;
     if (!aligned(request_ids, 8) || !aligned(pass_idx, 4) || !aligned(scores, 4) ||
         (status && !aligned(status, 4)))
         return BKV_ERR_INVALID;
@@ -399,7 +422,7 @@ int32_t bkv_topk_select_shared(const bkv_cache* cache, const void* scores, int32
     if (!scores || !keep_idx) return BKV_ERR_NULL;
     if (score_kind != BKV_SCORE_F32 && score_kind != BKV_SCORE_U32) return BKV_ERR_INVALID;
     if (score_stride < 1 || score_stride > BKV_MAX_CANDIDATES || budget < 1) return BKV_ERR_INVALID;
-    if (score_heads < 1 || score_heads > v.H) return BKV_ERR_INVALID;
+    if (score_heads < 1 || score_heads > v.H || v.head_table) return BKV_ERR_INVALID;
     if (!aligned(scores, 4) || !aligned(keep_idx, 4) || (status && !aligned(status, 4)))
         return BKV_ERR_INVALID;
     return hip_status(launch_topk_select(v, scores, score_kind, score_stride, score_heads, 1,
@@ -414,7 +437,8 @@ int32_t bkv_kv_compact(const bkv_cache* cache, const int32_t* keep_idx, int32_t 
     int32_t e = check_cache(cache, &v);
     if (e) return e;
     if (!keep_idx) return BKV_ERR_NULL;
-    if (budget < 1 || (keep_shared != 0 && keep_shared != 1)) return BKV_ERR_INVALID;
+    if (budget < 1 || (keep_shared != 0 && keep_shared != 1) || (keep_shared && v.head_table))
+        return BKV_ERR_INVALID;
     if (pos_ids && pos_stride < v.max_blocks * kBlock) return BKV_ERR_INVALID;
     if (!aligned(keep_idx, 4) || (pos_ids && !aligned(pos_ids, 4)) ||
         (status && !aligned(status, 4)))
@@ -434,7 +458,7 @@ int32_t bkv_page_retain(const bkv_cache* cache, const void* scores, int32_t scor
     if (!scores || !keep_pages || !block_table_out || !seq_len_out || !freed_blocks)
         return BKV_ERR_NULL;
     if (score_kind != BKV_SCORE_F32 && score_kind != BKV_SCORE_U32) return BKV_ERR_INVALID;
-    if (score_rows != BKV_ROWS_PER_HEAD && score_rows != BKV_ROWS_PER_REQUEST)
+    if ((score_rows != BKV_ROWS_PER_HEAD && score_rows != BKV_ROWS_PER_REQUEST) || v.head_table)
         return BKV_ERR_INVALID;
     if (score_stride < 1 || budget < kBlock || budget % kBlock != 0) return BKV_ERR_INVALID;
     if (!aligned(scores, 4) || !aligned(keep_pages, 4) || !aligned(block_table_out, 4) ||
@@ -444,6 +468,27 @@ int32_t bkv_page_retain(const bkv_cache* cache, const void* scores, int32_t scor
                                          keep_pages, block_table_out, seq_len_out, freed_blocks,
                                          Check{budget, score_stride, 1, 1}, status,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int32_t bkv_page_retain_heads(const bkv_cache* cache, const void* scores, int32_t score_kind,
+                              int32_t score_stride, int32_t budget, int32_t* keep_pages,
+                              int32_t* head_table_out, int32_t* head_seq_len_out,
+                              int32_t* dropped_blocks, int32_t* status, bkv_stream_t stream) {
+    CacheView v;
+    int32_t e = check_cache(cache, &v);
+    if (e) return e;
+    if (!scores || !keep_pages || !head_table_out || !head_seq_len_out || !dropped_blocks)
+        return BKV_ERR_NULL;
+    if (score_kind != BKV_SCORE_F32 && score_kind != BKV_SCORE_U32) return BKV_ERR_INVALID;
+    if (score_stride < 1 || budget < kBlock || budget % kBlock != 0) return BKV_ERR_INVALID;
+    if (!aligned(scores, 4) || !aligned(keep_pages, 4) || !aligned(head_table_out, 4) ||
+        !aligned(head_seq_len_out, 4) || !aligned(dropped_blocks, 4) ||
+        (status && !aligned(status, 4)))
+        return BKV_ERR_INVALID;
+    return hip_status(launch_page_retain_heads(v, scores, score_kind, score_stride, budget,
+                                               keep_pages, head_table_out, head_seq_len_out,
+                                               dropped_blocks, Check{budget, score_stride, 1, 1},
+                                               status, static_cast<hipStream_t>(stream)));
 }
 
 int32_t bkv_decode_attention(const bkv_cache* cache, const uint16_t* queries, int32_t G,

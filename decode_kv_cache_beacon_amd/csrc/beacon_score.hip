@@ -274,8 +274,8 @@ __device__ __forceinline__ bool score_head(
     __shared__ int s_rescue;
 
     const HeadIdx x = split_hc(c, hc);
-    if (!request_ok(c, x.layer, x.req, ck, status)) return false;
-    const int N = c.seq_len[x.req];
+    if (!request_ok(c, x.layer, x.req, hc, ck, status)) return false;
+    const int N = slot_count(c, hc, x.req);
     const int P = c.prompt_len[x.req];
 
     const int tid = threadIdx.x;
@@ -292,7 +292,7 @@ __device__ __forceinline__ bool score_head(
     const bool computes = mb0 < MB;
 
     const int nb = (N + kBlock - 1) / kBlock;
-    const int32_t* bt = c.block_table + (size_t)x.req * c.max_blocks;
+    const int32_t* bt = table_row(c, hc, x.req);
     for (int i = tid; i < nb; i += blockDim.x) s_bt[i] = bt[i];
     for (int j = tid; j < Kp; j += blockDim.x)
         s_live[j] = (j < K) && counts[(size_t)hc * K + j] > 0;

@@ -22,7 +22,22 @@ struct CacheView {
     const int32_t* block_table;
     const int32_t* seq_len;
     const int32_t* prompt_len;
+    // per-head page tables (both null, or both set): head-cache hc reads its
+    // slots through row hc and has head_len[hc] of them
+    const int32_t* head_table;
+    const int32_t* head_len;
 };
+
+// The block-table row and the slot count of head-cache hc of request r (hc <
+// 0: the request's own row, for kernels that serve whole requests, which the
+// entry points never launch on a cache with per-head tables).
+__device__ __forceinline__ const int32_t* table_row(const CacheView& c, int hc, int r) {
+    return (c.head_table && hc >= 0) ? c.head_table + (size_t)hc * c.max_blocks
+                                     : c.block_table + (size_t)r * c.max_blocks;
+}
+__device__ __forceinline__ int slot_count(const CacheView& c, int hc, int r) {
+    return (c.head_len && hc >= 0) ? c.head_len[hc] : c.seq_len[r];
+}
 
 struct HeadIdx {
     int layer, req, head;
@@ -62,12 +77,17 @@ __device__ __forceinline__ bool any_thread(bool p) {
     else return __syncthreads_or(p) != 0;
 }
 
-// Checks of request r by `nthreads` cooperating threads (this one is `tid`);
-// `any` ORs a predicate over them.  Errors are OR-ed into *status by tid 0.
+// Checks of head-cache hc of request r (hc < 0: of the request's own row) by
+// `nthreads` cooperating threads (this one is `tid`); `any` ORs a predicate
+// over them.  Errors are OR-ed into *status by tid 0.  Without per-head page
+// tables every head-cache of a request reads the same row and lengths, so the
+// outcome is the request's; with them the row and the slot count checked are
+// the head-cache's own.
 template <class Any>
-__device__ inline bool request_ok_impl(const CacheView& c, int layer, int r, const Check& ck,
-                                       int32_t* status, int tid, int nthreads, Any any) {
-    const int N = c.seq_len[r];
+__device__ inline bool request_ok_impl(const CacheView& c, int layer, int r, int hc,
+                                       const Check& ck, int32_t* status, int tid, int nthreads,
+                                       Any any) {
+    const int N = slot_count(c, hc, r);
     const int P = c.prompt_len[r];
     int err = 0;
     if (P < 0 || N < P || N > c.max_blocks * kBlock) err |= 1 << BKV_ERR_LENGTH;
@@ -91,7 +111,7 @@ __device__ inline bool request_ok_impl(const CacheView& c, int layer, int r, con
     if (ck.blocks) {
         if (((c.k_pools[layer] | c.v_pools[layer]) & 15u) != 0) err |= 1 << BKV_ERR_INVALID;
         const int nb = (err & (1 << BKV_ERR_LENGTH)) ? 0 : (N + kBlock - 1) / kBlock;
-        const int32_t* row = c.block_table + (size_t)r * c.max_blocks;
+        const int32_t* row = table_row(c, hc, r);
         for (int i = tid; i < nb; i += nthreads) {
             const int b = row[i];
             bad |= (b < 0) || ((int64_t)b >= c.num_blocks);
@@ -103,15 +123,15 @@ __device__ inline bool request_ok_impl(const CacheView& c, int layer, int r, con
     return err == 0;
 }
 
-// Validates request r.  Every thread of the block (kWaveOnly: of the wave)
-// must call it; the result is uniform.  Errors are OR-ed into *status by
-// thread (lane) 0.
+// Validates head-cache hc of request r (hc < 0: the request's own row).
+// Every thread of the block (kWaveOnly: of the wave) must call it; the result
+// is uniform.  Errors are OR-ed into *status by thread (lane) 0.
 template <bool kWaveOnly = false>
-__device__ inline bool request_ok(const CacheView& c, int layer, int r, const Check& ck,
+__device__ inline bool request_ok(const CacheView& c, int layer, int r, int hc, const Check& ck,
                                   int32_t* status) {
     const int tid = kWaveOnly ? (int)(threadIdx.x % kWave) : (int)threadIdx.x;
     const int nthreads = kWaveOnly ? kWave : (int)blockDim.x;
-    return request_ok_impl(c, layer, r, ck, status, tid, nthreads,
+    return request_ok_impl(c, layer, r, hc, ck, status, tid, nthreads,
                            [](bool p) { return any_thread<kWaveOnly>(p); });
 }
 
@@ -119,12 +139,12 @@ __device__ inline bool request_ok(const CacheView& c, int layer, int r, const Ch
 // group checking its own request r: every lane of the wave must call it, and
 // the result is uniform within each group.
 template <int G>
-__device__ inline bool request_ok_lanes(const CacheView& c, int layer, int r, const Check& ck,
-                                        int32_t* status) {
+__device__ inline bool request_ok_lanes(const CacheView& c, int layer, int r, int hc,
+                                        const Check& ck, int32_t* status) {
     const int lane = (int)(threadIdx.x % kWave);
     const unsigned long long gmask =
         G >= kWave ? ~0ull : (((1ull << G) - 1ull) << (lane / G * G));
-    return request_ok_impl(c, layer, r, ck, status, lane % G, G,
+    return request_ok_impl(c, layer, r, hc, ck, status, lane % G, G,
                            [gmask](bool p) { return (__ballot(p) & gmask) != 0ull; });
 }
 
@@ -217,6 +237,12 @@ hipError_t launch_page_retain(const CacheView& c, const void* scores, int kind, 
                               int rows, int budget, int32_t* keep_pages, int32_t* block_table_out,
                               int32_t* seq_len_out, int32_t* freed, Check ck, int32_t* status,
                               hipStream_t s);
+// Page retention per head-cache: each head-cache keeps budget / 16 pages of
+// its own (its own score row), written to its own page-table row.
+hipError_t launch_page_retain_heads(const CacheView& c, const void* scores, int kind, int stride,
+                                    int budget, int32_t* keep_pages, int32_t* head_table_out,
+                                    int32_t* head_len_out, int32_t* dropped, Check ck,
+                                    int32_t* status, hipStream_t s);
 hipError_t launch_topk_select(const CacheView& c, const void* scores, int kind, int stride,
                               int score_heads, int shared, int budget, int32_t* keep, Check ck,
                               int32_t* status, hipStream_t s);

@@ -74,15 +74,15 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(
     if (hc >= HC) return;  // the whole wave leaves; nothing below waits on other waves
     const HeadIdx x = split_hc(c, hc);
     // the workgroup's four waves may serve different requests: checks per wave
-    if (!request_ok<true>(c, x.layer, x.req, Check{-1, -1, 1, 0}, status)) return;
-    const int N = c.seq_len[x.req];
+    if (!request_ok<true>(c, x.layer, x.req, hc, Check{-1, -1, 1, 0}, status)) return;
+    const int N = slot_count(c, hc, x.req);
     const int rr = lane >> 4;          // slot within an instruction
     const int cc = lane & 15;          // 16-byte chunk of the row
     float* o = out + (size_t)hc * G * kHeadDim;
 
     // the head-cache's block-table row, in this wave's part of LDS
     int* bt = s_bt[w];
-    const int32_t* btg = c.block_table + (size_t)x.req * c.max_blocks;
+    const int32_t* btg = table_row(c, hc, x.req);
     for (int i = lane; i < (N + kBlock - 1) / kBlock; i += kWave) bt[i] = btg[i];
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

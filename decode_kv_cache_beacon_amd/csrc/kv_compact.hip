@@ -27,9 +27,9 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CacheView c,
                                                               int32_t* status) {
     const int hc = blockIdx.x;
     const HeadIdx x = split_hc(c, hc);
-    if (!request_ok(c, x.layer, x.req, ck, status)) return;
+    if (!request_ok(c, x.layer, x.req, hc, ck, status)) return;
 
-    const int N = c.seq_len[x.req];
+    const int N = slot_count(c, hc, x.req);
     const int nk = min(N, B);
     const int32_t* kp = keep + (size_t)(keep_shared ? hc / c.H : hc) * B;
 
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void kv_compact_kernel(CacheView c,
 
     const uint64_t kbase = c.k_pools[x.layer];
     const uint64_t vbase = c.v_pools[x.layer];
-    const int32_t* bt = c.block_table + (size_t)x.req * c.max_blocks;
+    const int32_t* bt = table_row(c, hc, x.req);
     const int nb = (N + kBlock - 1) / kBlock;
     for (int i = threadIdx.x; i < nb; i += kThreads) s_bt[i] = bt[i];
     __syncthreads();

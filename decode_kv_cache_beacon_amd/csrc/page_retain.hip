@@ -8,7 +8,13 @@
 // block equal to the cache page and one selection per request, both hold at
 // once and the selection maps straight onto the paged layout.
 //
-// One workgroup of 1024 threads per request:
+// Per head-cache (Random Attention article, section "发现二", which finds the
+// heads' selections largely redundant but credits per-head selection): every
+// head-cache selects its own pages from its own score row and writes its own
+// page-table row, still with no K/V row moves; the cache then reads each
+// head-cache through its row.
+//
+// One workgroup of 1024 threads per request (256 per head-cache):
 //   1. stage the request's block-table row in LDS (before anything is written,
 //      so the output row may alias the input);
 //   2. page key = the largest candidate-slot score of the page over all the
@@ -25,27 +31,32 @@
 namespace bkv {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxPagesPerThread = (kMaxBlocksPerReq + kThreads - 1) / kThreads;
-
+// kPerHead: workgroup u serves head-cache u (its own score row, its own
+// page-table row and slot count, outputs at row u); otherwise request u (its
+// score rows across every layer and head, or one per-request row).
+template <int kThreads, bool kPerHead>
 __global__ __launch_bounds__(kThreads) void page_retain_kernel(
     CacheView c, const uint32_t* __restrict__ scores, int is_f32, int stride, int per_request_row,
-    int B, int32_t* __restrict__ keep_pages, int32_t* block_table_out, int32_t* seq_len_out,
+    int B, int32_t* __restrict__ keep_pages, int32_t* table_out, int32_t* len_out,
     int32_t* __restrict__ freed, Check ck, int32_t* status) {
+    constexpr int kWaves = kThreads / kWave;
+    constexpr int kMaxPagesPerThread = (kMaxBlocksPerReq + kThreads - 1) / kThreads;
     __shared__ int s_bt[kMaxBlocksPerReq];
     __shared__ uint32_t s_pkey[kMaxBlocksPerReq];
     __shared__ RadixScratch s_rs;
     __shared__ int s_wsum[kWaves];
 
-    const int r = blockIdx.x;
+    const int u = blockIdx.x;
+    const HeadIdx x = kPerHead ? split_hc(c, u) : HeadIdx{0, u, 0};
+    const int r = x.req;
+    const int hc = kPerHead ? u : -1;
     const int tid = threadIdx.x;
-    if (!request_ok(c, 0, r, ck, status)) return;
-    const int N = c.seq_len[r];
+    if (!request_ok(c, x.layer, r, hc, ck, status)) return;
+    const int N = slot_count(c, hc, r);
     const int P = c.prompt_len[r];
     const int npages = (N + kBlock - 1) / kBlock;
     const int Bp = B / kBlock;
-    const int32_t* bt = c.block_table + (size_t)r * c.max_blocks;
+    const int32_t* bt = table_row(c, hc, r);
     for (int j = tid; j < npages; j += kThreads) {
         s_bt[j] = bt[j];
         s_pkey[j] = 0;
@@ -63,11 +74,12 @@ __global__ __launch_bounds__(kThreads) void page_retain_kernel(
     if (k > 0) {
         // candidate slots n in [pf*16, pe*16), at score column n - P
         const int i0 = pf * kBlock - P, i1 = pe * kBlock - P;
-        const int layers = per_request_row ? 1 : c.L;
-        const int heads = per_request_row ? 1 : c.H;
-        const size_t layer_step = per_request_row ? 0 : (size_t)c.R * c.H * stride;
-        const uint32_t* first_row =
-            scores + (per_request_row ? (size_t)r : (size_t)r * c.H) * stride;
+        const bool one_row = kPerHead || per_request_row;
+        const int layers = one_row ? 1 : c.L;
+        const int heads = one_row ? 1 : c.H;
+        const size_t layer_step = one_row ? 0 : (size_t)c.R * c.H * stride;
+        const size_t row0 = kPerHead ? (size_t)u : per_request_row ? (size_t)r : (size_t)r * c.H;
+        const uint32_t* first_row = scores + row0 * stride;
         for (int i = i0 + tid; i < i1; i += kThreads) {
             uint32_t v = 0;
             for (int l = 0; l < layers; ++l) {
@@ -112,9 +124,9 @@ __global__ __launch_bounds__(kThreads) void page_retain_kernel(
     const int kept_before = block_exclusive_scan<kThreads>(kept, s_wsum);
     const int n_kept = evict ? Bp : npages;
 
-    int32_t* kp = keep_pages + (size_t)r * Bp;
-    int32_t* row_out = block_table_out + (size_t)r * c.max_blocks;
-    int32_t* fr = freed + (size_t)r * c.max_blocks;
+    int32_t* kp = keep_pages + (size_t)u * Bp;
+    int32_t* row_out = table_out + (size_t)u * c.max_blocks;
+    int32_t* fr = freed + (size_t)u * c.max_blocks;
     int kb = kept_before;
 #pragma unroll
     for (int u = 0; u < kMaxPagesPerThread; ++u) {
@@ -134,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void page_retain_kernel(
     if (tid == 0) {
         // every kept page is full except a partial last page, which is always kept
         const int tail = N % kBlock;
-        seq_len_out[r] = evict ? n_kept * kBlock - (tail ? kBlock - tail : 0) : N;
+        len_out[u] = evict ? n_kept * kBlock - (tail ? kBlock - tail : 0) : N;
     }
 }
 
@@ -145,10 +157,23 @@ hipError_t launch_page_retain(const CacheView& c, const void* scores, int kind, 
                               int32_t* seq_len_out, int32_t* freed, Check ck, int32_t* status,
                               hipStream_t s) {
     if (c.R == 0) return hipSuccess;
-    hipLaunchKernelGGL(page_retain_kernel, dim3(c.R), dim3(kThreads), 0, s, c,
+    hipLaunchKernelGGL((page_retain_kernel<1024, false>), dim3(c.R), dim3(1024), 0, s, c,
                        static_cast<const uint32_t*>(scores), kind == BKV_SCORE_F32 ? 1 : 0,
                        stride, rows == BKV_ROWS_PER_REQUEST ? 1 : 0, budget, keep_pages,
                        block_table_out, seq_len_out, freed, ck, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_page_retain_heads(const CacheView& c, const void* scores, int kind, int stride,
+                                    int budget, int32_t* keep_pages, int32_t* head_table_out,
+                                    int32_t* head_len_out, int32_t* dropped, Check ck,
+                                    int32_t* status, hipStream_t s) {
+    const unsigned HC = (unsigned)(c.L * c.R * c.H);
+    if (HC == 0) return hipSuccess;
+    hipLaunchKernelGGL((page_retain_kernel<256, true>), dim3(HC), dim3(256), 0, s, c,
+                       static_cast<const uint32_t*>(scores), kind == BKV_SCORE_F32 ? 1 : 0,
+                       stride, 0, budget, keep_pages, head_table_out, head_len_out, dropped, ck,
+                       status);
     return hipGetLastError();
 }
 

@@ -52,8 +52,9 @@ __global__ __launch_bounds__(kThreads) void random_score_kernel(
     const HeadIdx x = rows == BKV_ROWS_PER_REQUEST        ? HeadIdx{0, row, 0}
                       : rows == BKV_ROWS_PER_LAYER_REQUEST ? HeadIdx{row / c.R, row % c.R, 0}
                                                            : split_hc(c, row);
-    if (!request_ok(c, x.layer, x.req, ck, status)) return;
-    const int N = c.seq_len[x.req];
+    const int hc = rows == BKV_ROWS_PER_HEAD ? row : -1;
+    if (!request_ok(c, x.layer, x.req, hc, ck, status)) return;
+    const int N = slot_count(c, hc, x.req);
     const int P = c.prompt_len[x.req];
     const int g = blockIdx.y * kThreads + threadIdx.x;  // counter word 0: slot group
     const int n0 = g * 4;
@@ -93,8 +94,8 @@ __global__ __launch_bounds__(kThreads) void random_evict_kernel(
 
     const int hc = blockIdx.x;
     const HeadIdx x = split_hc(c, hc);
-    if (!request_ok(c, x.layer, x.req, ck, status)) return;
-    const int N = c.seq_len[x.req];
+    if (!request_ok(c, x.layer, x.req, hc, ck, status)) return;
+    const int N = slot_count(c, hc, x.req);
     const int P = c.prompt_len[x.req];
     const int tid = threadIdx.x;
     int32_t* keep_row = keep_out ? keep_out + (size_t)hc * B : nullptr;
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void random_evict_kernel(
     const int m = N - P, k = B - P;
     if (k == 0) return;  // only the prompt survives, and it does not move
     const int nb = (N + kBlock - 1) / kBlock;
-    const int32_t* bt = c.block_table + (size_t)x.req * c.max_blocks;
+    const int32_t* bt = table_row(c, hc, x.req);
     for (int i = tid; i < nb; i += kThreads) s_bt[i] = bt[i];
     // kept candidate r -> its slot, after the stride keys
     select_and_move<kThreads, 8>(c, x.layer, x.head, 1, P, B, m, s_key,

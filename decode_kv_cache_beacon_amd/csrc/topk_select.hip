@@ -41,8 +41,9 @@ __global__ __launch_bounds__(kThreads) void topk_select_kernel(CacheView c,
 
     const int unit = blockIdx.x;  // head-cache, or (layer, request) when shared
     const HeadIdx x = shared ? HeadIdx{unit / c.R, unit % c.R, 0} : split_hc(c, unit);
-    if (!request_ok(c, x.layer, x.req, ck, status)) return;
-    const int N = c.seq_len[x.req];
+    const int hc = shared ? -1 : unit;
+    if (!request_ok(c, x.layer, x.req, hc, ck, status)) return;
+    const int N = slot_count(c, hc, x.req);
     const int P = c.prompt_len[x.req];
     int32_t* out = keep + (size_t)unit * B;
     const int tid = threadIdx.x;

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define BKV_ABI_VERSION 7
+#define BKV_ABI_VERSION 8
 
 typedef void* bkv_stream_t; /* hipStream_t */
 
@@ -87,6 +87,8 @@ enum { BKV_SELECT_BEACON = 0, BKV_SELECT_RANDOM = 1 };   /* selector of bkv_evic
 /* Row layout of a score buffer: one row per head-cache (hc), per (layer,
  * request) (row layer * n_requests + r), or per request (row r). */
 enum { BKV_ROWS_PER_HEAD = 0, BKV_ROWS_PER_LAYER_REQUEST = 1, BKV_ROWS_PER_REQUEST = 2 };
+/* bkv_pass_args.page_retention */
+enum { BKV_PAGES_OFF = 0, BKV_PAGES_PER_REQUEST = 1, BKV_PAGES_PER_HEAD = 2 };
 
 #define BKV_MAX_BEACONS 256
 #define BKV_MAX_CANDIDATES 32768 /* largest score_stride bkv_topk_select accepts */
@@ -106,7 +108,19 @@ enum { BKV_ROWS_PER_HEAD = 0, BKV_ROWS_PER_LAYER_REQUEST = 1, BKV_ROWS_PER_REQUE
  * pool address must be 16-byte aligned.  A request holds at most
  * max_blocks * block_size <= 32768 slots (the kernels stage a request's block
  * table in LDS); n_layers * n_requests * n_kv_heads and num_blocks must fit
- * in int32.  Violations return BKV_ERR_INVALID before anything is enqueued. */
+ * in int32.  Violations return BKV_ERR_INVALID before anything is enqueued.
+ *
+ * Per-head page tables (head_block_table and head_seq_len, both set or both
+ * NULL; bkv_page_retain_heads writes them): head-cache
+ * hc = (layer * n_requests + r) * n_kv_heads + h then reads its slots through
+ * row hc of head_block_table and has head_seq_len[hc] of them, in place of
+ * the request's block_table row and seq_len (prompt_len stays per request).
+ * The kernels then check each head-cache's own row and length, so a bad
+ * block id or length skips that head-cache only.  Selections shared by the
+ * heads of a request (bkv_topk_select_shared, shared keep lists of
+ * bkv_kv_compact, bkv_page_retain, draw rows per (layer, request) or per
+ * request, shared_positions in a pass) are refused with BKV_ERR_INVALID on
+ * such a cache. */
 typedef struct bkv_cache {
     int32_t n_layers;
     int32_t n_requests;
@@ -120,6 +134,9 @@ typedef struct bkv_cache {
     const int32_t* block_table;   /* device [n_requests][max_blocks] */
     const int32_t* seq_len;       /* device [n_requests] N: valid slots [0, N) */
     const int32_t* prompt_len;    /* device [n_requests] P: prompt slots [0, P) */
+    const int32_t* head_block_table; /* nullable device [n_layers][n_requests][n_kv_heads]
+                                        [max_blocks] per-head page tables */
+    const int32_t* head_seq_len;     /* nullable device [n_layers][n_requests][n_kv_heads] */
 } bkv_cache;
 
 /* ABI version of the loaded library (BKV_ABI_VERSION when it was built). */
@@ -262,6 +279,33 @@ int32_t bkv_page_retain(const bkv_cache* cache, const void* scores, int32_t scor
                         int32_t* keep_pages, int32_t* block_table_out, int32_t* seq_len_out,
                         int32_t* freed_blocks, int32_t* status, bkv_stream_t stream);
 
+/* Page retention per head-cache (the survey's block-granular retention with
+ * per-head block tables; Random Attention article, section "发现二": blocks of
+ * up to 64 tokens keep accuracy, and the heads' independent selections are
+ * what the common-position result is measured against).  Every head-cache hc
+ * selects its own pages exactly as bkv_page_retain selects a request's, from
+ * its own score row scores[hc][:] (BKV_ROWS_PER_HEAD; f32 beacon scores or
+ * u32 draws) and over its own pages: the cache's head_block_table row hc and
+ * head_seq_len[hc] when the cache has them, else its request's block_table
+ * row and seq_len.  No K/V row moves.  Outputs per head-cache, written for
+ * every head-cache that passes its checks (a failing one is untouched):
+ *   keep_pages int32 [HC][budget / 16]: kept page indices ascending, -1 padded;
+ *   head_table_out int32 [HC][max_blocks]: entry i < kept = the block of the
+ *     i-th kept page, entries [kept, npages) = -1, the rest untouched (it may
+ *     be the cache's own head_block_table);
+ *   head_seq_len_out int32 [HC]: the new slot count (may be head_seq_len);
+ *   dropped_blocks int32 [HC][max_blocks]: the blocks of the head-cache's
+ *     dropped pages in page order, then -1.  A block id is shared by every
+ *     layer and head of its request, so the caller frees a block once no
+ *     head-cache's row holds it any more (for example with a count of the
+ *     rows holding each block).
+ * To read the cache through the new rows, pass head_table_out and
+ * head_seq_len_out as the cache's head_block_table and head_seq_len. */
+int32_t bkv_page_retain_heads(const bkv_cache* cache, const void* scores, int32_t score_kind,
+                              int32_t score_stride, int32_t budget, int32_t* keep_pages,
+                              int32_t* head_table_out, int32_t* head_seq_len_out,
+                              int32_t* dropped_blocks, int32_t* status, bkv_stream_t stream);
+
 /* Decode attention over the (compacted) cache: the step every selector hands
  * its cache to (Random Attention article, section "发现四": the selectors share
  * the attention kernels and the paging).  For every head-cache hc and query
@@ -287,15 +331,20 @@ typedef struct bkv_pass_args {
                                   random draws one row); keep lists then have
                                   n_layers * n_requests rows, and so does the random
                                   selector's score buffer */
-    int32_t page_retention;    /* 1: bkv_page_retain replaces selection and compaction
-                                  (budget a multiple of 16, shared_positions 0,
-                                  pos_ids NULL); keep lists are the kept pages
-                                  [n_requests][budget / 16], the random selector
-                                  draws one row per request, and the three outputs
-                                  below are required */
-    int32_t* block_table_out;  /* page retention: [n_requests][max_blocks], may alias */
-    int32_t* seq_len_out;      /* page retention: [n_requests], may alias */
-    int32_t* freed_blocks;     /* page retention: [n_requests][max_blocks] */
+    int32_t page_retention;    /* BKV_PAGES_PER_REQUEST: bkv_page_retain replaces
+                                  selection and compaction (budget a multiple of 16,
+                                  shared_positions 0, pos_ids NULL); keep lists are the
+                                  kept pages [n_requests][budget / 16], the random
+                                  selector draws one row per request, and the three
+                                  outputs below are required.  BKV_PAGES_PER_HEAD:
+                                  bkv_page_retain_heads instead, with keep lists
+                                  [HC][budget / 16], per-head draw rows and the outputs
+                                  below per head-cache */
+    int32_t* block_table_out;  /* page retention: [n_requests][max_blocks] (per head:
+                                  [HC][max_blocks]), may alias */
+    int32_t* seq_len_out;      /* page retention: [n_requests] ([HC]), may alias */
+    int32_t* freed_blocks;     /* page retention: [n_requests][max_blocks] (per head:
+                                  the dropped blocks, [HC][max_blocks]) */
     /* beacon selector */
     int32_t n_beacons;         /* K */
     int32_t T, G;              /* buffered decode steps, query heads per KV head */

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(bk.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -37,7 +37,7 @@ def test_binding_constants_match_the_header():
 
 
 def test_version_and_status_strings():
-    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 7
+    assert bk.bkv_abi_version() == bk.BKV_ABI_VERSION == 8
     for code in range(0, 10):
         s = bk.bkv_status_string(code)
         assert s and s != "unknown status code"
@@ -183,6 +183,62 @@ def test_page_retain_validation():
     assert call(bt=None) == bk.BKV_ERR_NULL
     assert call(fr=None) == bk.BKV_ERR_NULL
     assert call(sl=FAKE + 2) == bk.BKV_ERR_INVALID
+
+
+def test_per_head_tables_validation():
+    """Per-head page tables come as an aligned pair, and the calls that share
+    one selection across a request's heads refuse a cache read through them."""
+    assert _score(_cache(head_block_table=FAKE)) == bk.BKV_ERR_INVALID        # without lengths
+    assert _score(_cache(head_seq_len=FAKE)) == bk.BKV_ERR_INVALID            # without rows
+    assert _score(_cache(head_block_table=FAKE + 2, head_seq_len=FAKE)) == bk.BKV_ERR_INVALID
+    hc = _cache(head_block_table=FAKE, head_seq_len=FAKE)
+    sh = bk._lib.bkv_topk_select_shared
+    assert sh(ctypes.byref(hc), FAKE, 0, 160, 8, 64, FAKE, None, None) == bk.BKV_ERR_INVALID
+    cmp_ = bk._lib.bkv_kv_compact
+    assert cmp_(ctypes.byref(hc), FAKE, 64, 1, None, 0, None, None) == bk.BKV_ERR_INVALID
+    rnd = bk._lib.bkv_random_score
+    for rows in (bk.BKV_ROWS_PER_LAYER_REQUEST, bk.BKV_ROWS_PER_REQUEST):
+        assert rnd(ctypes.byref(hc), 1, FAKE, FAKE, rows, FAKE, 160, None, None) == \
+            bk.BKV_ERR_INVALID
+    pr = bk._lib.bkv_page_retain
+    assert pr(ctypes.byref(hc), FAKE, 0, 160, bk.BKV_ROWS_PER_HEAD, 64, FAKE, FAKE, FAKE, FAKE,
+              None, None) == bk.BKV_ERR_INVALID
+    a = bk.bkv_pass_args()
+    a.selector, a.budget = bk.BKV_SELECT_RANDOM, 64
+    n = ctypes.c_size_t(0)
+    ws = bk._lib.bkv_workspace_size
+    assert ws(ctypes.byref(hc), ctypes.byref(a), ctypes.byref(n)) == 0
+    a.shared_positions = 1
+    assert ws(ctypes.byref(hc), ctypes.byref(a), ctypes.byref(n)) == bk.BKV_ERR_INVALID
+    a.shared_positions, a.page_retention = 0, bk.BKV_PAGES_PER_REQUEST
+    assert ws(ctypes.byref(hc), ctypes.byref(a), ctypes.byref(n)) == bk.BKV_ERR_INVALID
+    a.page_retention = bk.BKV_PAGES_PER_HEAD   # per-head pages: draws and page lists per head
+    assert ws(ctypes.byref(hc), ctypes.byref(a), ctypes.byref(n)) == 0
+    HC = 2 * 3 * 8
+    assert HC * 160 * 4 + HC * 4 * 4 <= n.value <= HC * 160 * 4 + HC * 4 * 4 + 512
+    a.page_retention = 3
+    assert ws(ctypes.byref(hc), ctypes.byref(a), ctypes.byref(n)) == bk.BKV_ERR_INVALID
+
+
+def test_page_retain_heads_validation():
+    c = _cache()
+    f = bk._lib.bkv_page_retain_heads
+    ok = dict(scores=FAKE, kind=0, stride=160, budget=64, keep=FAKE, bt=FAKE, sl=FAKE, dr=FAKE)
+
+    def call(cache=c, **kw):
+        a = dict(ok, **kw)
+        return f(ctypes.byref(cache), a["scores"], a["kind"], a["stride"], a["budget"],
+                 a["keep"], a["bt"], a["sl"], a["dr"], None, None)
+
+    assert call(budget=40) == bk.BKV_ERR_INVALID          # not a whole number of pages
+    assert call(budget=0) == bk.BKV_ERR_INVALID
+    assert call(kind=2) == bk.BKV_ERR_INVALID
+    assert call(stride=0) == bk.BKV_ERR_INVALID
+    assert call(scores=None) == bk.BKV_ERR_NULL
+    assert call(bt=None) == bk.BKV_ERR_NULL
+    assert call(dr=None) == bk.BKV_ERR_NULL
+    assert call(sl=FAKE + 2) == bk.BKV_ERR_INVALID
+    assert call(cache=_cache(head_dim=64)) == bk.BKV_ERR_UNSUPPORTED
 
 
 def test_shared_select_validation():
