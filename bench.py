@@ -986,9 +986,65 @@ def main():
                           "page_retain_gbps": round(pbytes / (kms_["page_retain"] * 1e-3) / 1e9, 1)}
         pages["note"] = ("whole 16-slot pages kept once per request for every layer and head; "
                          "the block table is rewritten in place and no K/V row moves")
-        result["page_retention"] = pages
         cache.block_table.copy_(bt0)
         cache.seq_len.copy_(seq0)
+
+        # per-head pages: every head-cache keeps its own pages in its own row of
+        # a per-head page table (rewritten in place).  A head-cache's tiles of a
+        # block are its own, so between passes (untimed) each one takes the
+        # blocks it dropped back as its tail pages, with the keys they hold
+        L_ = wl.n_layers
+        hrow0 = bt0.repeat_interleave(H, 0).repeat(L_, 1).contiguous()
+        hlen0 = seq0.repeat_interleave(H).repeat(L_).contiguous()
+        hcache = bk.PagedCache(cache.k_pools, cache.v_pools, cache.block_table, cache.seq_len,
+                               cache.prompt_len, head_block_table=hrow0.clone(),
+                               head_seq_len=hlen0.clone())
+        kp_h = torch.zeros((HC, Bp), dtype=torch.int32, device=dev)
+        dropped = torch.zeros((HC, cache.max_blocks), dtype=torch.int32, device=dev)
+        uh = torch.zeros((HC, stride), dtype=torch.int32, device=dev)
+        per_head = {}
+        for sel in ("beacon", "random"):
+            n_ev = 4 if sel == "beacon" else 3
+            runs = []
+            for s in range(args.warmup + args.steps):
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+                outs = (hcache.head_block_table, hcache.head_seq_len, dropped)
+                if sel == "beacon":
+                    bk.bkv_evict_pass(hcache, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b,
+                                      counts=c, window=W, bonus=wl.bonus, scores_out=scores,
+                                      keep_out=kp_h, score_stride=stride, status=status,
+                                      check=False, timing_events=ev, page_retention=outs,
+                                      page_heads=True)
+                else:
+                    pss.fill_(s + 5000)
+                    bk.bkv_evict_pass(hcache, bk.BKV_SELECT_RANDOM, B, seed=wl.seed,
+                                      request_ids=rid, pass_idx=pss, scores_out=uh,
+                                      keep_out=kp_h, score_stride=stride, status=status,
+                                      check=False, timing_events=ev, page_retention=outs,
+                                      page_heads=True)
+                if s >= args.warmup:
+                    runs.append(ev)
+                hcache.head_block_table[:, Bp:npages] = dropped[:, :npages - Bp]
+                hcache.head_seq_len.copy_(hlen0)
+            torch.cuda.synchronize()
+            bk.check_status(status, f"per-head page-retention {sel} passes")
+            kn_ = (["beacon_update", "beacon_score"] if sel == "beacon" else ["random_score"]) + \
+                ["page_retain"]
+            tpass = sum(e[0].elapsed_time(e[-1]) for e in runs) / len(runs)
+            kms_ = {n: round(sum(e[i].elapsed_time(e[i + 1]) for e in runs) / len(runs), 4)
+                    for i, n in enumerate(kn_)}
+            pbytes = HC * (stride * 4 + 2 * cache.max_blocks * 4 + Bp * 4 + 4)
+            per_head[sel] = {"passes_per_s": round(1000.0 / tpass, 3), "ms": round(tpass, 4),
+                             "kernel_ms": kms_,
+                             "page_retain_algorithmic_bytes": int(pbytes),
+                             "page_retain_gbps": round(pbytes / (kms_["page_retain"] * 1e-3) / 1e9,
+                                                       1)}
+        per_head["note"] = ("whole 16-slot pages kept per head-cache from its own scores, each "
+                            "head-cache's row of a per-head page table rewritten in place; no "
+                            "K/V row moves")
+        pages["per_head"] = per_head
+        result["page_retention"] = pages
+        del hcache, kp_h, dropped, uh
 
     # beacon forgetting: the maintenance kernel with a count cap (moving
     # average once a row is full), timed alone on the same queries and state
