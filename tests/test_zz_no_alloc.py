@@ -2,8 +2,9 @@
 bkv_evict_pass with a workspace: the same kernels on the same inputs, so every
 output must match byte for byte -- beacons, counts, assignments, the K/V pools,
 position ids, and with page retention the block table, lengths and released
-blocks.  Two calls in a row for every pass kind, the second on a smaller
-cache, so the second call runs over the scratch the first one left behind."""
+blocks (per request, or the per-head rows, lengths and dropped blocks).  Two
+calls in a row for every pass kind, the second on a smaller cache, so the
+second call runs over the scratch the first one left behind."""
 import numpy as np
 import pytest
 import torch
@@ -36,7 +37,8 @@ def say(*a):
 # prompt and tail pages; the second request of the second shape fits the budget)
 SHAPES = [(2, 3, 2, [576, 541, 400], [200, 333, 100]),
           (1, 2, 2, [560, 330], [120, 64])]
-MODES = ["beacon", "beacon_separate", "random", "random_shared", "beacon_pages"]
+MODES = ["beacon", "beacon_separate", "random", "random_shared", "beacon_pages",
+         "beacon_head_pages"]
 
 
 class Run:
@@ -54,11 +56,18 @@ class Run:
         self.bt = self.cache.block_table.clone()
         self.seq = self.cache.seq_len.clone()
         self.freed = torch.full((R, self.cache.max_blocks), -5, dtype=torch.int32).cuda()
+        # per-head page tables, starting from the request rows
+        H, L = self.cache.n_kv_heads, self.cache.n_layers
+        self.hbt = self.bt.repeat_interleave(H, 0).repeat(L, 1).contiguous()
+        self.hseq = self.seq.repeat_interleave(H).repeat(L).contiguous()
+        self.hfreed = torch.full((HC, self.cache.max_blocks), -5, dtype=torch.int32).cuda()
+        self.hbt_in = self.hbt.cpu().numpy().copy()
         self.st = torch.zeros(1, dtype=torch.int32).cuda()
 
     def outputs(self):
         torch.cuda.synchronize()
-        out = [self.b, self.c, self.assign, self.pos, self.bt, self.seq, self.freed, self.st]
+        out = [self.b, self.c, self.assign, self.pos, self.bt, self.seq, self.freed, self.st,
+               self.hbt, self.hseq, self.hfreed]
         out += list(self.cache.k_pools) + list(self.cache.v_pools)
         return [(t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy().copy()
                 for t in out]
@@ -69,6 +78,9 @@ def run_pass(fn, run, mode, q, B, rid, pss, extra):
     kw = dict(status=run.st, **extra)
     if mode == "beacon_pages":
         kw["page_retention"] = (run.bt, run.seq, run.freed)
+    elif mode == "beacon_head_pages":
+        kw["page_retention"] = (run.hbt, run.hseq, run.hfreed)
+        kw["page_heads"] = True
     else:
         kw["pos_ids"] = run.pos
     if beacon:
@@ -101,12 +113,15 @@ def test_noalloc_pass_matches_the_workspace_pass(mode):
         r_out, m_out = ref.outputs(), mine.outputs()
         assert int(r_out[7][0]) == 0 and int(m_out[7][0]) == 0, (r_out[7], m_out[7])
         names = ["beacons", "counts", "assign", "pos_ids", "block_table", "seq_len", "freed",
-                 "status"] + [f"k{layer}" for layer in range(L)] + [f"v{layer}" for layer in range(L)]
+                 "status", "head_table", "head_seq_len", "dropped"] + \
+            [f"k{layer}" for layer in range(L)] + [f"v{layer}" for layer in range(L)]
         for name, x, y in zip(names, r_out, m_out):
             assert x.shape == y.shape and np.array_equal(x.view(np.uint8), y.view(np.uint8)), \
                 (mode, call, name)
         if mode == "beacon_pages":
             assert not np.array_equal(r_out[4], batch.block_table.numpy()), "no page moved"
+        elif mode == "beacon_head_pages":
+            assert not np.array_equal(r_out[8], ref.hbt_in), "no page moved"
         else:
-            assert not np.array_equal(r_out[8].view(np.uint16), synth.bits(batch.k_pools[0])), \
+            assert not np.array_equal(r_out[11].view(np.uint16), synth.bits(batch.k_pools[0])), \
                 "no row moved"
