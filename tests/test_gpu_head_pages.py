@@ -258,3 +258,56 @@ def test_evict_pass_per_head_pages(selector):
                            head_seq_len=torch.from_numpy(lens1).cuda())
     b1, c1 = b.cpu().numpy().copy(), c.cpu().numpy().copy()
     run(hcache, 256, rows1, lens1, b1, c1, 12)
+
+
+def test_per_head_tables_skip_only_the_failing_head_cache():
+    """With per-head page tables a device check fails for one head-cache only:
+    a block id outside the pool in one row and a length past the table in
+    another.  Those two head-caches are left untouched by every kernel of a
+    per-head page pass (beacons, counts, rows, lengths); the others match a
+    pass over the same cache without the faults."""
+    say("head pages: per-head skip")
+    wl = small(n_layers=1, n_requests=2, n_kv_heads=4, n_beacons=64, budget=256, prompt_len=64,
+               seq_len=400, steps=4)
+    batch = synth.make_batch(wl)
+    N, P, B = [400, 333], [64, 40], 256
+    cache = device_cache(batch, N, P)
+    HC, M = cache.n_head_caches, cache.max_blocks
+    bt = batch.block_table.numpy().copy()
+    rows0, lens0 = _head_rows(cache, bt, N)
+    bad_block, bad_len = 1, 6                    # head-cache 1: bad block id; 6: bad length
+    faulty_rows, faulty_lens = rows0.copy(), lens0.copy()
+    faulty_rows[bad_block, 3] = wl.num_blocks + 9
+    faulty_lens[bad_len] = M * 16 + 5
+    q = batch.queries.cuda()
+    outs = {}
+    for name, rows, lens in (("clean", rows0, lens0), ("faulty", faulty_rows, faulty_lens)):
+        hc_ = bk.PagedCache(cache.k_pools, cache.v_pools, cache.block_table, cache.seq_len,
+                            cache.prompt_len, head_block_table=torch.from_numpy(rows).cuda(),
+                            head_seq_len=torch.from_numpy(lens).cuda())
+        b, c = batch.beacons.cuda(), batch.counts.cuda()
+        kp, _, _, dr = _outputs(HC, M, B)
+        st = bk.bkv_evict_pass(hc_, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                               keep_out=kp, page_retention=(hc_.head_block_table,
+                                                            hc_.head_seq_len, dr),
+                               page_heads=True, check=False)
+        torch.cuda.synchronize()
+        outs[name] = (int(st.item()), b.cpu().numpy(), c.cpu().numpy(),
+                      hc_.head_block_table.cpu().numpy(), hc_.head_seq_len.cpu().numpy(),
+                      kp.cpu().numpy())
+    st_c, b_c, c_c, r_c, l_c, k_c = outs["clean"]
+    st_f, b_f, c_f, r_f, l_f, k_f = outs["faulty"]
+    assert st_c == 0
+    assert st_f == (1 << bk.BKV_ERR_BLOCK_TABLE) | (1 << bk.BKV_ERR_LENGTH), st_f
+    b0, c0 = batch.beacons.numpy(), batch.counts.numpy()
+    for hc in range(HC):
+        if hc in (bad_block, bad_len):
+            assert np.array_equal(b_f[hc].view(np.int32), b0[hc].view(np.int32)), hc
+            assert np.array_equal(c_f[hc], c0[hc]), hc
+            assert np.array_equal(r_f[hc], faulty_rows[hc]) and l_f[hc] == faulty_lens[hc], hc
+            assert np.all(k_f[hc] == -7), hc
+        else:
+            assert np.array_equal(b_f[hc].view(np.int32), b_c[hc].view(np.int32)), hc
+            assert np.array_equal(c_f[hc], c_c[hc]), hc
+            assert np.array_equal(r_f[hc], r_c[hc]) and l_f[hc] == l_c[hc], hc
+            assert np.array_equal(k_f[hc], k_c[hc]), hc
