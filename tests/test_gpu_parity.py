@@ -894,7 +894,7 @@ def test_evict_pass_tiny_one_shot():
     _pass_case(synth.WORKLOADS["tiny"], N=[4096], P=[512], B=1024, selector="beacon")
 
 
-@pytest.mark.parametrize("case", ["k256", "k64-rescue", "k128-sparse", "k256-shared"])
+@pytest.mark.parametrize("case", ["k256", "k64-rescue", "k128-sparse", "k256-shared", "k5-edges"])
 def test_evict_pass_split_scoring(case):
     """More candidates and keep entries than a fused kernel holds, and few
     head-caches: the pass splits each head-cache's keys over several
@@ -919,10 +919,16 @@ def test_evict_pass_split_scoring(case):
             k[batch.block_table[0, 500]] *= 40.0   # a late block of huge keys, request 0
             batch.k_pools[0] = k.to(torch.bfloat16)
         _pass_case(wl, N, P, B, selector="beacon", mutate=mutate)
-    else:
+    elif case == "k128-sparse":
         wl = small(n_layers=1, n_requests=3, n_kv_heads=2, n_beacons=128, budget=B,
                    seq_len=max(N), steps=2, prewarm=False)
         _pass_case(wl, N, P, B, selector="beacon")
+    else:
+        # K = 5 (one 32-row block, so some row groups hold no beacons), an
+        # empty request, and one whose 10 candidates sit in a single tile
+        wl = small(n_layers=1, n_requests=3, n_kv_heads=2, n_beacons=5, budget=B,
+                   seq_len=max(N), steps=2)
+        _pass_case(wl, [12288, 0, 4100], [0, 0, 4090], B, selector="beacon")
 
 
 def test_evict_pass_k256_group8():
