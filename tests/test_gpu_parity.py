@@ -1027,6 +1027,88 @@ def test_evict_pass_skips_invalid_request_entirely(mode):
     assert any(not np.array_equal(k_in[0][blk], k_out[0][blk]) for blk in btn[0])
 
 
+@pytest.mark.parametrize("mode", ["split", "head_pages"])
+def test_split_and_head_page_passes_replay_from_a_hip_graph(mode):
+    """The same for a pass whose scoring splits each head-cache's keys over
+    several workgroups (its partial log-sum-exps in the workspace) and for a
+    per-head page pass rewriting per-head rows in place: three replays from
+    restored inputs, each byte for byte the eager pass."""
+    say("graph replay", mode)
+    if mode == "split":
+        N, P, B = [12288, 5000, 9001], [512, 100, 0], 4096
+    else:
+        N, P, B = [576, 541, 400], [200, 333, 100], 384
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=2, n_beacons=64, budget=B,
+               prompt_len=max(P), seq_len=max(N), steps=4)
+    batch = synth.make_batch(wl)
+    cache = device_cache(batch, N, P)
+    HC, S, M = cache.n_head_caches, cache.max_slots, cache.max_blocks
+    q = batch.queries.cuda()
+    b0, c0 = batch.beacons.cuda(), batch.counts.cuda()
+    k0 = [k.clone() for k in cache.k_pools]
+    v0 = [v.clone() for v in cache.v_pools]
+    b, c = b0.clone(), c0.clone()
+    sc = torch.zeros((HC, S)).cuda()
+    st = torch.zeros(1, dtype=torch.int32).cuda()
+    ws = torch.empty(4 << 20, dtype=torch.uint8).cuda()
+    H, L = cache.n_kv_heads, cache.n_layers
+    hrow0 = cache.block_table.repeat_interleave(H, 0).repeat(L, 1).contiguous()
+    hlen0 = cache.seq_len.repeat_interleave(H).repeat(L).contiguous()
+    hrow, hlen = hrow0.clone(), hlen0.clone()
+    dropped = torch.zeros((HC, M), dtype=torch.int32).cuda()
+    pc = cache
+    if mode == "head_pages":
+        pc = bk.PagedCache(cache.k_pools, cache.v_pools, cache.block_table, cache.seq_len,
+                           cache.prompt_len, head_block_table=hrow, head_seq_len=hlen)
+        keep = torch.zeros((HC, B // 16), dtype=torch.int32).cuda()
+    else:
+        keep = torch.zeros((HC, B), dtype=torch.int32).cuda()
+
+    def restore():
+        b.copy_(b0)
+        c.copy_(c0)
+        hrow.copy_(hrow0)
+        hlen.copy_(hlen0)
+        for dst, src in zip(cache.k_pools + cache.v_pools, k0 + v0):
+            dst.copy_(src)
+
+    def run():
+        kw = dict(page_retention=(hrow, hlen, dropped), page_heads=True) \
+            if mode == "head_pages" else {}
+        bk.bkv_evict_pass(pc, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
+                          scores_out=sc, keep_out=keep, status=st, check=False, workspace=ws,
+                          **kw)
+
+    run()                                   # eager reference
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    outs = (b, c, sc, keep, hrow, hlen, dropped, *cache.k_pools, *cache.v_pools)
+    ref = [t.clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm-up on the capture stream
+        restore()
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    restore()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(3):
+        restore()
+        if mode == "head_pages":
+            dropped.fill_(-3)               # every entry is written again
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        for i, (x, y) in enumerate(zip(outs, ref)):
+            assert torch.equal(x.view(torch.uint8) if x.dtype == torch.bfloat16 else x,
+                               y.view(torch.uint8) if y.dtype == torch.bfloat16 else y), (rep, i)
+
+
 @pytest.mark.parametrize("mode", ["beacon", "shared", "random"])
 def test_evict_pass_replays_from_a_hip_graph(mode):
     """The pass allocates nothing and sets no memory, so it can be captured: a
