@@ -73,7 +73,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct PassLayout {
     int stride;
     int parts;  // beacon scoring: workgroups per head-cache (1: unsplit)
-    size_t scores_off, keep_off, part_off, total;
+    size_t scores_off, keep_off, part_off, pkey_off, total;
 };
 
 // Row layout of the random selector's draws in a pass: per head-cache, per
@@ -145,7 +145,7 @@ int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     size_t off = 0;
     L->stride = stride;
     L->parts = score_parts(v, a, stride);
-    L->scores_off = L->keep_off = L->part_off = 0;
+    L->scores_off = L->keep_off = L->part_off = L->pkey_off = 0;
     if (!a->scores_out) {
         L->scores_off = off;
         off = round_up(off + score_rows(v, a) * (size_t)stride * 4, 256);
@@ -157,6 +157,10 @@ int32_t pass_layout(const CacheView& v, const bkv_pass_args* a, PassLayout* L) {
     if (L->parts > 1) {  // the parts' log-sum-exps
         L->part_off = off;
         off = round_up(off + (size_t)head_caches(v) * L->parts * BKV_MAX_BEACONS * 4, 256);
+    }
+    if (a->page_retention == BKV_PAGES_PER_REQUEST && a->selector == BKV_SELECT_BEACON) {
+        L->pkey_off = off;  // the requests' page keys
+        off = round_up(off + (size_t)v.R * v.max_blocks * 4, 256);
     }
     L->total = off;
     return BKV_OK;
@@ -257,7 +261,7 @@ int32_t run_pass(const CacheView& v, const PassLayout& L, const bkv_pass_args* a
         else if (he == hipSuccess && pages)
             he = launch_page_retain(v, sc, BKV_SCORE_F32, L.stride, BKV_ROWS_PER_HEAD, a->budget,
                                     keep, a->block_table_out, a->seq_len_out, a->freed_blocks,
-                                    all, status, s);
+                                    reinterpret_cast<uint32_t*>(ws + L.pkey_off), all, status, s);
         else if (he == hipSuccess)  // shared: the largest of the H per-head scores
             he = launch_topk_select(v, sc, BKV_SCORE_F32, L.stride, v.H, shared, a->budget, keep,
                                     all, status, s);
@@ -272,7 +276,7 @@ int32_t run_pass(const CacheView& v, const PassLayout& L, const bkv_pass_args* a
         else if (he == hipSuccess && pages)
             he = launch_page_retain(v, sc, BKV_SCORE_U32, L.stride, BKV_ROWS_PER_REQUEST,
                                     a->budget, keep, a->block_table_out, a->seq_len_out,
-                                    a->freed_blocks, all, status, s);
+                                    a->freed_blocks, nullptr, all, status, s);
         else if (he == hipSuccess)  // shared: one draw row per (layer, request)
             he = launch_topk_select(v, sc, BKV_SCORE_U32, L.stride, 1, shared, a->budget, keep,
                                     all, status, s);
@@ -466,7 +470,7 @@ int32_t bkv_page_retain(const bkv_cache* cache, const void* scores, int32_t scor
         return BKV_ERR_INVALID;
     return hip_status(launch_page_retain(v, scores, score_kind, score_stride, score_rows, budget,
                                          keep_pages, block_table_out, seq_len_out, freed_blocks,
-                                         Check{budget, score_stride, 1, 1}, status,
+                                         nullptr, Check{budget, score_stride, 1, 1}, status,
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -233,10 +233,12 @@ hipError_t launch_random_evict(const CacheView& c, uint64_t seed, const uint64_t
                                int32_t* status, hipStream_t s);
 hipError_t launch_decode_attention(const CacheView& c, const uint16_t* q, int G, float scale,
                                    float* out, int32_t* status, hipStream_t s);
+// key_ws (nullable, [R][max_blocks] u32): with per-head score rows, the page
+// keys are formed first by one workgroup per (layer, request) into it.
 hipError_t launch_page_retain(const CacheView& c, const void* scores, int kind, int stride,
                               int rows, int budget, int32_t* keep_pages, int32_t* block_table_out,
-                              int32_t* seq_len_out, int32_t* freed, Check ck, int32_t* status,
-                              hipStream_t s);
+                              int32_t* seq_len_out, int32_t* freed, uint32_t* key_ws, Check ck,
+                              int32_t* status, hipStream_t s);
 // Page retention per head-cache: each head-cache keeps budget / 16 pages of
 // its own (its own score row), written to its own page-table row.
 hipError_t launch_page_retain_heads(const CacheView& c, const void* scores, int kind, int stride,

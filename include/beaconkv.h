@@ -279,10 +279,10 @@ int32_t bkv_page_retain(const bkv_cache* cache, const void* scores, int32_t scor
                         int32_t* keep_pages, int32_t* block_table_out, int32_t* seq_len_out,
                         int32_t* freed_blocks, int32_t* status, bkv_stream_t stream);
 
-/* Page retention per head-cache (the survey's block-granular retention with
- * per-head block tables; Random Attention article, section "发现二": blocks of
- * up to 64 tokens keep accuracy, and the heads' independent selections are
- * what the common-position result is measured against).  Every head-cache hc
+/* Page retention per head-cache (block-granular retention with per-head
+ * block tables; Random Attention article, section "发现二": blocks of up to 64
+ * tokens keep accuracy with every head selecting on its own, an independence
+ * the section credits with redundancy across heads).  Every head-cache hc
  * selects its own pages exactly as bkv_page_retain selects a request's, from
  * its own score row scores[hc][:] (BKV_ROWS_PER_HEAD; f32 beacon scores or
  * u32 draws) and over its own pages: the cache's head_block_table row hc and
