@@ -395,7 +395,15 @@ typedef struct bkv_pass_args {
  * aligned to 256 bytes. */
 int32_t bkv_workspace_size(const bkv_cache* cache, const bkv_pass_args* args, size_t* bytes);
 
-/* Runs, on `stream`: (beacon) maintenance -> beacon scoring -> selection ->
+/* One eviction pass at a compression point.  The beacon pass's order --
+ * absorb the buffered queries into the beacons, score every key against
+ * them, keep the budget -- is the mechanism of the BeaconKV explainer,
+ * section 3.2; the random pass is the random-retention rule of the Random
+ * Attention article (section "Random Attention：不判断重要性，只随机保留":
+ * prompt kept, one draw and one top-k per head); both end in the cache
+ * compaction that the article's section "发现四" counts as a cost every
+ * selector shares.
+ * Runs, on `stream`: (beacon) maintenance -> beacon scoring -> selection ->
  * compaction, or (random) random scoring -> selection -> compaction; with
  * page_retention, bkv_page_retain takes the place of the last two.  Scoring,
  * selection and compaction run as one fused kernel where separate_steps
