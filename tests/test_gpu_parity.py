@@ -1027,12 +1027,14 @@ def test_evict_pass_skips_invalid_request_entirely(mode):
     assert any(not np.array_equal(k_in[0][blk], k_out[0][blk]) for blk in btn[0])
 
 
-@pytest.mark.parametrize("mode", ["split", "head_pages"])
+@pytest.mark.parametrize("mode", ["split", "head_pages", "pages"])
 def test_split_and_head_page_passes_replay_from_a_hip_graph(mode):
     """The same for a pass whose scoring splits each head-cache's keys over
-    several workgroups (its partial log-sum-exps in the workspace) and for a
-    per-head page pass rewriting per-head rows in place: three replays from
-    restored inputs, each byte for byte the eager pass."""
+    several workgroups (its partial log-sum-exps in the workspace), for a
+    per-head page pass rewriting per-head rows in place, and for a
+    per-request beacon page pass (its page keys formed in the workspace after
+    a fill kernel zeroes them) rewriting the block table and lengths in place:
+    three replays from restored inputs, each byte for byte the eager pass."""
     say("graph replay", mode)
     if mode == "split":
         N, P, B = [12288, 5000, 9001], [512, 100, 0], 4096
@@ -1056,11 +1058,15 @@ def test_split_and_head_page_passes_replay_from_a_hip_graph(mode):
     hlen0 = cache.seq_len.repeat_interleave(H).repeat(L).contiguous()
     hrow, hlen = hrow0.clone(), hlen0.clone()
     dropped = torch.zeros((HC, M), dtype=torch.int32).cuda()
+    bt0, sl0 = cache.block_table.clone(), cache.seq_len.clone()
+    freed = torch.zeros((cache.n_requests, M), dtype=torch.int32).cuda()
     pc = cache
     if mode == "head_pages":
         pc = bk.PagedCache(cache.k_pools, cache.v_pools, cache.block_table, cache.seq_len,
                            cache.prompt_len, head_block_table=hrow, head_seq_len=hlen)
         keep = torch.zeros((HC, B // 16), dtype=torch.int32).cuda()
+    elif mode == "pages":
+        keep = torch.zeros((cache.n_requests, B // 16), dtype=torch.int32).cuda()
     else:
         keep = torch.zeros((HC, B), dtype=torch.int32).cuda()
 
@@ -1069,12 +1075,17 @@ def test_split_and_head_page_passes_replay_from_a_hip_graph(mode):
         c.copy_(c0)
         hrow.copy_(hrow0)
         hlen.copy_(hlen0)
+        cache.block_table.copy_(bt0)
+        cache.seq_len.copy_(sl0)
         for dst, src in zip(cache.k_pools + cache.v_pools, k0 + v0):
             dst.copy_(src)
 
     def run():
-        kw = dict(page_retention=(hrow, hlen, dropped), page_heads=True) \
-            if mode == "head_pages" else {}
+        kw = {}
+        if mode == "head_pages":
+            kw = dict(page_retention=(hrow, hlen, dropped), page_heads=True)
+        elif mode == "pages":
+            kw = dict(page_retention=(cache.block_table, cache.seq_len, freed))
         bk.bkv_evict_pass(pc, bk.BKV_SELECT_BEACON, B, queries=q, beacons=b, counts=c,
                           scores_out=sc, keep_out=keep, status=st, check=False, workspace=ws,
                           **kw)
@@ -1082,7 +1093,8 @@ def test_split_and_head_page_passes_replay_from_a_hip_graph(mode):
     run()                                   # eager reference
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    outs = (b, c, sc, keep, hrow, hlen, dropped, *cache.k_pools, *cache.v_pools)
+    outs = (b, c, sc, keep, hrow, hlen, dropped, cache.block_table, cache.seq_len, freed,
+            *cache.k_pools, *cache.v_pools)
     ref = [t.clone() for t in outs]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -1100,6 +1112,8 @@ def test_split_and_head_page_passes_replay_from_a_hip_graph(mode):
         restore()
         if mode == "head_pages":
             dropped.fill_(-3)               # every entry is written again
+        if mode == "pages":
+            freed.fill_(-3)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
