@@ -513,6 +513,38 @@ def test_evict_pass_end_to_end(selector, separate):
                separate=separate)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_evict_pass_random_shapes(seed):
+    """A seeded sweep of small shapes beside the hand-picked ones: K, G, T,
+    the layer, request and head counts, the budget, paged or dense pools, a
+    prewarmed or empty beacon state, ragged lengths and prompts per request
+    (some at or under the budget, some prompts equal to it, empty caches),
+    either selector, per head or shared, fused or separate; every output
+    checked against the oracle as in the end-to-end test."""
+    rng = np.random.default_rng(2000 + seed)
+    K = int(rng.choice([1, 7, 32, 33, 64, 100, 128, 200, 256]))
+    G, T = int(rng.choice([1, 2, 4, 8])), int(rng.integers(1, 41))
+    L, R, H = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 3))
+    B = int(rng.choice([64, 128, 256, 384]))
+    S = B + int(rng.integers(1, 300))
+    # request 0 always evicts; the others may be empty, full or anywhere between
+    N = [S] + [0 if u < 0.1 else S if u < 0.4 else int(rng.integers(1, S + 1))
+               for u in rng.random(R - 1)]
+    P = [0 if u < 0.2 else min(n, B) if u < 0.35 else int(rng.integers(0, min(n, B) + 1))
+         for n, u in zip(N, rng.random(R))]
+    selector = "beacon" if seed % 3 else "random"
+    shared, separate = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    paged, prewarm = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    say("random shape", seed, dict(K=K, G=G, T=T, L=L, R=R, H=H, B=B, N=N, P=P, sel=selector,
+                                   shared=shared, separate=separate, paged=paged,
+                                   prewarm=prewarm))
+    wl = small(n_layers=L, n_requests=R, n_kv_heads=H, n_beacons=K, group=G, steps=T,
+               budget=B, prompt_len=max(P), seq_len=S, paged=paged, prewarm=prewarm,
+               seed=30 + seed)
+    _pass_case(wl, N=N, P=P, B=B, selector=selector, seed=5 + seed, shared=shared,
+               separate=separate)
+
+
 @pytest.mark.parametrize("selector,K", [("beacon", 64), ("beacon", 128), ("beacon", 256),
                                         ("random", 128), ("shared", 128), ("shared", 256)])
 def test_fused_pass_matches_separate_steps(selector, K):
