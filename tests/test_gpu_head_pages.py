@@ -192,16 +192,12 @@ def test_page_retain_heads_then_read_through_rows():
         assert np.array_equal(o[:len(kk)], oracle.kv_compact(a, kk)), hc
 
 
-@pytest.mark.parametrize("selector", ["beacon", "random"])
-def test_evict_pass_per_head_pages(selector):
-    """A whole pass with per-head page retention: each head-cache's pages from
-    its own scores (beacon: after maintenance; random: its own draw row),
-    written to per-head rows; then a second pass on the per-head cache."""
-    say("pass head pages", selector)
-    wl = small(n_layers=2, n_requests=3, n_kv_heads=2, n_beacons=64, budget=512, prompt_len=100,
-               seq_len=900, steps=4)
+def _head_page_pass_case(wl, N, P, B, B2, selector):
+    """A whole pass with per-head page retention at budget B, each head-cache's
+    pages from its own scores (beacon: after maintenance; random: its own draw
+    row) written to per-head rows, then a second pass at budget B2 on the
+    cache read through those rows; every output against the oracle."""
     batch = synth.make_batch(wl)
-    N, P, B = [900, 777, 400], [100, 37, 64], 512
     cache = device_cache(batch, N, P)
     L, R, H, M, HC = (cache.n_layers, cache.n_requests, cache.n_kv_heads, cache.max_blocks,
                       cache.n_head_caches)
@@ -257,7 +253,44 @@ def test_evict_pass_per_head_pages(selector):
                            cache.prompt_len, head_block_table=torch.from_numpy(rows1).cuda(),
                            head_seq_len=torch.from_numpy(lens1).cuda())
     b1, c1 = b.cpu().numpy().copy(), c.cpu().numpy().copy()
-    run(hcache, 256, rows1, lens1, b1, c1, 12)
+    run(hcache, B2, rows1, lens1, b1, c1, 12)
+
+
+@pytest.mark.parametrize("selector", ["beacon", "random"])
+def test_evict_pass_per_head_pages(selector):
+    """A whole pass with per-head page retention, then a second pass on the
+    per-head cache."""
+    say("pass head pages", selector)
+    wl = small(n_layers=2, n_requests=3, n_kv_heads=2, n_beacons=64, budget=512, prompt_len=100,
+               seq_len=900, steps=4)
+    _head_page_pass_case(wl, N=[900, 777, 400], P=[100, 37, 64], B=512, B2=256,
+                         selector=selector)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_evict_pass_per_head_pages_random_shapes(seed):
+    """The same over seeded random small shapes: K, G, T, the counts, both
+    budgets (multiples of 16, the second at most the first), lengths on and
+    off page boundaries with empty caches, prompts up to a page under the
+    second budget, paged or dense pools, either selector."""
+    rng = np.random.default_rng(4000 + seed)
+    K = int(rng.choice([1, 33, 64, 128, 256]))
+    G, T = int(rng.choice([1, 4, 8])), int(rng.integers(1, 33))
+    L, R, H = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 3))
+    B = 16 * int(rng.integers(3, 25))
+    B2 = 16 * int(rng.integers(2, B // 16 + 1))
+    S = B + int(rng.integers(1, 300))
+    N = [S] + [0 if u < 0.1 else S if u < 0.4 else int(rng.integers(1, S + 1))
+               for u in rng.random(R - 1)]
+    P = [int(rng.integers(0, max(0, min(n, B2 - 16)) + 1)) for n in N]
+    selector = "beacon" if seed % 2 else "random"
+    paged, prewarm = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    say("random head-page shape", seed, dict(K=K, G=G, T=T, L=L, R=R, H=H, B=B, B2=B2, N=N,
+                                             P=P, sel=selector, paged=paged, prewarm=prewarm))
+    wl = small(n_layers=L, n_requests=R, n_kv_heads=H, n_beacons=K, group=G, steps=T,
+               budget=B, prompt_len=max(P), seq_len=S, paged=paged, prewarm=prewarm,
+               seed=80 + seed)
+    _head_page_pass_case(wl, N=N, P=P, B=B, B2=B2, selector=selector)
 
 
 def test_per_head_tables_skip_only_the_failing_head_cache():

@@ -867,6 +867,32 @@ def test_evict_pass_page_retention(selector):
     _page_pass_case(wl, N=[584, 541, 400], P=[200, 333, 100], B=512, selector=selector)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_evict_pass_page_retention_random_shapes(seed):
+    """Page-retention passes over seeded random small shapes: the budget any
+    multiple of 16, lengths on and off page boundaries (empty caches
+    included), prompts up to a page under the budget, paged or dense pools,
+    either selector; pages, the rewritten table, lengths and released blocks
+    against the oracle."""
+    rng = np.random.default_rng(3000 + seed)
+    K = int(rng.choice([1, 33, 64, 128, 256]))
+    G, T = int(rng.choice([1, 4, 8])), int(rng.integers(1, 33))
+    L, R, H = int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 3))
+    B = 16 * int(rng.integers(2, 25))
+    S = B + int(rng.integers(1, 300))
+    N = [S] + [0 if u < 0.1 else S if u < 0.4 else int(rng.integers(1, S + 1))
+               for u in rng.random(R - 1)]
+    P = [int(rng.integers(0, max(0, min(n, B - 16)) + 1)) for n in N]
+    selector = "beacon" if seed % 2 else "random"
+    paged, prewarm = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    say("random page shape", seed, dict(K=K, G=G, T=T, L=L, R=R, H=H, B=B, N=N, P=P,
+                                        sel=selector, paged=paged, prewarm=prewarm))
+    wl = small(n_layers=L, n_requests=R, n_kv_heads=H, n_beacons=K, group=G, steps=T,
+               budget=B, prompt_len=max(P), seq_len=S, paged=paged, prewarm=prewarm,
+               seed=60 + seed)
+    _page_pass_case(wl, N=N, P=P, B=B, selector=selector, seed=40 + seed)
+
+
 # ------------------------------------------------------------------ decode attention
 def _check_attention(out, q, keys, vals, where):
     ref = oracle.decode_attention(q, keys, vals)
