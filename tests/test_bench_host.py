@@ -35,8 +35,8 @@ def test_algorithmic_bytes_by_hand():
     # compaction: 100 moved rows, K and V each read and written (102400);
     # the keep lists it reads (8 x 8192) are extra
     assert b["kv_compact"] == 102400 and x["kv_compact"] == 65536
-    # the fused kernel: keys once, beacons, moved rows (the survey's
-    # N*d*2 + K*d*4 + 4*M*d*2 per head-cache)
+    # the fused kernel: keys once, beacons, moved rows
+    # (N*d*2 + K*d*4 + 4*M*d*2 per head-cache)
     assert b["beacon_evict"] == 8 * (2112 * 128 * 2 + 128 * 128 * 4) + 4 * 100 * 128 * 2
     assert x["beacon_evict"] == 8 * 5392 + 65536
 
