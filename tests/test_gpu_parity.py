@@ -317,6 +317,45 @@ def test_beacon_update_teacher_forced_adversarial(case, K, G, T, cap):
     assert inexact <= INEXACT_LIMIT, (inexact, worst)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_beacon_update_random_shapes(seed):
+    """Seeded random maintenance shapes beside the hand-picked ones: K on and
+    off the 32-row blocks, G, T (ragged last chunks), the count cap (1
+    included), an empty or prewarmed state and, half the time, rows pushed
+    into near and exact ties.  Teacher-forced against the oracle: every pick
+    its argmax, counts and beacons bit for bit."""
+    rng = np.random.default_rng(5000 + seed)
+    K = int(rng.choice([1, 3, 31, 32, 33, 64, 65, 100, 128, 129, 200, 256]))
+    G, T = int(rng.choice([1, 2, 3, 4, 8])), int(rng.integers(1, 50))
+    cap = int(rng.choice([0, 0, 1, 2, 7, 64]))
+    R, H = int(rng.integers(1, 4)), int(rng.integers(1, 3))
+    prewarm, ties = bool(rng.integers(0, 2)), bool(rng.integers(0, 2)) and K >= 2
+    say("update random shape", seed, dict(K=K, G=G, T=T, cap=cap, R=R, H=H, prewarm=prewarm,
+                                          ties=ties))
+    wl = small(n_layers=1, n_requests=R, n_kv_heads=H, n_beacons=K, group=G, steps=T,
+               prewarm=prewarm, budget=512, prompt_len=100, seq_len=300, seed=90 + seed)
+    batch = synth.make_batch(wl)
+    b, c = batch.beacons.clone(), batch.counts.clone()
+    if ties:
+        _near_tie_rows(b, c, rng)
+    HC = b.shape[0]
+    qd, bd, cd = batch.queries.cuda(), b.cuda(), c.cuda()
+    assign = torch.full((HC, T * G), -1, dtype=torch.int32).cuda()
+    bk.bkv_beacon_update(qd, bd, cd, assign, count_cap=cap)
+    torch.cuda.synchronize()
+    qb = synth.bits(batch.queries)
+    bg, cg, ag = bd.cpu().numpy(), cd.cpu().numpy(), assign.cpu().numpy()
+    inexact = 0
+    for hc in range(HC):
+        ob, oc, gap = oracle.beacon_update_forced(qb[hc], b[hc].numpy(), c[hc].numpy(), ag[hc],
+                                                  cap=cap)
+        assert np.all(np.isfinite(gap)) and gap.max() <= ASSIGN_TOL, (hc, gap.max())
+        inexact += int((gap > 0).sum())
+        assert np.array_equal(oc, cg[hc]), hc
+        assert np.array_equal(ob.view(np.int32), bg[hc].view(np.int32)), hc
+    assert inexact <= INEXACT_LIMIT, inexact
+
+
 # ------------------------------------------------------------------ scoring
 def _score_case(wl, N, P, kill=(), window=64, bonus=1.0, mutate=None):
     batch = synth.make_batch(wl)
@@ -919,6 +958,41 @@ def test_decode_attention_parity(G):
         keys = oracle.gather_paged(k_in[layer], bt[r], h, N[r])
         vals = oracle.gather_paged(v_in[layer], bt[r], h, N[r])
         _check_attention(on[hc], qn[hc], keys, vals, f"G {G} hc {hc} N {N[r]}")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_decode_attention_random_shapes(seed):
+    """Seeded random attention shapes: G from 1 to 8, the layer, request and
+    head counts, lengths from empty through one slot, page boundaries and
+    ragged, paged or dense pools, the default scale or another; every output
+    against the oracle."""
+    rng = np.random.default_rng(6000 + seed)
+    G = int(rng.integers(1, 9))
+    L, R, H = int(rng.integers(1, 3)), int(rng.integers(1, 5)), int(rng.integers(1, 3))
+    S = int(rng.integers(1, 700))
+    N = [S] + [int(rng.choice([0, 1, S, 16 * (S // 16), int(rng.integers(0, S + 1))]))
+               for _ in range(R - 1)]
+    paged = bool(rng.integers(0, 2))
+    scale = [None, 0.05, 0.12][seed % 3]
+    say("attention random shape", seed, dict(G=G, L=L, R=R, H=H, N=N, paged=paged,
+                                             scale=scale))
+    wl = small(n_layers=L, n_requests=R, n_kv_heads=H, group=G, steps=2, seq_len=S,
+               prompt_len=0, budget=512, paged=paged, seed=120 + seed)
+    batch = synth.make_batch(wl)
+    cache = device_cache(batch, N, [0] * R)
+    k_in, v_in = host_pools(cache)
+    bt = batch.block_table.numpy()
+    q = batch.queries[:, -1].contiguous().cuda()
+    out = torch.full((cache.n_head_caches, G, 128), float("nan")).cuda()
+    bk.bkv_decode_attention(cache, q, out, scale=scale)
+    on, qn = out.cpu().numpy(), synth.bits(q)
+    for hc, layer, r, h in head_iter(cache):
+        keys = oracle.gather_paged(k_in[layer], bt[r], h, N[r])
+        vals = oracle.gather_paged(v_in[layer], bt[r], h, N[r])
+        ref = oracle.decode_attention(qn[hc], keys, vals, scale)
+        vmax = float(np.abs(bf16_values(vals)).max()) if len(vals) else 1.0
+        err = np.abs(np.asarray(on[hc], np.float64) - ref).max()
+        assert err <= ATT_TOL * vmax, (hc, N[r], err, vmax)
 
 
 def test_decode_attention_after_compaction():
