@@ -125,3 +125,53 @@ def test_noalloc_pass_matches_the_workspace_pass(mode):
         else:
             assert not np.array_equal(r_out[11].view(np.uint16), synth.bits(batch.k_pools[0])), \
                 "no row moved"
+
+
+@pytest.mark.parametrize("mode", ["beacon", "beacon_pages", "random"])
+def test_noalloc_pass_replays_from_a_hip_graph(mode):
+    """Code under HIP graph capture is one of the callers this entry point
+    serves: a captured allocation-free pass (the scratch address was looked up
+    by an eager call before), replayed three times from restored inputs with
+    eager copies and synchronisations between the replays, matches an eager
+    allocation-free pass byte for byte every time."""
+    B = 384
+    L, R, H, N, P = SHAPES[0]
+    say("noalloc graph replay", mode)
+    wl = synth.WORKLOADS["serving_r128"].with_(n_layers=L, n_requests=R, n_kv_heads=H, budget=B,
+                                              prompt_len=max(P), seq_len=max(N), seed=140)
+    batch = synth.make_batch(wl)
+    q = batch.queries.cuda()
+    rid = torch.arange(3, 3 + R, dtype=torch.int64).cuda()
+    pss = torch.full((R,), 2, dtype=torch.int32).cuda()
+    ref = Run(batch, N, P)
+    run_pass(bk.bkv_evict_pass_noalloc, ref, mode, q, B, rid, pss, {})
+    r_out = ref.outputs()
+    assert int(r_out[7][0]) == 0
+    mine = Run(batch, N, P)
+    state = [mine.b, mine.c, mine.assign, mine.pos, mine.bt, mine.seq, mine.freed, mine.st,
+             mine.hbt, mine.hseq, mine.hfreed, *mine.cache.k_pools, *mine.cache.v_pools]
+    init = [t.clone() for t in state]
+
+    def restore():
+        for dst, src in zip(state, init):
+            dst.copy_(src)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):           # warm-up on the capture stream
+        restore()
+        run_pass(bk.bkv_evict_pass_noalloc, mine, mode, q, B, rid, pss, {})
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    restore()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        run_pass(bk.bkv_evict_pass_noalloc, mine, mode, q, B, rid, pss, {})
+    for rep in range(3):
+        restore()
+        torch.cuda.synchronize()
+        g.replay()
+        m_out = mine.outputs()
+        for i, (x, y) in enumerate(zip(r_out, m_out)):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), (mode, rep, i)
