@@ -217,3 +217,19 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+@pytest.mark.parametrize("workload", ["serving_r128", "qwen3_32b_r32", "qwen3_4b_r16"])
+def test_committed_counters_match_the_current_kernel_sources(workload):
+    """The bench reports counter traffic only from profiles taken on the
+    current kernel sources; the committed summaries of every profiled
+    workload must therefore be refreshed with any kernel change, or the
+    line's `traffic` field goes null."""
+    path = bench.traffic_file(workload)
+    with open(path) as f:
+        t = json.load(f)
+    kernels = [k for k in t if not k.startswith("_")]
+    assert {"beacon_update", "beacon_evict"} <= set(kernels), kernels
+    for k in kernels:
+        assert t[k]["source_sha"] == bench.kernel_source_hash(k), (workload, k)
+        assert bench.stored_counters(k, workload), (workload, k)
